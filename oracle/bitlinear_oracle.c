@@ -1,0 +1,325 @@
+/*
+ * bitlinear_oracle.c -- plain, slow CPU oracle for the BitNet b1.58 BitLinear
+ * forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark do.  It shares no code, header, table or constant with the GPU
+ * library: every constant below is declared here again on purpose.
+ *
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fno-fast-math -shared -fPIC
+ *        (no -ffast-math: every float operation must be the IEEE one written).
+ *
+ * Sources, cited by page title and section:
+ *  [P1] "BitNet b1.58 & 1-Bit LLMs in Production: Ternary Quantization,
+ *       MatMul-Free Kernels, and Edge AI Silicon Deployment"
+ *  [P2] "1-Bit Large Language Models and BitNet b1.58: How Ternary Weights and
+ *       Additive Kernels Eliminate Matrix Multiplications"
+ *  [P4] "BitNet b1.58 & 1-Bit LLM Architectures: Eliminating Matrix
+ *       Multiplication and Running 70B Models on CPU in 2026"
+ *  [P5] "BitNet b1.58: Ternary Weight LLMs That Eliminate Matrix
+ *       Multiplication"
+ *
+ * Readings taken where the pages are silent or disagree (each is listed with
+ * its reason in the design notes of the repository):
+ *  - gamma is the exact mean of |W| over the whole matrix, rounded once to the
+ *    nearest float32 (ties to even), then clamped below at 1e-5.  The pages give
+ *    the mean as a formula and leave its evaluation order open.
+ *  - Rounding is round-half-to-even everywhere (the listings use torch.round).
+ *  - Activation scale: eta = max(max_k |x[m][k]|, 1e-5) per token row m;
+ *    xq = clamp(rne((x * 127) / eta), -128, 127), multiply first, then an IEEE
+ *    float32 division, as both code listings write it.
+ *  - Dequant: s = (eta * gamma) / 127 in float32, y = float(y_int) * s.
+ *  - Canonical 2-bit code: -1 -> 00, 0 -> 01, +1 -> 10; weight j of a byte sits
+ *    in bits 2j..2j+1; a row holds ceil(K/4) bytes and pads with code 01.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+#include <pthread.h>
+
+#define OR_QB 127.0f          /* Q_b of the activation quantizer          */
+#define OR_SCALE_FLOOR 1e-5f  /* lower clamp on eta and gamma             */
+
+/* ------------------------------------------------------------------------ */
+/* Exact arithmetic on non-negative integers held as little-endian 32-bit    */
+/* limbs.  Used only by the gamma computation.                               */
+/* ------------------------------------------------------------------------ */
+#define OR_LIMBS 14 /* 448 bits: the exact sum of up to 2^40 |floats| needs 318 */
+
+typedef struct { uint32_t w[OR_LIMBS]; } or_big;
+
+static void big_zero(or_big* a) { memset(a, 0, sizeof(*a)); }
+
+/* a += v * 2^shift, v < 2^32 */
+static void big_add_shifted(or_big* a, uint32_t v, int shift) {
+    int limb = shift / 32, bit = shift % 32;
+    uint64_t carry = ((uint64_t)v) << bit; /* at most 63 bits */
+    for (int i = limb; i < OR_LIMBS && carry; ++i) {
+        uint64_t s = (uint64_t)a->w[i] + (carry & 0xffffffffu);
+        a->w[i] = (uint32_t)s;
+        carry = (carry >> 32) + (s >> 32);
+    }
+}
+
+static int big_bitlen(const or_big* a) {
+    for (int i = OR_LIMBS - 1; i >= 0; --i)
+        if (a->w[i]) {
+            int b = 32;
+            while (!(a->w[i] & (1u << (b - 1)))) --b;
+            return i * 32 + b;
+        }
+    return 0;
+}
+
+static int big_bit(const or_big* a, int pos) {
+    if (pos < 0 || pos >= OR_LIMBS * 32) return 0;
+    return (a->w[pos / 32] >> (pos % 32)) & 1u;
+}
+
+/*
+ * Absmean weight scale.
+ * [P1] section "1. Absmean Weight Quantization" (gamma = mean of |W_ij| over
+ * the n x m matrix) and the WeightQuantizerSTE listing in "Production PyTorch
+ * Implementation: BitLinear b1.58 Layer" (clamp at 1e-5); [P2] "Inside the
+ * BitLinear Layer", "1. Absmean Weight Quantization"; [P4] "The Weight
+ * Quantization Function: Absmean Scaling".
+ *
+ * Every finite float32 magnitude is sig * 2^(t - 149) with an integer sig <
+ * 2^24 and 0 <= t <= 253, so the sum of all |W| is an exact integer count of
+ * 2^-149 units.  The mean S / (N*K) is then rounded to float32 by plain long
+ * division, bit by bit.
+ */
+int oracle_absmean_gamma(const float* W, int64_t N, int64_t K, float* gamma_out) {
+    if (!W || !gamma_out || N <= 0 || K <= 0) return -1;
+    const uint64_t D = (uint64_t)N * (uint64_t)K;
+    if (D >> 40) return -1;
+    or_big S;
+    big_zero(&S);
+    for (uint64_t i = 0; i < D; ++i) {
+        uint32_t bits;
+        memcpy(&bits, &W[i], 4);
+        bits &= 0x7fffffffu;             /* |w| */
+        uint32_t e = bits >> 23, f = bits & 0x7fffffu;
+        if (e == 255) return -2;         /* Inf/NaN: outside the contract */
+        uint32_t sig = e ? (f | 0x800000u) : f;
+        int t = e ? (int)e - 1 : 0;      /* |w| = sig * 2^(t-149) */
+        if (sig) big_add_shifted(&S, sig, t);
+    }
+    /* Long division S / D, producing quotient bits from the top. */
+    int L = big_bitlen(&S);
+    /* quotient bits q_i for bit positions i = L-1 .. -(guard) relative to the
+       2^-149 unit; keep the first 26 significant ones and a sticky flag */
+    uint64_t rem = 0;                    /* rem < D < 2^40 at all times */
+    uint32_t q = 0;                      /* significant quotient bits so far */
+    int nsig = 0, qexp = 0, sticky = 0;  /* qexp: position of the last kept bit */
+    for (int pos = L - 1; pos >= -200; --pos) {
+        rem = (rem << 1) | (uint64_t)big_bit(&S, pos);
+        int qb = 0;
+        if (rem >= D) { rem -= D; qb = 1; }
+        if (nsig == 0 && !qb) continue;  /* leading zeros of the quotient */
+        if (nsig < 26) { q = (q << 1) | (uint32_t)qb; ++nsig; qexp = pos; }
+        else if (qb) sticky = 1;
+        if (nsig == 26 && pos < -160) break;
+    }
+    if (rem) sticky = 1;
+    float g;
+    if (nsig == 0) {
+        g = 0.0f;
+    } else {
+        /* normalise to exactly 26 bits: q = 24-bit significand, round, sticky */
+        while (nsig < 26) { q <<= 1; ++nsig; --qexp; }
+        uint32_t sig = q >> 2, rb = (q >> 1) & 1u, lb = q & 1u;
+        int exp2 = qexp + 2;             /* value = sig * 2^(exp2 - 149) */
+        if (rb && (lb || sticky || (sig & 1u))) ++sig;
+        if (sig == (1u << 24)) { sig >>= 1; ++exp2; }
+        /* value = sig * 2^(exp2-149); means below 2^-126 are under the clamp */
+        double v = ldexp((double)sig, exp2 - 149);
+        g = (float)v; /* exact: sig has 24 bits and the exponent is in range */
+        if (exp2 - 149 + 23 < -126) g = 0.0f; /* subnormal means: clamp below */
+    }
+    if (g < OR_SCALE_FLOOR) g = OR_SCALE_FLOOR;
+    *gamma_out = g;
+    return 0;
+}
+
+/*
+ * Ternarization: W~ = Clip(Round(W / gamma), -1, +1).
+ * [P1] "1. Absmean Weight Quantization" and the WeightQuantizerSTE listing
+ * (division, torch.round, clamp); [P2] "1. Absmean Weight Quantization".
+ */
+int oracle_ternarize(const float* W, int64_t N, int64_t K, float gamma, int8_t* Wt) {
+    if (!W || !Wt || N <= 0 || K <= 0 || !(gamma > 0.0f)) return -1;
+    for (int64_t i = 0; i < N * K; ++i) {
+        float t = W[i] / gamma;          /* IEEE float32 division */
+        float r = nearbyintf(t);         /* round half to even */
+        if (r > 1.0f) r = 1.0f;
+        if (r < -1.0f) r = -1.0f;
+        Wt[i] = (int8_t)r;
+    }
+    return 0;
+}
+
+/*
+ * Canonical 2-bit packing, four weights per byte.
+ * [P1] "Production Deployment Standards for Edge Systems Engineers", item 1
+ * ({-1,0,+1} -> {00,01,10}); [P5] "Kernel Implementation: The Lookup Table
+ * Approach" (encoding comment; field j of a byte at bits 2j..2j+1).
+ * Row n occupies ceil(K/4) bytes; byte b holds k = 4b + j; pad fields hold 01.
+ */
+int64_t oracle_packed_row_bytes(int64_t K) { return (K + 3) / 4; }
+
+int oracle_pack(const int8_t* Wt, int64_t N, int64_t K, uint8_t* packed) {
+    if (!Wt || !packed || N <= 0 || K <= 0) return -1;
+    const int64_t rb = oracle_packed_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < rb; ++b) {
+            uint8_t byte = 0;
+            for (int j = 0; j < 4; ++j) {
+                int64_t k = 4 * b + j;
+                int code;
+                if (k >= K) code = 1;                     /* pad: zero weight */
+                else if (Wt[n * K + k] == 1) code = 2;
+                else if (Wt[n * K + k] == 0) code = 1;
+                else if (Wt[n * K + k] == -1) code = 0;
+                else return -3;                           /* not ternary */
+                byte |= (uint8_t)(code << (2 * j));
+            }
+            packed[n * rb + b] = byte;
+        }
+    return 0;
+}
+
+int oracle_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wt) {
+    if (!Wt || !packed || N <= 0 || K <= 0) return -1;
+    const int64_t rb = oracle_packed_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int code = (packed[n * rb + k / 4] >> (2 * (k % 4))) & 3;
+            if (code == 3) return -4;                     /* never produced */
+            Wt[n * K + k] = (int8_t)(code - 1);
+        }
+    return 0;
+}
+
+/*
+ * Per-token absmax INT8 activation quantization.
+ * [P1] "2. Absmax Dynamic Activation Quantization" (Q_b = 127) and the
+ * ActivationQuantizerSTE listing (max over the last dim, clamp 1e-5,
+ * round(x * 127.0 / eta), clamp to [-128, 127]); [P4] "Activation
+ * Quantization: 8-Bit Absmax Scaling"; [P5] bitlinear_forward listing in
+ * "Weight Quantization: Absmean Centralization".
+ */
+int oracle_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta) {
+    if (!x || !xq || !eta || M < 0 || K <= 0) return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        const float* row = x + m * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(row[k]);
+            if (a > amax) amax = a;
+        }
+        float e = amax < OR_SCALE_FLOOR ? OR_SCALE_FLOOR : amax;
+        eta[m] = e;
+        for (int64_t k = 0; k < K; ++k) {
+            float scaled = row[k] * OR_QB;   /* x * 127.0 */
+            float q = scaled / e;            /* ... / eta, IEEE division */
+            float r = nearbyintf(q);         /* round half to even */
+            if (r > 127.0f) r = 127.0f;
+            if (r < -128.0f) r = -128.0f;
+            xq[m * K + k] = (int8_t)r;
+        }
+    }
+    return 0;
+}
+
+/*
+ * The multiplication-free contraction:
+ *   y_int[m][n] = sum_{k : W~[n][k] = +1} xq[m][k] - sum_{k : W~[n][k] = -1} xq[m][k]
+ * [P1] "The MatMul-Free Breakthrough" (partition of additions and
+ * subtractions) and pipeline box 4; [P2] "3. Additive Integer Accumulation"
+ * (add on +1, subtract on -1, skip on 0); [P5] "The Arithmetic Collapse".
+ * W~ is [N][K] (output-major, as nn.Linear stores it); accumulation is int64
+ * and checked to fit int32.
+ */
+typedef struct {
+    const int8_t* xq; const int8_t* Wt; int64_t M, N, K; int32_t* y;
+    int64_t n0, n1; int overflow;
+} or_contract_job;
+
+static void* or_contract_rows(void* arg) {
+    or_contract_job* j = (or_contract_job*)arg;
+    for (int64_t m = 0; m < j->M; ++m)
+        for (int64_t n = j->n0; n < j->n1; ++n) {
+            const int8_t* xr = j->xq + m * j->K;
+            const int8_t* wr = j->Wt + n * j->K;
+            int64_t plus = 0, minus = 0;
+            for (int64_t k = 0; k < j->K; ++k) {
+                if (wr[k] == 1) plus += xr[k];
+                else if (wr[k] == -1) minus += xr[k];
+                /* zero weight: skipped */
+            }
+            int64_t acc = plus - minus;
+            if (acc > INT32_MAX || acc < INT32_MIN) j->overflow = 1;
+            j->y[m * j->N + n] = (int32_t)acc;
+        }
+    return 0;
+}
+
+int oracle_ternary_contract(const int8_t* xq, const int8_t* Wt, int64_t M, int64_t N,
+                            int64_t K, int32_t* y_int, int threads) {
+    if (!xq || !Wt || !y_int || M < 0 || N <= 0 || K <= 0) return -1;
+    if (threads < 1) threads = 1;
+    if (threads > 256) threads = 256;
+    if (threads > N) threads = (int)N;
+    or_contract_job jobs[256];
+    pthread_t tid[256];
+    for (int t = 0; t < threads; ++t) {
+        jobs[t].xq = xq; jobs[t].Wt = Wt; jobs[t].M = M; jobs[t].N = N; jobs[t].K = K;
+        jobs[t].y = y_int; jobs[t].overflow = 0;
+        jobs[t].n0 = N * t / threads; jobs[t].n1 = N * (t + 1) / threads;
+    }
+    if (threads == 1) or_contract_rows(&jobs[0]);
+    else {
+        for (int t = 0; t < threads; ++t) pthread_create(&tid[t], 0, or_contract_rows, &jobs[t]);
+        for (int t = 0; t < threads; ++t) pthread_join(tid[t], 0);
+    }
+    for (int t = 0; t < threads; ++t) if (jobs[t].overflow) return -5;
+    return 0;
+}
+
+/*
+ * Dequantization: y = y_int * ((eta * gamma) / 127).
+ * [P1] pipeline box 5 and step 5 of BitLinear158.forward (scale =
+ * (eta * gamma) / 127.0, output = y_raw * scale); [P5] bitlinear_forward
+ * listing (one scalar rescale per token); [P2] "3. Additive Integer
+ * Accumulation" (rescale once by beta*gamma/Q_b).
+ */
+int oracle_dequant(const int32_t* y_int, const float* eta, float gamma, int64_t M,
+                   int64_t N, float* y) {
+    if (!y_int || !eta || !y || M < 0 || N <= 0) return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        float eg = eta[m] * gamma;   /* eta * gamma */
+        float s = eg / OR_QB;        /* ... / 127.0 */
+        for (int64_t n = 0; n < N; ++n) y[m * N + n] = (float)y_int[m * N + n] * s;
+    }
+    return 0;
+}
+
+/*
+ * The whole forward from float32 activations and ternary weights with their
+ * scale: quantize, contract, dequantize.  xq/eta/y_int may be NULL when the
+ * caller does not need the intermediates (they are then kept internally only
+ * when provided).  [P1] BitLinear158.forward steps 2, 4 and 5 (step 1, the
+ * RMSNorm, and step 3, the weight quantizer, happen outside this call).
+ */
+int oracle_forward(const float* x, const int8_t* Wt, float gamma, int64_t M, int64_t N,
+                   int64_t K, float* y, int8_t* xq, float* eta, int32_t* y_int,
+                   int threads) {
+    if (!x || !Wt || !y || !xq || !eta || !y_int) return -1;
+    int rc = oracle_quantize_act(x, M, K, xq, eta);
+    if (rc) return rc;
+    rc = oracle_ternary_contract(xq, Wt, M, N, K, y_int, threads);
+    if (rc) return rc;
+    return oracle_dequant(y_int, eta, gamma, M, N, y);
+}

@@ -1,0 +1,441 @@
+"""Pins for the CPU oracle: checks against what the BitNet b1.58 pages and the
+mathematics fix, none of which re-types the oracle's own formula.
+
+Each ``pin_*`` takes an oracle handle (``oracle.Oracle``) and raises
+AssertionError when the oracle disagrees.  ``test_oracle_pins.py`` runs them on
+the oracle as built; ``test_oracle_pin_strength.py`` runs them on copies of the
+oracle with a planted mistake and requires that each copy fails at least one.
+
+Kinds of pin used (no page prints a numeric worked example):
+* facts the pages print (``golden/page_constants.txt``),
+* hand-derived examples whose every step is exact,
+* exact rational arithmetic (``fractions.Fraction``) for the mean,
+* a library routine the method reduces to (integer matrix product),
+* brute force over every ternary row of a tiny width,
+* invariants and metamorphic relations, and closed-form statistics.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+from math import erf, sqrt, pi
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def page_constants():
+    facts = {}
+    with open(os.path.join(GOLDEN, "page_constants.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, *vals = line.split()
+            facts.setdefault(name, []).append(vals)
+    return facts
+
+
+def f32(v) -> np.float32:
+    return np.float32(v)
+
+
+def nearest_f32(fr: Fraction) -> np.float32:
+    """The float32 nearest to a positive rational, ties to even, found by exact
+    comparison among the neighbours of a first guess."""
+    guess = np.float32(float(fr))
+    cands = {guess, np.nextafter(guess, np.float32(0)), np.nextafter(guess, np.float32(np.inf))}
+    best = None
+    for c in sorted(cands):
+        d = abs(Fraction(float(c)) - fr)
+        if best is None or d < best[0]:
+            best = (d, c)
+        elif d == best[0]:
+            # tie: keep the one with an even significand
+            if int(np.float32(c).view(np.uint32)) % 2 == 0:
+                best = (d, c)
+    return np.float32(best[1])
+
+
+def exact_mean_abs(W: np.ndarray) -> Fraction:
+    total = Fraction(0)
+    for v in np.asarray(W, np.float32).ravel():
+        total += Fraction(abs(float(v)))
+    return total / W.size
+
+
+# ------------------------------------------------------------------ gamma
+def pin_gamma_hand(O):
+    # mean(|0.5|, |-0.5|, |1.5|, |-1.5|) = 1 exactly
+    W = np.array([[0.5, -0.5, 1.5, -1.5]], np.float32)
+    assert O.absmean_gamma(W) == f32(1.0)
+    # 2x4 matrix: mean of |.| = (1+2+3+4+5+6+7+8)/8 = 4.5
+    W = np.arange(1, 9, dtype=np.float32).reshape(2, 4) * np.array([1, -1, 1, -1], np.float32)
+    assert O.absmean_gamma(W) == f32(4.5)
+
+
+def pin_gamma_exact_rational(O):
+    rng = np.random.default_rng(1234)
+    cases = [
+        rng.standard_normal((7, 13), dtype=np.float32) * f32(0.02),
+        rng.standard_normal((1, 257), dtype=np.float32),
+        rng.uniform(-3, 3, (33, 5)).astype(np.float32),
+        # magnitudes spanning 2^-140 .. 2^120: any finite-precision running sum loses them
+        (np.float32(2.0) ** rng.integers(-140, 120, (9, 11)).astype(np.float32)
+         * rng.uniform(1, 2, (9, 11)).astype(np.float32)),
+        np.array([[3e38, 1.0, 1e-30, 2.5e-45]], np.float32),
+    ]
+    for W in cases:
+        want = max(nearest_f32(exact_mean_abs(W)), f32(1e-5))
+        got = O.absmean_gamma(W)
+        assert got == want, (W.shape, got, want)
+
+
+def pin_gamma_ties(O):
+    one = 1.0
+    u = 2.0 ** -23
+    # exact mean 1 + 2^-24 lies halfway between 1 and 1 + 2^-23: ties to even -> 1
+    W = np.array([[one, one + u]], np.float32)
+    assert O.absmean_gamma(W) == f32(1.0)
+    # mean 1 + 3*2^-24 is halfway between 1 + 2^-23 (odd) and 1 + 2^-22 (even)
+    W = np.array([[one + u, one + 2 * u]], np.float32)
+    assert O.absmean_gamma(W) == f32(one + 2 * u)
+    # just above the first midpoint: rounds up
+    W = np.array([[one, one + u, one, one + 2 * u]], np.float32)  # mean = 1 + 3u/4
+    assert O.absmean_gamma(W) == f32(one + u)
+    # 1 + 2^-24 + 2^-41: a tie only in its first 25 bits; the far tail decides
+    W = np.array([[2.0, u + 2.0 ** -40]], np.float32)
+    assert O.absmean_gamma(W) == f32(one + u)
+
+
+def pin_gamma_clamp(O):
+    floor = f32(float(page_constants()["scale_floor"][0][0]))
+    assert O.absmean_gamma(np.zeros((3, 5), np.float32)) == floor
+    assert O.absmean_gamma(np.full((2, 2), 1e-7, np.float32)) == floor
+    tiny = np.full((4, 4), 2.0 ** -149, np.float32)  # subnormal inputs
+    assert O.absmean_gamma(tiny) == floor
+
+
+def pin_gamma_metamorphic(O):
+    rng = np.random.default_rng(7)
+    W = rng.standard_normal((31, 17), dtype=np.float32) * f32(0.02)
+    g = O.absmean_gamma(W)
+    for e in (-8, 5, 20):
+        assert O.absmean_gamma(W * f32(2.0 ** e)) == g * f32(2.0 ** e)
+    assert O.absmean_gamma(-W) == g
+    P = rng.permutation(W.ravel()).reshape(17, 31)  # order and shape free
+    assert O.absmean_gamma(P) == g
+
+
+def pin_gamma_statistics(O):
+    # E|Z| = sigma * sqrt(2/pi) for Z ~ N(0, sigma^2); sd of |Z| is sigma*sqrt(1-2/pi)
+    sigma = 0.02
+    n = 1 << 20
+    W = np.random.default_rng(99).standard_normal((1024, n // 1024), dtype=np.float32) * f32(sigma)
+    g = float(O.absmean_gamma(W))
+    mu = sigma * sqrt(2 / pi)
+    se = sigma * sqrt(1 - 2 / pi) / sqrt(n)
+    assert abs(g - mu) < 5 * se, (g, mu, se)
+
+
+# ------------------------------------------------------------------ ternarize
+def pin_ternarize_range_and_threshold(O):
+    lo, hi = (int(v) for v in page_constants()["weight_clip"][0])
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((64, 96), dtype=np.float32) * f32(0.02)
+    g = O.absmean_gamma(W)
+    Wt = O.ternarize(W, g)
+    assert set(np.unique(Wt)).issubset({lo, 0, hi})
+    # Round-then-clip to [-1, 1] is a threshold at 1/2 on the float32 quotient:
+    # +-1 exactly when |W/gamma| > 1/2 (round-half-even sends 0.5 to 0).
+    t = W / g
+    expect = np.where(np.abs(t) > f32(0.5), np.sign(t), 0).astype(np.int8)
+    assert np.array_equal(Wt, expect)
+
+
+def pin_ternarize_ties(O):
+    g = f32(0.25)
+    W = np.array([[0.125, -0.125, 0.1250001, 0.375, -0.375, 1.0, -7.0, 0.0]], np.float32)
+    # quotients 0.5, -0.5, just above 0.5, 1.5, -1.5, 4, -28, 0
+    assert O.ternarize(W, g).tolist() == [[0, 0, 1, 1, -1, 1, -1, 0]]
+
+
+def pin_ternarize_division(O):
+    # The weight quantizer listing divides W by gamma.  For these (gamma, W)
+    # pairs the IEEE quotient lands just above 1/2 (so W~ = +1), while a
+    # multiply by a rounded reciprocal of gamma would land at or below 1/2.
+    # The quotient is rounded to float32 in exact rational arithmetic here.
+    cases = [(0.028031973, 0.0140159875), (0.0059057022, 0.0029528514),
+             (0.0062154713, 0.003107736), (0.013053724, 0.0065268623)]
+    for g, w in cases:
+        g, w = f32(g), f32(w)
+        q = Fraction(float(nearest_f32(Fraction(float(w)) / Fraction(float(g)))))
+        assert q > Fraction(1, 2)
+        recip = nearest_f32(1 / Fraction(float(g)))
+        assert Fraction(float(nearest_f32(Fraction(float(w)) * Fraction(float(recip))))) <= Fraction(1, 2)
+        W = np.array([[w, -w]], np.float32)
+        assert O.ternarize(W, g).tolist() == [[1, -1]], (g, w)
+
+
+def pin_ternarize_symmetry(O):
+    rng = np.random.default_rng(6)
+    W = rng.standard_normal((16, 40), dtype=np.float32)
+    g = O.absmean_gamma(W)
+    assert np.array_equal(O.ternarize(-W, g), -O.ternarize(W, g))
+    assert np.array_equal(O.ternarize(W * f32(8.0), g * f32(8.0)), O.ternarize(W, g))
+
+
+def pin_ternarize_statistics(O):
+    # gamma -> sigma*sqrt(2/pi), so P(w~ = 0) = P(|Z| <= sqrt(2/pi)/2) = erf(sqrt(1/pi)/2)
+    n_rows, K = 1024, 1024
+    W = np.random.default_rng(11).standard_normal((n_rows, K), dtype=np.float32) * f32(0.02)
+    Wt, g = O.quantize_weights(W)
+    p0 = erf(sqrt(2 / pi) / 2 / sqrt(2))
+    n = Wt.size
+    se = sqrt(p0 * (1 - p0) / n)
+    z = float((Wt == 0).mean())
+    assert abs(z - p0) < 5 * se, (z, p0)
+    assert abs(p0 - 0.31006) < 1e-4
+    assert abs(float((Wt == 1).mean()) - (1 - p0) / 2) < 5 * se
+    # the pages report about a third of weights at zero for trained models
+    assert abs(z - float(page_constants()["reported_zero_share"][0][0])) < 0.03
+
+
+# ------------------------------------------------------------------ packing
+def _code_of():
+    return {int(w): int(c) for w, c in page_constants()["code"]}
+
+
+def _shift_of():
+    return {int(j): int(s) for j, s in page_constants()["field_shift"]}
+
+
+def pin_pack_page_bytes(O):
+    code, shift = _code_of(), _shift_of()
+
+    def byte_of(ws):
+        return sum(code[w] << shift[j] for j, w in enumerate(ws))
+
+    for ws in ([-1, 0, 1, 0], [1, 1, 1, 1], [0, 0, 0, 0], [-1, -1, -1, -1], [1, -1, 0, 1]):
+        got = O.pack(np.array([ws], np.int8))
+        assert got.shape == (1, 1) and int(got[0, 0]) == byte_of(ws), (ws, got)
+    assert int(O.pack(np.array([[-1, 0, 1, 0]], np.int8))[0, 0]) == 0x64
+    assert int(O.pack(np.array([[1, 1, 1, 1]], np.int8))[0, 0]) == 0xAA
+    assert int(O.pack(np.array([[0, 0, 0, 0]], np.int8))[0, 0]) == 0x55
+    assert int(O.pack(np.array([[-1, -1, -1, -1]], np.int8))[0, 0]) == 0x00
+
+
+def pin_pack_layout_and_padding(O):
+    # K = 6: two bytes per row; the second byte holds k = 4, 5 and two pad fields (code 01)
+    Wt = np.array([[1, 0, -1, 1, -1, 1], [0, 0, 0, 0, 1, -1]], np.int8)
+    P = O.pack(Wt)
+    assert P.shape == (2, 2)
+    assert P.tolist() == [[0b10_00_01_10, 0b01_01_10_00], [0x55, 0b01_01_00_10]]
+
+
+def pin_pack_roundtrip(O):
+    rng = np.random.default_rng(3)
+    for K in (1, 3, 4, 5, 63, 64, 130):
+        Wt = rng.integers(-1, 2, (9, K)).astype(np.int8)
+        P = O.pack(Wt)
+        assert P.shape == (9, (K + 3) // 4)
+        assert np.array_equal(O.unpack(P, K), Wt)
+        # code 11 never appears
+        fields = np.stack([(P >> s) & 3 for s in (0, 2, 4, 6)])
+        assert not np.any(fields == 3)
+
+
+def pin_pack_rejects(O):
+    import oracle
+    try:
+        O.unpack(np.array([[0xFF]], np.uint8), 4)
+    except oracle.OracleError:
+        pass
+    else:
+        raise AssertionError("code 11 accepted")
+    try:
+        O.pack(np.array([[2, 0, 0, 0]], np.int8))
+    except oracle.OracleError:
+        pass
+    else:
+        raise AssertionError("non-ternary weight accepted")
+
+
+# ------------------------------------------------------------------ activation quant
+def pin_quant_hand(O):
+    # eta = 127 so every quotient x*127/127 = x is exact: this isolates the
+    # rounding rule (half to even) from the division.
+    x = np.array([[127, 62.5, 63.5, -0.5, 0.5, 1.5, 2.5, -2.5]], np.float32)
+    xq, eta = O.quantize_act(x)
+    assert eta.tolist() == [127.0]
+    assert xq.tolist() == [[127, 62, 64, 0, 0, 2, 2, -2]]
+    # eta = 2: quotients (x*127)/2 = 127, -63.5 (-> -64, even), 31.75, -15.875, 0
+    x = np.array([[2.0, -1.0, 0.5, -0.25, 0.0]], np.float32)
+    xq, eta = O.quantize_act(x)
+    assert eta.tolist() == [2.0]
+    assert xq.tolist() == [[127, -64, 32, -16, 0]]
+
+
+def _fl32(fr: Fraction) -> Fraction:
+    """Round a rational to the nearest float32 (ties to even), exactly."""
+    if fr == 0:
+        return Fraction(0)
+    r = nearest_f32(abs(fr))
+    return Fraction(float(r)) if fr > 0 else -Fraction(float(r))
+
+
+def pin_quant_op_order(O):
+    # Both page listings write round(x * 127.0 / eta): multiply first, then an
+    # IEEE division.  For these inputs the other order, (x / eta) * 127,
+    # rounds to a different integer.  Each float step below is carried out in
+    # exact rational arithmetic and rounded to float32 explicitly.
+    cases = [(5.2772126, -4.466932), (7.6121526, 4.2855816), (2.7765708, 2.1316192),
+             (1.1328796, 0.084742956), (3.7839653, -3.5307078)]
+    for eta, xv in cases:
+        eta, xv = f32(eta), f32(xv)
+        x = np.array([[eta, xv]], np.float32)
+        xq, e = O.quantize_act(x)
+        assert e[0] == eta
+        mul_first = round(_fl32(_fl32(Fraction(float(xv)) * 127) / Fraction(float(eta))))
+        div_first = round(_fl32(_fl32(Fraction(float(xv)) / Fraction(float(eta))) * 127))
+        assert mul_first != div_first
+        assert int(xq[0, 1]) == mul_first, (eta, xv, int(xq[0, 1]), mul_first)
+
+
+def pin_quant_invariants(O):
+    qb = int(page_constants()["qb"][0][0])
+    rng = np.random.default_rng(8)
+    x = np.concatenate([rng.standard_normal((5, 300), dtype=np.float32),
+                        rng.standard_t(3, (5, 300)).astype(np.float32)])
+    xq, eta = O.quantize_act(x)
+    assert np.array_equal(eta, np.abs(x).max(axis=1))
+    assert xq.min() >= -qb and xq.max() <= qb
+    arg = np.abs(x).argmax(axis=1)
+    assert np.array_equal(np.abs(xq[np.arange(len(x)), arg]), np.full(len(x), qb))
+    assert np.all((np.sign(xq) == np.sign(x)) | (xq == 0))
+    # within a rounding step of the real-valued x*127/eta (two float roundings
+    # add at most 2^-17 on a quotient of magnitude <= 127)
+    real = x.astype(np.float64) * qb / eta.astype(np.float64)[:, None]
+    assert np.max(np.abs(xq - real)) <= 0.5 + 2.0 ** -16
+    # monotone within a row
+    for m in range(len(x)):
+        o = np.argsort(x[m], kind="stable")
+        assert np.all(np.diff(xq[m][o].astype(int)) >= 0)
+
+
+def pin_quant_metamorphic(O):
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((4, 77), dtype=np.float32)
+    xq, eta = O.quantize_act(x)
+    for e in (-10, 3, 30):
+        xq2, eta2 = O.quantize_act(x * f32(2.0 ** e))
+        assert np.array_equal(xq2, xq)
+        assert np.array_equal(eta2, eta * f32(2.0 ** e))
+    xqn, etan = O.quantize_act(-x)
+    assert np.array_equal(xqn, -xq) and np.array_equal(etan, eta)
+    # per token: each row is quantized on its own
+    for m in range(4):
+        r, e = O.quantize_act(x[m:m + 1])
+        assert np.array_equal(r[0], xq[m]) and e[0] == eta[m]
+
+
+def pin_quant_floor(O):
+    floor = f32(float(page_constants()["scale_floor"][0][0]))
+    xq, eta = O.quantize_act(np.zeros((2, 9), np.float32))
+    assert np.all(xq == 0) and np.all(eta == floor)
+    x = np.array([[5e-6, -2.5e-6, 0.0, 1e-6]], np.float32)  # |x| below the floor
+    xq, eta = O.quantize_act(x)
+    assert eta[0] == floor
+    # 5e-6*127/1e-5 = 63.5 -> 64 or 63 depending on float rounding of the
+    # operands; the magnitude is bounded by 127 * 5e-6 / 1e-5 = 63.5
+    assert abs(int(xq[0, 0])) in (63, 64) and int(xq[0, 2]) == 0
+
+
+# ------------------------------------------------------------------ contraction
+def pin_contract_hand(O):
+    xq = np.array([[127, 62, 64, 0, 0, 2, 2, -2]], np.int8)
+    Wt = np.array([[1, -1, 0, 1, -1, 1, 1, -1]], np.int8)
+    # +1 at k=0,3,5,6: 127+0+2+2 = 131; -1 at k=1,4,7: 62+0-2 = 60 -> 71
+    assert O.ternary_contract(xq, Wt).tolist() == [[71]]
+
+
+def pin_contract_bruteforce(O):
+    # every ternary row of width 5 (3^5 = 243 rows) against random int8 rows,
+    # including the extremes; compared with numpy's integer and float64 matmul
+    import itertools
+    Wt = np.array(list(itertools.product((-1, 0, 1), repeat=5)), np.int8)
+    rng = np.random.default_rng(12)
+    xq = np.concatenate([rng.integers(-128, 128, (6, 5)),
+                         [[127] * 5, [-128] * 5, [0] * 5, [127, -128, 1, -1, 0]]]).astype(np.int8)
+    y = O.ternary_contract(xq, Wt)
+    assert y.shape == (10, 243)
+    assert np.array_equal(y, xq.astype(np.int64) @ Wt.astype(np.int64).T)
+    assert np.array_equal(y, (xq.astype(np.float64) @ Wt.astype(np.float64).T).astype(np.int64))
+
+
+def pin_contract_library(O):
+    rng = np.random.default_rng(13)
+    M, N, K = 3, 37, 211  # all distinct, so a transposed operand cannot pass
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    Wt = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    ref = xq.astype(np.int64) @ Wt.astype(np.int64).T
+    assert np.array_equal(O.ternary_contract(xq, Wt), ref)
+    assert np.array_equal(O.ternary_contract(xq, Wt, threads=4), ref)
+    # a consistent permutation of the reduction index changes nothing
+    p = rng.permutation(K)
+    assert np.array_equal(O.ternary_contract(xq[:, p], Wt[:, p]), ref)
+
+
+def pin_contract_extremes(O):
+    K = 28672
+    xq = np.full((2, K), 127, np.int8)
+    xq[1] = -127
+    Wt = np.ones((2, K), np.int8)
+    Wt[1] = -1
+    y = O.ternary_contract(xq, Wt)
+    assert y.tolist() == [[127 * K, -127 * K], [-127 * K, 127 * K]]
+
+
+# ------------------------------------------------------------------ dequant and chain
+def pin_dequant(O):
+    qb = int(page_constants()["qb"][0][0])
+    rng = np.random.default_rng(14)
+    y_int = rng.integers(-3_600_000, 3_600_000, (4, 50)).astype(np.int32)
+    y_int[0, 0] = 0
+    eta = rng.uniform(0.5, 40, 4).astype(np.float32)
+    g = f32(0.0173)
+    y = O.dequant(y_int, eta, g)
+    real = y_int.astype(np.float64) * eta.astype(np.float64)[:, None] * float(g) / qb
+    nz = real != 0
+    # three float32 roundings: relative error below 2^-22
+    assert np.all(np.abs(y[nz] - real[nz]) <= 2.0 ** -22 * np.abs(real[nz]))
+    assert y[0, 0] == 0.0
+    # exact case: eta*gamma = 127 -> scale 1
+    assert O.dequant(np.array([[5, -9]], np.int32), np.array([127.0], np.float32),
+                     f32(1.0)).tolist() == [[5.0, -9.0]]
+
+
+def pin_chain_hand(O):
+    # W = [1,-1,0,1,-1,1,1,-1]: gamma = 7/8; W/gamma = +-8/7 or 0 -> W~ = W
+    W = np.array([[1, -1, 0, 1, -1, 1, 1, -1]], np.float32)
+    Wt, g = O.quantize_weights(W)
+    assert g == f32(0.875) and Wt.tolist() == [[1, -1, 0, 1, -1, 1, 1, -1]]
+    x = np.array([[127, 62.5, 63.5, -0.5, 0.5, 1.5, 2.5, -2.5]], np.float32)
+    y, xq, eta, y_int = O.forward(x, Wt, g)
+    # y_int = 71; scale = (127 * 0.875) / 127 = 0.875 exactly; y = 62.125
+    assert y_int.tolist() == [[71]] and y.tolist() == [[62.125]]
+
+
+def pin_demo_shapes(O):
+    # the first page's demonstration: batch 2 x seq 64 tokens, 1024 -> 2048
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((2 * 64, 1024), dtype=np.float32)
+    W = rng.standard_normal((2048, 1024), dtype=np.float32) * f32(0.02)
+    Wt, g = O.quantize_weights(W)
+    y, xq, eta, y_int = O.forward(x, Wt, g, threads=4)
+    assert y.shape == (128, 2048) and set(np.unique(Wt)) == {-1, 0, 1}
+    assert np.array_equal(y_int, xq.astype(np.int64) @ Wt.astype(np.int64).T)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

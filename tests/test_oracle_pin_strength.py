@@ -1,0 +1,76 @@
+"""The pins must be strong enough to catch plausible mistakes in the oracle.
+
+Each case below plants one mistake in a copy of the oracle's C source (on the
+CPU, in a temporary directory), builds that copy with gcc and runs the pins on
+it.  The copy must fail at least one pin.  Mistakes are chosen so that every
+access stays in bounds.
+"""
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    # activation quantizer
+    "qb_128": ("#define OR_QB 127.0f", "#define OR_QB 128.0f"),
+    "act_round_half_away": ("float r = nearbyintf(q);", "float r = roundf(q);"),
+    "act_reciprocal_multiply": ("float q = scaled / e;", "float q = scaled * (1.0f / e);"),
+    "act_divide_before_multiply": ("float scaled = row[k] * OR_QB;   /* x * 127.0 */\n"
+                                   "            float q = scaled / e;",
+                                   "float scaled = row[k] / e;\n"
+                                   "            float q = scaled * OR_QB;"),
+    "act_no_abs": ("float a = fabsf(row[k]);", "float a = row[k];"),
+    "act_no_floor": ("float e = amax < OR_SCALE_FLOOR ? OR_SCALE_FLOOR : amax;",
+                     "float e = amax;"),
+    # weight quantizer
+    "gamma_divides_by_rows": ("const uint64_t D = (uint64_t)N * (uint64_t)K;",
+                              "const uint64_t D = (uint64_t)N;"),
+    "gamma_exponent_off_by_one": ("int t = e ? (int)e - 1 : 0;", "int t = e ? (int)e : 0;"),
+    "gamma_no_sticky": ("else if (qb) sticky = 1;", "else if (qb) sticky = 0;"),
+    "gamma_truncates": ("if (rb && (lb || sticky || (sig & 1u))) ++sig;", ""),
+    "gamma_no_floor": ("if (g < OR_SCALE_FLOOR) g = OR_SCALE_FLOOR;", ""),
+    "ternary_round_half_away": ("float r = nearbyintf(t);", "float r = roundf(t);"),
+    "ternary_no_clip": ("if (r > 1.0f) r = 1.0f;", ""),
+    "ternary_reciprocal": ("float t = W[i] / gamma;", "float t = W[i] * (1.0f / gamma);"),
+    # packing
+    "pack_field_order_reversed": ("byte |= (uint8_t)(code << (2 * j));",
+                                  "byte |= (uint8_t)(code << (6 - 2 * j));"),
+    "pack_codes_swapped": ("if (Wt[n * K + k] == 1) code = 2;\n"
+                           "                else if (Wt[n * K + k] == 0) code = 1;\n"
+                           "                else if (Wt[n * K + k] == -1) code = 0;",
+                           "if (Wt[n * K + k] == 1) code = 0;\n"
+                           "                else if (Wt[n * K + k] == 0) code = 1;\n"
+                           "                else if (Wt[n * K + k] == -1) code = 2;"),
+    "pack_pad_code_zero": ("if (k >= K) code = 1;", "if (k >= K) code = 0;"),
+    # contraction
+    "contract_sign_swapped": ("int64_t acc = plus - minus;", "int64_t acc = minus - plus;"),
+    "contract_drops_minus": ("else if (wr[k] == -1) minus += xr[k];",
+                             "else if (wr[k] == -1) minus += 0;"),
+    "contract_short_loop": ("for (int64_t k = 0; k < j->K; ++k) {\n                if (wr[k]",
+                            "for (int64_t k = 0; k + 1 < j->K; ++k) {\n                if (wr[k]"),
+    "contract_transposed_store": ("j->y[m * j->N + n] = (int32_t)acc;",
+                                  "j->y[n * j->M + m] = (int32_t)acc;"),
+    # dequant
+    "dequant_drops_gamma": ("float eg = eta[m] * gamma;", "float eg = eta[m];"),
+    "dequant_divides_by_128": ("float s = eg / OR_QB;", "float s = eg / 128.0f;"),
+}
+
+
+def _pins_fail(O) -> list:
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(O)
+        except (AssertionError, oracle.OracleError) as e:  # noqa: F841
+            failed.append(pin.__name__)
+            break
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = oracle.source_text()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    O = oracle.compile_variant(src.replace(old, new), str(tmp_path / f"liboracle_{name}.so"))
+    assert _pins_fail(O), f"no pin caught the planted mistake {name}"
