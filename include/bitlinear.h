@@ -1,0 +1,216 @@
+/*
+ * bitlinear.h -- C ABI of the BitNet b1.58 BitLinear forward pass for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (cited by page title and section):
+ *  [P1] "BitNet b1.58 & 1-Bit LLMs in Production: Ternary Quantization,
+ *       MatMul-Free Kernels, and Edge AI Silicon Deployment"
+ *  [P2] "1-Bit Large Language Models and BitNet b1.58: How Ternary Weights and
+ *       Additive Kernels Eliminate Matrix Multiplications"
+ *  [P4] "BitNet b1.58 & 1-Bit LLM Architectures: Eliminating Matrix
+ *       Multiplication and Running 70B Models on CPU in 2026"
+ *  [P5] "BitNet b1.58: Ternary Weight LLMs That Eliminate Matrix
+ *       Multiplication"
+ *
+ *   eta[m]   = max(max_k |x[m][k]|, 1e-5)                       per token row
+ *   xq[m][k] = clamp(rne((x[m][k] * 127) / eta[m]), -128, 127)   int8
+ *   gamma    = max(mean |W|, 1e-5)   (exact mean, rounded once to float32)
+ *   Wt[n][k] = clamp(rne(W[n][k] / gamma), -1, 1)                 ternary
+ *   y_int    = sum_{Wt=+1} xq - sum_{Wt=-1} xq                    int32
+ *   y[m][n]  = float(y_int[m][n]) * ((eta[m] * gamma) / 127)      float32
+ * All float steps are single IEEE float32 operations in the order written
+ * (no fused multiply-add, correctly rounded division, round half to even).
+ *
+ * Conventions shared by every call
+ *  - Matrices are dense and row-major: x, xq are [M][K]; W, Wt are [N][K]
+ *    (output features by input features, as nn.Linear stores them); y and
+ *    y_int are [M][N].
+ *  - Every pointer is a device pointer (HIP device memory), unless its name
+ *    ends in _host.  The caller allocates and frees every buffer; the library
+ *    never allocates device memory, keeps no state between calls and is
+ *    re-entrant.  Buffers must stay valid until the work queued on `stream`
+ *    has finished.
+ *  - `stream` is a hipStream_t (NULL is the default stream).  Every call only
+ *    queues work on it and returns, except where a call says it synchronizes.
+ *  - K must be a multiple of 16.  M may be 0 (nothing is queued).  N, K >= 1.
+ *  - Inputs must be finite; NaN or Inf give unspecified (but bounded) output.
+ *  - Arguments are validated before anything is queued: on a non-zero return
+ *    nothing has been written.
+ *
+ * Packed weight layout ("device layout")
+ *   A bijection of the canonical 2-bit format of [P1] "Production Deployment
+ *   Standards for Edge Systems Engineers" item 1 and [P5] "Kernel
+ *   Implementation: The Lookup Table Approach": codes 00 = -1, 01 = 0,
+ *   10 = +1, four weights per byte; code 11 never occurs.  Rows are grouped by
+ *   64 and K is cut into blocks of 64; block (g, b) of 1024 bytes holds, for
+ *   each of its 64 rows r in order, 16 bytes = 4 little-endian 32-bit words;
+ *   word d covers k = 64b + 16d + 4j + i at bits 8i + 2j .. 8i + 2j + 1
+ *   (i = byte, j = field).  Rows past N and k past K hold code 01.
+ *   Size: bitlinear_packed_bytes(N, K) = ceil(N/64) * ceil(K/64) * 1024.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-valued call. */
+#define BITLINEAR_OK 0
+#define BITLINEAR_EINVAL (-1)       /* null pointer, negative or zero size, bad count */
+#define BITLINEAR_EUNSUPPORTED (-2) /* K not a multiple of 16, or a size beyond 2^31 */
+#define BITLINEAR_EWORKSPACE (-3)   /* workspace missing or smaller than required */
+#define BITLINEAR_EBADCODE (-4)     /* a ternary input outside {-1, 0, 1} */
+#define BITLINEAR_EHIP (-5)         /* a HIP runtime call or kernel launch failed */
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* bitlinear_status_string(int status);
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+int bitlinear_abi_version(void);
+
+/* Bytes of the packed device layout for an N x K ternary matrix (host only;
+ * 0 for invalid sizes). */
+size_t bitlinear_packed_bytes(int64_t N, int64_t K);
+
+/* Workspace bytes that bitlinear_pack_weights, bitlinear_forward and
+ * bitlinear_forward_f32 need for these sizes (host only; 0 for invalid
+ * sizes).  One workspace of this size serves all three; it must be 256-byte
+ * aligned. */
+size_t bitlinear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Per-token absmax INT8 activation quantization.
+ * [P1] "2. Absmax Dynamic Activation Quantization" (Q_b = 127) and the
+ * ActivationQuantizerSTE listing of "Production PyTorch Implementation:
+ * BitLinear b1.58 Layer"; [P4] "Activation Quantization: 8-Bit Absmax
+ * Scaling"; [P2] "2. Absmax Activation Quantization" (per token).
+ *   x    [M][K] float32 (in)
+ *   xq   [M][K] int8    (out)
+ *   eta  [M]    float32 (out)
+ *   xsum [M]    int32   (out, may be NULL): sum over k of xq[m][k]
+ */
+int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta,
+                           int32_t* xsum, void* stream);
+
+/*
+ * Absmean ternary weight quantization and packing.
+ * [P1] "1. Absmean Weight Quantization" and the WeightQuantizerSTE listing;
+ * [P2] "1. Absmean Weight Quantization"; [P4] "The Weight Quantization
+ * Function: Absmean Scaling"; packing as in the layout note above.
+ *   W          [N][K] float32 latent weights (in)
+ *   packed     bitlinear_packed_bytes(N, K) bytes (out)
+ *   gamma      float32 device scalar (out, may be NULL)
+ *   gamma_host float32 host scalar (out, may be NULL); when given, the call
+ *              synchronizes `stream` and returns with it written
+ *   ws         workspace of bitlinear_workspace_bytes(0, N, K) bytes
+ * gamma is the exact mean of |W| over all N*K entries, rounded once to the
+ * nearest float32 (ties to even), then clamped below at 1e-5; the result does
+ * not depend on summation order.
+ */
+int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                           float* gamma_host, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Pack ternary weights that are already in {-1, 0, 1} (e.g. drawn directly,
+ * with gamma supplied separately).
+ *   Wt     [N][K] int8 (in)
+ *   packed bitlinear_packed_bytes(N, K) bytes (out)
+ *   bad    int32 device scalar (out, may be NULL): set to the number of
+ *          entries outside {-1, 0, 1} (those are packed as 0)
+ * Asynchronous; a caller that needs BITLINEAR_EBADCODE reads `bad` after
+ * synchronizing.
+ */
+int bitlinear_pack_ternary(const int8_t* Wt, int64_t N, int64_t K, uint8_t* packed,
+                           int32_t* bad, void* stream);
+
+/*
+ * Unpack the device layout back to ternary int8 [N][K] (round trip, tests).
+ *   bad int32 device scalar (out, may be NULL): number of 11 codes found
+ *       inside [0, N) x [0, K) (decoded as 0).
+ */
+int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wt,
+                             int32_t* bad, void* stream);
+
+/*
+ * BitLinear forward from quantized activations: the multiplication-free
+ * ternary contraction and the fused dequantization.
+ * [P1] "The MatMul-Free Breakthrough" and pipeline boxes 4-5; [P2] "3.
+ * Additive Integer Accumulation"; [P5] "The Arithmetic Collapse" and the
+ * bitlinear_forward listing.
+ *   xq     [M][K] int8   (in)
+ *   eta    [M]    float32 (in)
+ *   packed device layout of the [N][K] ternary matrix (in)
+ *   gamma  the matrix's scale (by value)
+ *   y      [M][N] float32 (out)
+ *   y_int  [M][N] int32   (out, may be NULL): the exact integer sums
+ *   ws     workspace of bitlinear_workspace_bytes(M, N, K) bytes (may be NULL
+ *          with ws_bytes 0 when that size is 0)
+ */
+int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
+                      int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/*
+ * Fused forward from float32 activations: quantize (into the workspace),
+ * contract, dequantize.  Same arguments as above; ws is required.
+ * [P1] BitLinear158.forward steps 2, 4 and 5.
+ */
+int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, int64_t M,
+                          int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * Grouped forward: many independent BitLinear problems of the same token
+ * count M in one pass (e.g. every projection of every layer of a decode
+ * step).  Planning builds a work table in caller-owned device memory once;
+ * each forward then queues at most two kernels (quantize all, contract all).
+ */
+typedef struct bitlinear_problem {
+    const float* x;        /* [M][K] float32, or NULL: xq/eta already hold the quantized rows */
+    int8_t* xq;            /* [M][K] int8: written by the quantize stage when x != NULL */
+    float* eta;            /* [M] float32: likewise */
+    const uint8_t* packed; /* device layout of the [N][K] ternary matrix */
+    float* y;              /* [M][N] float32 output */
+    int32_t* y_int;        /* [M][N] int32 output or NULL */
+    float gamma;           /* the matrix's scale */
+    int32_t N;
+    int32_t K;
+    int32_t reserved;      /* must be 0 */
+} bitlinear_problem;
+
+/* Host-side handle of a plan; plain data owned by the caller. */
+typedef struct bitlinear_grouped_plan {
+    void* table;           /* device memory holding the work table */
+    size_t table_bytes;
+    int64_t units;         /* work units of the contraction kernel */
+    int64_t quant_rows;    /* rows the quantize stage handles (0: no stage) */
+    int32_t count;         /* number of problems */
+    int32_t M;             /* tokens per problem */
+    int32_t kernel;        /* contraction kernel variant chosen by the planner */
+    int32_t max_K;
+} bitlinear_grouped_plan;
+
+/* Device bytes the work table for these problems needs (host only). */
+size_t bitlinear_grouped_table_bytes(const bitlinear_problem* problems_host, int32_t count,
+                                     int64_t M);
+
+/* Validate the problems, build the work table in `table` (device memory of
+ * bitlinear_grouped_table_bytes bytes) and fill *plan.  Synchronizes `stream`
+ * (the table is uploaded from a host copy).  Problems may share x, xq and
+ * eta buffers only when they also share x. */
+int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t count, int64_t M,
+                                void* table, size_t table_bytes, bitlinear_grouped_plan* plan,
+                                void* stream);
+
+/* Queue the grouped forward described by a plan. */
+int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

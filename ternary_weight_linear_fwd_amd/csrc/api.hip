@@ -1,0 +1,282 @@
+// api.hip -- the C ABI declared in include/bitlinear.h.
+//
+// Host side only: argument validation (before anything is queued), workspace
+// carving, kernel choice by token count and the grouped planner.  All the
+// arithmetic of the forward pass runs in the kernels of quant.hip, pack.hip,
+// gemv.hip and gemm.hip.  Nothing here allocates device memory.
+#include <cstring>
+#include <map>
+#include <vector>
+
+#include "kernels.hpp"
+
+using namespace bl;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shared size rules: N, K in [1, 2^31), K % 16 == 0, N*K < 2^40, M in [0, 2^31).
+int check_sizes(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N <= 0 || K <= 0) return BITLINEAR_EINVAL;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return BITLINEAR_EUNSUPPORTED;
+    if (K % 16 != 0) return BITLINEAR_EUNSUPPORTED;
+    if (N * K >= (int64_t(1) << 40)) return BITLINEAR_EUNSUPPORTED;
+    if (M * K >= (int64_t(1) << 40) || M * N >= (int64_t(1) << 40)) return BITLINEAR_EUNSUPPORTED;
+    return BITLINEAR_OK;
+}
+
+size_t forward_ws_bytes(int64_t M, int64_t N, int64_t K) {
+    return M <= kGemvMaxM ? gemv_ws_bytes(M, N, K) : 0;
+}
+
+Problem make_problem(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
+                     int64_t N, int64_t K, float* y, int32_t* y_int) {
+    Problem p{};
+    p.xq = xq;
+    p.eta = eta;
+    p.packed = reinterpret_cast<const uint4*>(packed);
+    p.y = y;
+    p.y_int = y_int;
+    p.gamma = gamma;
+    p.N = (int32_t)N;
+    p.K = (int32_t)K;
+    p.Kb = (int32_t)ceil_div(K, 64);
+    return p;
+}
+
+int run_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma, int64_t M,
+                int64_t N, int64_t K, float* y, int32_t* y_int, void* ws, hipStream_t stream) {
+    if (M == 0) return BITLINEAR_OK;
+    const Problem p = make_problem(xq, eta, packed, gamma, N, K, y, y_int);
+    if (M <= kGemvMaxM) return launch_gemv(p, M, ws, stream);
+    return launch_gemm(p, M, stream);
+}
+
+struct TableLayout {
+    size_t problems_off, units_off, rows_off, bytes;
+};
+
+TableLayout table_layout(int64_t count, int64_t nunits, int64_t nrows) {
+    TableLayout t;
+    t.problems_off = 0;
+    t.units_off = align256((size_t)count * sizeof(Problem));
+    t.rows_off = t.units_off + align256((size_t)nunits * sizeof(Unit));
+    t.bytes = t.rows_off + align256((size_t)nrows * sizeof(QuantRow));
+    return t;
+}
+
+// Work units of the grouped contraction for one problem.
+int64_t problem_units(int64_t M, int64_t N) {
+    if (M <= kGemvMaxM) return ceil_div(N, 64);
+    return ceil_div(N, gemm_tile_n(M));
+}
+
+struct PlanHost {
+    std::vector<Problem> problems;
+    std::vector<Unit> units;
+    std::vector<QuantRow> rows;
+};
+
+int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& out) {
+    if (!pr || count <= 0 || M < 0 || M > kMaxDim) return BITLINEAR_EINVAL;
+    std::map<const int8_t*, const float*> xq_source;  // xq buffer -> its x
+    for (int32_t i = 0; i < count; ++i) {
+        const bitlinear_problem& q = pr[i];
+        if (q.reserved != 0) return BITLINEAR_EINVAL;
+        int rc = check_sizes(M, q.N, q.K);
+        if (rc) return rc;
+        if (!q.packed || !q.y || !q.xq || !q.eta) return BITLINEAR_EINVAL;
+        if (!aligned(q.packed, 16) || !aligned(q.xq, 16) || (q.x && !aligned(q.x, 16)))
+            return BITLINEAR_EINVAL;
+        auto it = xq_source.find(q.xq);
+        if (it == xq_source.end()) {
+            xq_source[q.xq] = q.x;
+            if (q.x) {
+                for (int64_t m = 0; m < M; ++m) {
+                    QuantRow r{};
+                    r.x = q.x + m * q.K;
+                    r.xq = q.xq + m * q.K;
+                    r.eta = q.eta + m;
+                    r.K = q.K;
+                    out.rows.push_back(r);
+                }
+            }
+        } else if (it->second != q.x) {
+            return BITLINEAR_EINVAL;  // one xq buffer fed from two different sources
+        }
+        Problem p = make_problem(q.xq, q.eta, q.packed, q.gamma, q.N, q.K, q.y, q.y_int);
+        p.unit_begin = (int32_t)out.units.size();
+        const int64_t nu = problem_units(M, q.N);
+        for (int64_t g = 0; g < nu; ++g) out.units.push_back(Unit{i, (int32_t)g});
+        out.problems.push_back(p);
+    }
+    if (out.units.size() >= (size_t)kMaxDim) return BITLINEAR_EUNSUPPORTED;
+    return BITLINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bitlinear_status_string(int status) {
+    switch (status) {
+        case BITLINEAR_OK: return "BITLINEAR_OK";
+        case BITLINEAR_EINVAL: return "BITLINEAR_EINVAL: invalid argument";
+        case BITLINEAR_EUNSUPPORTED: return "BITLINEAR_EUNSUPPORTED: unsupported size";
+        case BITLINEAR_EWORKSPACE: return "BITLINEAR_EWORKSPACE: workspace too small";
+        case BITLINEAR_EBADCODE: return "BITLINEAR_EBADCODE: value outside {-1, 0, 1}";
+        case BITLINEAR_EHIP: return "BITLINEAR_EHIP: HIP runtime error";
+        default: return "BITLINEAR_UNKNOWN";
+    }
+}
+
+int bitlinear_abi_version(void) { return 10000; }
+
+size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
+    if (check_sizes(0, N, K) != BITLINEAR_OK) return 0;
+    return (size_t)(ceil_div(N, 64) * ceil_div(K, 64) * kBlockBytes);
+}
+
+size_t bitlinear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (check_sizes(M, N, K) != BITLINEAR_OK) return 0;
+    const size_t f32 = align256((size_t)(M * K)) + align256((size_t)(4 * M)) +
+                       align256(forward_ws_bytes(M, N, K));
+    const size_t pack = align256(gamma_ws_bytes());
+    return f32 > pack ? f32 : pack;
+}
+
+int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta,
+                           int32_t* xsum, void* stream) {
+    int rc = check_sizes(M, 1, K);
+    if (rc) return rc;
+    if (!x || !xq || !eta) return BITLINEAR_EINVAL;
+    if (!aligned(x, 16) || !aligned(xq, 16)) return BITLINEAR_EINVAL;
+    return launch_quantize(x, M, K, xq, eta, xsum, (hipStream_t)stream);
+}
+
+int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
+                           float* gamma_host, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sizes(0, N, K);
+    if (rc) return rc;
+    if (!W || !packed) return BITLINEAR_EINVAL;
+    if (!aligned(W, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
+    if (!ws || !aligned(ws, 256) || ws_bytes < gamma_ws_bytes()) return BITLINEAR_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    rc = launch_pack_weights(W, N, K, packed, gamma, ws, s);
+    if (rc) return rc;
+    if (gamma_host) {
+        const float* g = (const float*)((const char*)ws + kGammaBins * sizeof(unsigned long long));
+        BL_HIP_CHECK(hipMemcpyAsync(gamma_host, g, sizeof(float), hipMemcpyDeviceToHost, s));
+        BL_HIP_CHECK(hipStreamSynchronize(s));
+    }
+    return BITLINEAR_OK;
+}
+
+int bitlinear_pack_ternary(const int8_t* Wt, int64_t N, int64_t K, uint8_t* packed, int32_t* bad,
+                           void* stream) {
+    int rc = check_sizes(0, N, K);
+    if (rc) return rc;
+    if (!Wt || !packed) return BITLINEAR_EINVAL;
+    if (!aligned(Wt, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
+    return launch_pack_ternary(Wt, N, K, packed, bad, (hipStream_t)stream);
+}
+
+int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wt, int32_t* bad,
+                             void* stream) {
+    int rc = check_sizes(0, N, K);
+    if (rc) return rc;
+    if (!Wt || !packed) return BITLINEAR_EINVAL;
+    if (!aligned(Wt, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
+    return launch_unpack(packed, N, K, Wt, bad, (hipStream_t)stream);
+}
+
+int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
+                      int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,
+                      size_t ws_bytes, void* stream) {
+    int rc = check_sizes(M, N, K);
+    if (rc) return rc;
+    if (!xq || !eta || !packed || !y) return BITLINEAR_EINVAL;
+    if (!aligned(xq, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
+    const size_t need = forward_ws_bytes(M, N, K);
+    if (need && (!ws || !aligned(ws, 256) || ws_bytes < need)) return BITLINEAR_EWORKSPACE;
+    return run_forward(xq, eta, packed, gamma, M, N, K, y, y_int, ws, (hipStream_t)stream);
+}
+
+int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, int64_t M, int64_t N,
+                          int64_t K, float* y, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sizes(M, N, K);
+    if (rc) return rc;
+    if (!x || !packed || !y) return BITLINEAR_EINVAL;
+    if (!aligned(x, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
+    const size_t xq_bytes = align256((size_t)(M * K)), eta_bytes = align256((size_t)(4 * M));
+    const size_t need = xq_bytes + eta_bytes + align256(forward_ws_bytes(M, N, K));
+    if (!ws || !aligned(ws, 256) || ws_bytes < need) return BITLINEAR_EWORKSPACE;
+    if (M == 0) return BITLINEAR_OK;
+    int8_t* xq = (int8_t*)ws;
+    float* eta = (float*)((char*)ws + xq_bytes);
+    void* rest = (char*)ws + xq_bytes + eta_bytes;
+    hipStream_t s = (hipStream_t)stream;
+    rc = launch_quantize(x, M, K, xq, eta, nullptr, s);
+    if (rc) return rc;
+    return run_forward(xq, eta, packed, gamma, M, N, K, y, nullptr, rest, s);
+}
+
+size_t bitlinear_grouped_table_bytes(const bitlinear_problem* problems_host, int32_t count,
+                                     int64_t M) {
+    PlanHost h;
+    if (build_plan(problems_host, count, M, h) != BITLINEAR_OK) return 0;
+    return table_layout(count, (int64_t)h.units.size(), (int64_t)h.rows.size()).bytes;
+}
+
+int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t count, int64_t M,
+                                void* table, size_t table_bytes, bitlinear_grouped_plan* plan,
+                                void* stream) {
+    if (!plan) return BITLINEAR_EINVAL;
+    PlanHost h;
+    int rc = build_plan(problems_host, count, M, h);
+    if (rc) return rc;
+    const TableLayout L = table_layout(count, (int64_t)h.units.size(), (int64_t)h.rows.size());
+    if (!table || !aligned(table, 256) || table_bytes < L.bytes) return BITLINEAR_EWORKSPACE;
+    std::vector<uint8_t> host(L.bytes, 0);
+    std::memcpy(host.data() + L.problems_off, h.problems.data(), h.problems.size() * sizeof(Problem));
+    std::memcpy(host.data() + L.units_off, h.units.data(), h.units.size() * sizeof(Unit));
+    if (!h.rows.empty())
+        std::memcpy(host.data() + L.rows_off, h.rows.data(), h.rows.size() * sizeof(QuantRow));
+    hipStream_t s = (hipStream_t)stream;
+    BL_HIP_CHECK(hipMemcpyAsync(table, host.data(), L.bytes, hipMemcpyHostToDevice, s));
+    BL_HIP_CHECK(hipStreamSynchronize(s));
+    int max_K = 0;
+    for (const Problem& p : h.problems) max_K = p.K > max_K ? p.K : max_K;
+    plan->table = table;
+    plan->table_bytes = L.bytes;
+    plan->units = (int64_t)h.units.size();
+    plan->quant_rows = (int64_t)h.rows.size();
+    plan->count = count;
+    plan->M = (int32_t)M;
+    plan->kernel = M <= kGemvMaxM ? 0 : 1;
+    plan->max_K = max_K;
+    return BITLINEAR_OK;
+}
+
+int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) {
+    if (!plan || !plan->table || plan->count <= 0 || plan->M < 0) return BITLINEAR_EINVAL;
+    if (plan->M == 0) return BITLINEAR_OK;
+    const TableLayout L = table_layout(plan->count, plan->units, plan->quant_rows);
+    if (plan->table_bytes < L.bytes) return BITLINEAR_EINVAL;
+    const char* base = (const char*)plan->table;
+    const Problem* problems = (const Problem*)(base + L.problems_off);
+    const Unit* units = (const Unit*)(base + L.units_off);
+    const QuantRow* rows = (const QuantRow*)(base + L.rows_off);
+    hipStream_t s = (hipStream_t)stream;
+    int rc = BITLINEAR_OK;
+    if (plan->quant_rows) rc = launch_quantize_grouped(rows, plan->quant_rows, s);
+    if (rc) return rc;
+    if (plan->kernel == 0) return launch_gemv_grouped(problems, units, plan->units, plan->M, s);
+    return launch_gemm_grouped(problems, units, plan->units, plan->M, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// kernels.hpp -- descriptors and launchers of the gfx950 kernels; the C ABI in
+// api.hip validates arguments and calls these.
+#pragma once
+
+#include "common.hpp"
+
+namespace bl {
+
+// One row of the grouped quantize stage.
+struct QuantRow {
+    const float* x;  // [K] float32
+    int8_t* xq;      // [K] int8
+    float* eta;      // scalar
+    int32_t K;
+    int32_t pad;
+};
+
+// One BitLinear contraction problem as the kernels see it.
+struct Problem {
+    const int8_t* xq;       // [M][K]
+    const float* eta;       // [M]
+    const uint4* packed;    // device layout, 16-byte row chunks
+    float* y;               // [M][N]
+    int32_t* y_int;         // [M][N] or null
+    float gamma;
+    int32_t N, K;
+    int32_t Kb;             // ceil(K / 64)
+    int32_t unit_begin;     // first work unit of this problem in a grouped table
+    int32_t pad;
+};
+static_assert(sizeof(Problem) == 64, "Problem descriptor is one 64-byte line");
+
+// One work unit of the grouped decode kernel: (problem, 64-row group).
+struct Unit {
+    int32_t problem;
+    int32_t group;
+};
+
+// Split-K partial sums of the single-problem decode path.
+struct SplitK {
+    int32_t* partial;       // [S][M][N] int32, or null when S == 1
+    int32_t S;              // number of k-slices
+    int32_t kb_per_slice;   // k-blocks per slice
+};
+
+// ---- activation quantization (quant.hip)
+int launch_quantize(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta, int32_t* xsum,
+                    hipStream_t stream);
+int launch_quantize_grouped(const QuantRow* rows, int64_t nrows, hipStream_t stream);
+
+// ---- weight quantization and packing (pack.hip)
+constexpr int kGammaBins = 256;  // bins[t] collects significands of 2^(t-149) units
+size_t gamma_ws_bytes();
+int launch_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma_dev,
+                        void* ws, hipStream_t stream);
+int launch_pack_ternary(const int8_t* Wt, int64_t N, int64_t K, uint8_t* packed, int32_t* bad,
+                        hipStream_t stream);
+int launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wt, int32_t* bad,
+                  hipStream_t stream);
+int launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+// ---- decode contraction, dot4 path for M <= 4 (gemv.hip)
+constexpr int kGemvMaxM = 4;
+int gemv_split_slices(int64_t M, int64_t N, int64_t K);
+size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K);
+int launch_gemv(const Problem& p, int64_t M, void* ws, hipStream_t stream);
+int launch_gemv_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
+                        hipStream_t stream);
+
+// ---- int8 MFMA contraction for M > 4 (gemm.hip)
+int launch_gemm(const Problem& p, int64_t M, hipStream_t stream);
+int gemm_tile_n(int64_t M);  // output rows per workgroup (column tile) for M
+int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
+                        hipStream_t stream);
+
+}  // namespace bl

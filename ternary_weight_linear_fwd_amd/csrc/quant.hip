@@ -1,0 +1,158 @@
+// quant.hip -- per-token absmax INT8 activation quantization on gfx950.
+//
+// [P1] "2. Absmax Dynamic Activation Quantization" and the
+// ActivationQuantizerSTE listing; [P4] "Activation Quantization: 8-Bit Absmax
+// Scaling"; [P2] "2. Absmax Activation Quantization" (per token).
+//
+// One workgroup per token row.  Pass 1 reduces max |x| with wavefront
+// butterflies (DPP/permute) and one LDS exchange across the workgroup's
+// waves; pass 2 quantizes with one IEEE multiply, one correctly rounded
+// division and round-half-even per element and stores four int8 per dword.
+// Rows whose float4 chunks fit the register budget (R per thread) are read
+// from HBM once; longer rows are read a second time (from L2/MALL).
+#include "kernels.hpp"
+
+namespace bl {
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ inline int8_t quant_one(float x, float eta) {
+    float scaled = __fmul_rn(x, kQb);   // x * 127
+    float q = __fdiv_rn(scaled, eta);   // ... / eta (IEEE division)
+    float r = rintf(q);                 // round half to even
+    r = fminf(fmaxf(r, -128.0f), 127.0f);
+    return (int8_t)(int)r;
+}
+
+__device__ inline uint32_t quant4(float4 v, float eta, int& sum) {
+    int8_t a = quant_one(v.x, eta), b = quant_one(v.y, eta), c = quant_one(v.z, eta),
+           d = quant_one(v.w, eta);
+    sum += (int)a + (int)b + (int)c + (int)d;
+    return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
+           ((uint32_t)(uint8_t)d << 24);
+}
+
+// Block-wide reductions through LDS (one slot per wave).
+template <int THREADS>
+__device__ inline float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < THREADS / 64; ++w) r = fmaxf(r, red[w]);
+    __syncthreads();
+    return r;
+}
+
+template <int THREADS>
+__device__ inline int block_sum(int v, int* red) {
+    v = wave_sum(v);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    int r = 0;
+#pragma unroll
+    for (int w = 0; w < THREADS / 64; ++w) r += red[w];
+    return r;
+}
+
+// Quantize one row of K floats (K % 4 == 0, 16-byte aligned).
+template <int THREADS, int R>
+__device__ inline void quant_row(const float* __restrict__ x, int K, int8_t* __restrict__ xq,
+                                 float* __restrict__ eta_out, int32_t* __restrict__ xsum_out) {
+    __shared__ float redf[THREADS / 64];
+    __shared__ int redi[THREADS / 64];
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    uint32_t* q4 = reinterpret_cast<uint32_t*>(xq);
+    const int n4 = K >> 2;
+    const int t = threadIdx.x;
+
+    float amax = 0.0f;
+    float4 cache[R > 0 ? R : 1];
+    if constexpr (R > 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = t + r * THREADS;
+            cache[r] = i < n4 ? ldnt_f4(&x4[i]) : make_float4(0, 0, 0, 0);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(cache[r].x), fabsf(cache[r].y)),
+                                     fmaxf(fabsf(cache[r].z), fabsf(cache[r].w))));
+        }
+    } else {
+        for (int i = t; i < n4; i += THREADS) {
+            float4 v = x4[i];
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+    }
+    amax = block_max<THREADS>(amax, redf);
+    const float eta = amax < kScaleFloor ? kScaleFloor : amax;
+
+    int sum = 0;
+    if constexpr (R > 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = t + r * THREADS;
+            if (i < n4) q4[i] = quant4(cache[r], eta, sum);
+        }
+    } else {
+        for (int i = t; i < n4; i += THREADS) q4[i] = quant4(x4[i], eta, sum);
+    }
+    if (t == 0) eta_out[0] = eta;
+    if (xsum_out) {
+        sum = block_sum<THREADS>(sum, redi);
+        if (t == 0) xsum_out[0] = sum;
+    }
+}
+
+template <int THREADS, int R>
+__global__ __launch_bounds__(THREADS) void quant_rows_kernel(const float* __restrict__ x, int K,
+                                                             int8_t* __restrict__ xq,
+                                                             float* __restrict__ eta,
+                                                             int32_t* __restrict__ xsum) {
+    const int64_t m = blockIdx.x;
+    quant_row<THREADS, R>(x + m * K, K, xq + m * K, eta + m, xsum ? xsum + m : nullptr);
+}
+
+// Grouped: one workgroup per row descriptor.
+__global__ __launch_bounds__(256) void quant_rows_grouped_kernel(const QuantRow* __restrict__ rows) {
+    const QuantRow r = rows[blockIdx.x];
+    quant_row<256, 0>(r.x, r.K, r.xq, r.eta, nullptr);
+}
+
+int launch_quantize(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta, int32_t* xsum,
+                    hipStream_t stream) {
+    if (M == 0) return BITLINEAR_OK;
+    const int n4 = (int)(K / 4);
+    dim3 grid((unsigned)M);
+#define BL_QL(T, R) hipLaunchKernelGGL((quant_rows_kernel<T, R>), grid, dim3(T), 0, stream, x, (int)K, xq, eta, xsum)
+    if (n4 <= 256) BL_QL(256, 1);
+    else if (n4 <= 512) BL_QL(256, 2);
+    else if (n4 <= 1024) BL_QL(256, 4);
+    else if (n4 <= 2048) BL_QL(256, 8);
+    else if (n4 <= 4096) BL_QL(512, 8);
+    else if (n4 <= 8192) BL_QL(1024, 8);
+    else BL_QL(1024, 0);
+#undef BL_QL
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
+
+int launch_quantize_grouped(const QuantRow* rows, int64_t nrows, hipStream_t stream) {
+    if (nrows == 0) return BITLINEAR_OK;
+    hipLaunchKernelGGL(quant_rows_grouped_kernel, dim3((unsigned)nrows), dim3(256), 0, stream, rows);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
+
+}  // namespace bl

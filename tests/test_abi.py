@@ -1,0 +1,139 @@
+"""The C ABI library on the CPU: it loads without a GPU, exports every call
+include/bitlinear.h declares, the header compiles as C and C++, host-only size
+queries are right, and argument validation returns the documented status
+before anything touches a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+CSRC = os.path.join(ROOT, "ternary_weight_linear_fwd_amd", "csrc")
+
+bl = pytest.importorskip("ternary_weight_linear_fwd_amd.bitlinear",
+                         reason="libbitlinear.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(bl.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bl.EXPORTED)
+    out = subprocess.check_output(["nm", "-D", "--defined-only", bl.LIB_PATH], text=True)
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+
+
+@pytest.mark.parametrize("lang,compiler", [("c", "gcc"), ("c++", "g++")])
+def test_header_compiles(lang, compiler, tmp_path):
+    src = tmp_path / ("t." + ("c" if lang == "c" else "cpp"))
+    src.write_text('#include "bitlinear.h"\nint main(void){ bitlinear_problem p; (void)p; '
+                   'return (int)sizeof(bitlinear_grouped_plan) > 0 ? 0 : 1; }\n')
+    subprocess.check_call([compiler, "-std=c99" if lang == "c" else "-std=c++11", "-Wall",
+                           "-Werror", "-pedantic", "-I", os.path.dirname(HEADER), "-fsyntax-only",
+                           str(src)])
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(bl.BitLinearProblem) == 64
+    assert ctypes.sizeof(bl.BitLinearGroupedPlan) == 48
+
+
+def test_status_strings():
+    assert bl.bitlinear_status_string(0) == "BITLINEAR_OK"
+    for code in (-1, -2, -3, -4, -5):
+        assert bl.bitlinear_status_string(code).startswith("BITLINEAR_E")
+    assert bl.bitlinear_status_string(7) == "BITLINEAR_UNKNOWN"
+    assert bl.bitlinear_abi_version() == 10000
+
+
+def test_packed_bytes():
+    assert bl.bitlinear_packed_bytes(64, 64) == 1024
+    assert bl.bitlinear_packed_bytes(2048, 2048) == 2048 * 2048 // 4
+    assert bl.bitlinear_packed_bytes(8640, 3200) == 8640 * 3200 // 4
+    assert bl.bitlinear_packed_bytes(1, 16) == 1024          # one padded block
+    assert bl.bitlinear_packed_bytes(65, 80) == 2 * 2 * 1024
+    assert bl.bitlinear_packed_bytes(8, 15) == 0              # K % 16 != 0
+    assert bl.bitlinear_packed_bytes(0, 64) == 0
+    assert bl.bitlinear_packed_bytes(1 << 20, 1 << 20) == 0   # N*K >= 2^40
+
+
+def test_workspace_bytes():
+    for M, N, K in ((1, 2048, 2048), (8, 3200, 8640), (2048, 8640, 3200), (0, 64, 64)):
+        ws = bl.bitlinear_workspace_bytes(M, N, K)
+        assert ws >= M * K + 4 * M and ws % 256 == 0 and ws >= 2048
+    assert bl.bitlinear_workspace_bytes(-1, 64, 64) == 0
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced by a rejected call
+
+
+def _rc(fn, *args):
+    return getattr(bl._lib, fn)(*args)
+
+
+def test_validation_before_any_device_work():
+    L = bl
+    # quantize: null pointers, bad sizes, misalignment
+    assert _rc("bitlinear_quantize_act", None, 1, 64, FAKE, FAKE, None, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_quantize_act", FAKE, -1, 64, FAKE, FAKE, None, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_quantize_act", FAKE, 1, 24, FAKE, FAKE, None, None) == L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_quantize_act", FAKE + 4, 1, 64, FAKE, FAKE, None, None) == L.BITLINEAR_EINVAL
+    # pack: workspace required
+    assert _rc("bitlinear_pack_weights", FAKE, 64, 64, FAKE, None, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_pack_weights", FAKE, 64, 64, FAKE, None, None, FAKE, 16, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_pack_weights", FAKE, 64, 0, FAKE, None, None, FAKE, 1 << 16, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_pack_ternary", None, 64, 64, FAKE, None, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_unpack_weights", FAKE, 64, 20, FAKE, None, None) == L.BITLINEAR_EUNSUPPORTED
+    # forward: null output, bad K, split-K workspace missing
+    assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 64, 64, None, None, None, 0, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 64, 48 + 1, FAKE, None, None, 0, None) == L.BITLINEAR_EUNSUPPORTED
+    need = L.bitlinear_workspace_bytes(1, 8192, 8192)
+    assert need > 0
+    assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, FAKE + 8, 1 << 20, None) == L.BITLINEAR_EWORKSPACE
+
+
+def test_grouped_planner_validation():
+    def probs(n, **over):
+        specs = []
+        for i in range(n):
+            s = dict(x=None, xq=FAKE + 4096 * i, eta=FAKE + 256, packed=FAKE, y=FAKE, gamma=0.5,
+                     N=128, K=64)
+            s.update(over)
+            specs.append(s)
+        return bl.make_problems(specs)
+
+    ok = probs(3)
+    assert bl.bitlinear_grouped_table_bytes(ok, 3, 1) > 0
+    assert bl.bitlinear_grouped_table_bytes(ok, 0, 1) == 0
+    assert bl.bitlinear_grouped_table_bytes(probs(2, K=40), 2, 1) == 0
+    bad = probs(2)
+    bad[1].reserved = 1
+    assert bl.bitlinear_grouped_table_bytes(bad, 2, 1) == 0
+    # one xq buffer fed from two different float32 sources
+    clash = bl.make_problems([dict(x=FAKE, xq=FAKE, eta=FAKE, packed=FAKE, y=FAKE, gamma=1, N=64, K=64),
+                              dict(x=FAKE + 4096, xq=FAKE, eta=FAKE, packed=FAKE, y=FAKE, gamma=1, N=64, K=64)])
+    assert bl.bitlinear_grouped_table_bytes(clash, 2, 1) == 0
+    plan = bl.BitLinearGroupedPlan()
+    rc = bl._lib.bitlinear_grouped_plan_init(ok, 3, 1, None, 0, ctypes.byref(plan), None)
+    assert rc == bl.BITLINEAR_EWORKSPACE
+
+
+def test_library_never_allocates():
+    for f in os.listdir(CSRC):
+        text = open(os.path.join(CSRC, f)).read()
+        for banned in ("hipMalloc", "hipFree", "hipHostMalloc", "malloc(", "new "):
+            assert banned not in text, (f, banned)

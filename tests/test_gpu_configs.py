@@ -1,0 +1,98 @@
+"""GPU parity on the five workloads at their full sizes.
+
+Where the oracle would take minutes (it runs about 0.16 G weight-ops per second
+per thread, by design), the HIP path still computes every output; the oracle
+then checks (a) a seeded sample of token rows in full and (b) two exact
+checksums of every row that hold at any size:
+    sum_n y_int[m][n]       = sum_k xq[m][k] * colsum(W~)[k]
+    sum_n r_n * y_int[m][n] = sum_k xq[m][k] * (W~^T r)[k]   (r_n random in [-3, 3])
+computed in int64 from the oracle's xq and W~."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (assert_y_close, forward, forward_f32, pack_ternary, pack_weights, say)
+from ternary_weight_linear_fwd_amd import synthetic as S
+
+pytestmark = pytest.mark.gpu
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def checksums_ok(y_int, xq, Wt, seed):
+    r = np.random.default_rng(seed).integers(-3, 4, Wt.shape[0]).astype(np.int64)
+    colsum = Wt.astype(np.int64).sum(axis=0)
+    proj = Wt.astype(np.int64).T @ r
+    x64 = xq.astype(np.int64)
+    assert np.array_equal(y_int.astype(np.int64).sum(axis=1), x64 @ colsum)
+    assert np.array_equal(y_int.astype(np.int64) @ r, x64 @ proj)
+
+
+def check_layer(x, Wt, g, packed, sample_rows=None, seed=0):
+    M, K = x.shape
+    N = Wt.shape[0]
+    xq, eta = oracle.quantize_act(x)
+    y, y_int = forward(xq, eta, packed, g, N)
+    rows = np.arange(M) if sample_rows is None or sample_rows >= M else \
+        np.sort(np.random.default_rng(seed).choice(M, sample_rows, replace=False))
+    y_ref, y_int_ref = oracle.forward_q(xq[rows], eta[rows], Wt, g, threads=THREADS)
+    assert np.array_equal(y_int[rows], y_int_ref)
+    assert_y_close(y[rows], y_ref)
+    assert np.array_equal(y[rows].view(np.uint32), y_ref.view(np.uint32))
+    checksums_ok(y_int, xq, Wt, seed)
+    return y
+
+
+def test_c1_single_layer():
+    W, x = S.c1_inputs()
+    packed, g = pack_weights(W)
+    Wt, g_ref = oracle.quantize_weights(W)
+    assert g == g_ref
+    say(f"C1 gamma={g!r} zeros={float((Wt == 0).mean()):.4f}")
+    check_layer(x, Wt, g, packed)
+    y_ref, *_ = oracle.forward(x, Wt, g)
+    assert_y_close(forward_f32(x, packed, g, 2048), y_ref)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_c2_block_decode(M):
+    for p in S.C2_PROJS:
+        say(f"C2 {p.name} M={M}")
+        W = S.c2_weight(p)
+        packed, g = pack_weights(W)
+        Wt, g_ref = oracle.quantize_weights(W)
+        assert g == g_ref
+        check_layer(S.c2_x(p, M), Wt, g, packed, seed=p.index)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("which", [0, 1])
+def test_c3_prefill(which):
+    W, x = S.c3_inputs(which)
+    say(f"C3 gemm {which}: M={x.shape[0]} K={x.shape[1]} N={W.shape[0]}")
+    packed, g = pack_weights(W)
+    Wt, g_ref = oracle.quantize_weights(W)
+    assert g == g_ref
+    check_layer(x, Wt, g, packed, sample_rows=24, seed=which)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M", [32, 64, 128])
+def test_c5_fused_end_to_end(M):
+    for p in S.C5_PROJS:
+        say(f"C5 {p.name} M={M}")
+        Wt, g = S.c5_ternary(p)
+        packed, bad = pack_ternary(Wt)
+        assert bad == 0
+        x = S.c5_x(p, M)
+        y = forward_f32(x, packed, g, p.N)
+        rows = np.sort(np.random.default_rng(p.index).choice(M, 8, replace=False))
+        y_ref, xq, eta, y_int_ref = oracle.forward(x[rows], Wt, g, threads=THREADS)
+        assert_y_close(y[rows], y_ref)
+        assert np.array_equal(y[rows].view(np.uint32), y_ref.view(np.uint32))
+        # every row: the unfused path's integer sums satisfy the checksums
+        xq_all, eta_all = oracle.quantize_act(x)
+        y2, y_int = forward(xq_all, eta_all, packed, g, p.N)
+        assert np.array_equal(y2.view(np.uint32), y.view(np.uint32))
+        checksums_ok(y_int, xq_all, Wt, p.index)

@@ -1,0 +1,95 @@
+"""GPU parity of the contraction and dequant epilogue: int32 sums bit-exact,
+float32 outputs within 1e-6 relative (and, with the same operation order,
+identical), across every kernel variant, ragged tiles and edge cases."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (assert_y_close, forward, forward_f32, pack_ternary, pack_weights, say)
+from ternary_weight_linear_fwd_amd import synthetic as S
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(M, N, K, seed, dist="normal", latent=True):
+    say(f"forward M={M} N={N} K={K} seed={seed}")
+    x = S.random_x(seed, M, K, dist)
+    if latent:
+        W = S.random_latent(seed + 1, N, K)
+        packed, g = pack_weights(W)
+        Wt, g_ref = oracle.quantize_weights(W)
+        assert g == g_ref
+    else:
+        Wt = S.random_ternary(seed + 1, N, K)
+        g = np.float32(0.0173)
+        packed, bad = pack_ternary(Wt)
+        assert bad == 0
+    xq, eta = oracle.quantize_act(x)
+    y, y_int = forward(xq, eta, packed, g, N)
+    y_ref, y_int_ref = oracle.forward_q(xq, eta, Wt, g, threads=8)
+    assert np.array_equal(y_int, y_int_ref), np.argwhere(y_int != y_int_ref)[:5]
+    assert_y_close(y, y_ref)
+    assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+    # fused path from float32 activations
+    yf = forward_f32(x, packed, g, N)
+    assert_y_close(yf, y_ref)
+
+
+# Every token count class: dot4 path (1..4), MFMA with 1, 2 and 4 M-tiles per
+# wave (<=16, <=32, <=64) and the 128-row prefill tiles (> 64), each with
+# ragged N (not a multiple of 64 or of the column tile) and K (tail blocks).
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16, 17, 32, 33, 64, 65, 128, 130, 257])
+def test_token_counts(M):
+    run_case(M, 200, 208, seed=1000 + M)
+
+
+@pytest.mark.parametrize("N,K", [(1, 16), (63, 32), (64, 48), (65, 64), (129, 80), (256, 1024),
+                                 (333, 1040), (1000, 4160)])
+@pytest.mark.parametrize("M", [1, 4, 16, 96])
+def test_ragged_shapes(M, N, K):
+    run_case(M, N, K, seed=M * 131 + N * 7 + K)
+
+
+def test_heavy_tails_and_direct_ternary():
+    run_case(64, 512, 1024, seed=5, dist="t3")
+    run_case(3, 777, 528, seed=6, latent=False)
+    run_case(128, 384, 2048, seed=7, latent=False)
+
+
+def test_extreme_sums():
+    # every xq = +-127 and every weight +-1: |y_int| = 127 * K, the largest magnitude
+    M, N, K = 4, 128, 28672
+    x = np.ones((M, K), np.float32)
+    x[1] *= -1
+    x[2, ::2] = -1
+    Wt = np.ones((N, K), np.int8)
+    Wt[1::2] = -1
+    packed, _ = pack_ternary(Wt)
+    xq, eta = oracle.quantize_act(x)
+    for m in (4, 16, 64):
+        xqm = np.resize(xq, (m, K)).astype(np.int8)
+        etam = np.resize(eta, m).astype(np.float32)
+        y, y_int = forward(xqm, etam, packed, np.float32(1.0), N)
+        ref = oracle.ternary_contract(xqm, Wt, threads=8)
+        assert np.array_equal(y_int, ref)
+        assert np.abs(ref).max() == 127 * K
+
+
+def test_zero_inputs():
+    M, N, K = 8, 64, 64
+    packed, g = pack_weights(np.zeros((N, K), np.float32))
+    assert g == np.float32(1e-5)
+    xq, eta = oracle.quantize_act(np.zeros((M, K), np.float32))
+    y, y_int = forward(xq, eta, packed, g, N)
+    assert not y_int.any() and not y.any()
+
+
+def test_determinism():
+    M, N, K = 2, 8192, 8192   # split-K path
+    x = S.random_x(11, M, K)
+    Wt = S.random_ternary(12, N, K)
+    packed, _ = pack_ternary(Wt)
+    xq, eta = oracle.quantize_act(x)
+    a = forward(xq, eta, packed, 0.02, N)
+    b = forward(xq, eta, packed, 0.02, N)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
