@@ -72,6 +72,11 @@ const char* bitlinear_status_string(int status);
 /* Version of this ABI (major * 10000 + minor * 100 + patch). */
 int bitlinear_abi_version(void);
 
+/* The HIP error behind the most recent BITLINEAR_EHIP returned on this host
+ * thread: error name, code and the failing call (static thread-local storage;
+ * never NULL). */
+const char* bitlinear_last_error(void);
+
 /* Bytes of the packed device layout for an N x K ternary matrix (host only;
  * 0 for invalid sizes). */
 size_t bitlinear_packed_bytes(int64_t N, int64_t K);

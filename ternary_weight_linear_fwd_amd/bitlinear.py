@@ -17,6 +17,11 @@ from typing import Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
+# torch ships its own HIP runtime (same SONAME, libamdhip64.so.7).  Load it
+# first so that the library binds to that one copy: two HIP runtimes in one
+# process do not share devices, streams or memory.
+import torch  # noqa: E402,F401
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build it with `python -m ternary_weight_linear_fwd_amd.build` "
@@ -53,6 +58,7 @@ class BitLinearGroupedPlan(ctypes.Structure):
 _SIGS = {
     "bitlinear_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "bitlinear_abi_version": ([], ctypes.c_int),
+    "bitlinear_last_error": ([], ctypes.c_char_p),
     "bitlinear_packed_bytes": ([_I64, _I64], _SZ),
     "bitlinear_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "bitlinear_quantize_act": ([_P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
@@ -77,7 +83,8 @@ EXPORTED = tuple(_SIGS)
 
 class BitLinearError(RuntimeError):
     def __init__(self, status: int, what: str):
-        super().__init__(f"{what}: {bitlinear_status_string(status)} ({status})")
+        detail = f" [{bitlinear_last_error()}]" if status == BITLINEAR_EHIP else ""
+        super().__init__(f"{what}: {bitlinear_status_string(status)} ({status}){detail}")
         self.status = status
 
 
@@ -111,6 +118,10 @@ def bitlinear_status_string(status: int) -> str:
 
 def bitlinear_abi_version() -> int:
     return _lib.bitlinear_abi_version()
+
+
+def bitlinear_last_error() -> str:
+    return _lib.bitlinear_last_error().decode()
 
 
 def bitlinear_packed_bytes(N: int, K: int) -> int:

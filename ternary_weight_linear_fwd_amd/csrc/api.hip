@@ -4,6 +4,7 @@
 // carving, kernel choice by token count and the grouped planner.  All the
 // arithmetic of the forward pass runs in the kernels of quant.hip, pack.hip,
 // gemv.hip and gemm.hip.  Nothing here allocates device memory.
+#include <cstdio>
 #include <cstring>
 #include <map>
 #include <vector>
@@ -12,7 +13,19 @@
 
 using namespace bl;
 
+namespace bl {
+static thread_local char g_last_error[256] = "no error";
+
+void set_hip_error(hipError_t e, const char* where) {
+    snprintf(g_last_error, sizeof(g_last_error), "%s (%d) in %s", hipGetErrorName(e), (int)e, where);
+}
+}  // namespace bl
+
 namespace {
+
+// Clear the process-wide sticky HIP error left by any earlier call outside
+// this library before queueing work.
+inline void clear_hip_error() { (void)hipGetLastError(); }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 
@@ -136,6 +149,8 @@ const char* bitlinear_status_string(int status) {
 
 int bitlinear_abi_version(void) { return 10000; }
 
+const char* bitlinear_last_error(void) { return g_last_error; }
+
 size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
     if (check_sizes(0, N, K) != BITLINEAR_OK) return 0;
     return (size_t)(ceil_div(N, 64) * ceil_div(K, 64) * kBlockBytes);
@@ -155,6 +170,7 @@ int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, flo
     if (rc) return rc;
     if (!x || !xq || !eta) return BITLINEAR_EINVAL;
     if (!aligned(x, 16) || !aligned(xq, 16)) return BITLINEAR_EINVAL;
+    clear_hip_error();
     return launch_quantize(x, M, K, xq, eta, xsum, (hipStream_t)stream);
 }
 
@@ -166,6 +182,7 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed
     if (!aligned(W, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
     if (!ws || !aligned(ws, 256) || ws_bytes < gamma_ws_bytes()) return BITLINEAR_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
+    clear_hip_error();
     rc = launch_pack_weights(W, N, K, packed, gamma, ws, s);
     if (rc) return rc;
     if (gamma_host) {
@@ -182,6 +199,7 @@ int bitlinear_pack_ternary(const int8_t* Wt, int64_t N, int64_t K, uint8_t* pack
     if (rc) return rc;
     if (!Wt || !packed) return BITLINEAR_EINVAL;
     if (!aligned(Wt, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
+    clear_hip_error();
     return launch_pack_ternary(Wt, N, K, packed, bad, (hipStream_t)stream);
 }
 
@@ -191,6 +209,7 @@ int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t
     if (rc) return rc;
     if (!Wt || !packed) return BITLINEAR_EINVAL;
     if (!aligned(Wt, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
+    clear_hip_error();
     return launch_unpack(packed, N, K, Wt, bad, (hipStream_t)stream);
 }
 
@@ -203,6 +222,7 @@ int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed,
     if (!aligned(xq, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
     const size_t need = forward_ws_bytes(M, N, K);
     if (need && (!ws || !aligned(ws, 256) || ws_bytes < need)) return BITLINEAR_EWORKSPACE;
+    clear_hip_error();
     return run_forward(xq, eta, packed, gamma, M, N, K, y, y_int, ws, (hipStream_t)stream);
 }
 
@@ -220,6 +240,7 @@ int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, in
     float* eta = (float*)((char*)ws + xq_bytes);
     void* rest = (char*)ws + xq_bytes + eta_bytes;
     hipStream_t s = (hipStream_t)stream;
+    clear_hip_error();
     rc = launch_quantize(x, M, K, xq, eta, nullptr, s);
     if (rc) return rc;
     return run_forward(xq, eta, packed, gamma, M, N, K, y, nullptr, rest, s);
@@ -247,6 +268,7 @@ int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t 
     if (!h.rows.empty())
         std::memcpy(host.data() + L.rows_off, h.rows.data(), h.rows.size() * sizeof(QuantRow));
     hipStream_t s = (hipStream_t)stream;
+    clear_hip_error();
     BL_HIP_CHECK(hipMemcpyAsync(table, host.data(), L.bytes, hipMemcpyHostToDevice, s));
     BL_HIP_CHECK(hipStreamSynchronize(s));
     int max_K = 0;
@@ -272,6 +294,7 @@ int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) 
     const Unit* units = (const Unit*)(base + L.units_off);
     const QuantRow* rows = (const QuantRow*)(base + L.rows_off);
     hipStream_t s = (hipStream_t)stream;
+    clear_hip_error();
     int rc = BITLINEAR_OK;
     if (plan->quant_rows) rc = launch_quantize_grouped(rows, plan->quant_rows, s);
     if (rc) return rc;

@@ -69,14 +69,27 @@ __device__ inline uint32_t codes_to_ternary(uint32_t codes) {
 
 }  // namespace bl
 
+namespace bl {
+// Records the failing HIP call for bitlinear_last_error() (per host thread).
+void set_hip_error(hipError_t e, const char* where);
+}  // namespace bl
+
 #define BL_HIP_CHECK(expr)                                   \
     do {                                                     \
         hipError_t _e = (expr);                              \
-        if (_e != hipSuccess) return BITLINEAR_EHIP;         \
+        if (_e != hipSuccess) {                              \
+            bl::set_hip_error(_e, #expr);                    \
+            return BITLINEAR_EHIP;                           \
+        }                                                    \
     } while (0)
 
+// After a kernel launch: the launch's own status (the error state is cleared
+// at every API entry, so an earlier failure elsewhere cannot leak in here).
 #define BL_LAUNCH_CHECK()                                    \
     do {                                                     \
         hipError_t _e = hipGetLastError();                   \
-        if (_e != hipSuccess) return BITLINEAR_EHIP;         \
+        if (_e != hipSuccess) {                              \
+            bl::set_hip_error(_e, __func__);                 \
+            return BITLINEAR_EHIP;                           \
+        }                                                    \
     } while (0)

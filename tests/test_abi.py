@@ -137,3 +137,10 @@ def test_library_never_allocates():
         text = open(os.path.join(CSRC, f)).read()
         for banned in ("hipMalloc", "hipFree", "hipHostMalloc", "malloc(", "new "):
             assert banned not in text, (f, banned)
+
+
+def test_single_hip_runtime_in_process():
+    # the library must bind to torch's HIP runtime, never load a second copy
+    import re
+    maps = open("/proc/self/maps").read()
+    assert len(set(re.findall(r"\S*libamdhip64\S*", maps))) == 1
