@@ -34,7 +34,18 @@ struct GemmArgs {
     const Unit* units;        // grouped: (problem, column tile)
     int64_t M;
     int64_t ntiles_n;         // single: column tiles
+    int64_t ntiles_m;         // single: row tiles
 };
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b % 8), each with its own L2.  Give each XCD a contiguous run of tiles
+// (column index fastest) so that its L2 serves a few A row blocks to all of
+// them and each B tile to the row blocks that run at the same time.
+__device__ inline int64_t xcd_tile(int64_t b, int64_t T) {
+    constexpr int64_t X = 8;
+    const int64_t xcd = b % X, slot = b / X, q = T / X, r = T % X;
+    return xcd * q + (xcd < r ? xcd : r) + slot;
+}
 
 template <int MT, int WM, int WN, bool GROUPED>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a) {
@@ -142,6 +153,194 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill variant (M > 64): 128 x 256 workgroup tile, four wavefronts side by
+// side in N; each owns all 128 rows x 64 columns as 4 x 2 tiles of
+// v_mfma_i32_32x32x32_i8, so every weight word is expanded exactly once per
+// workgroup.  The K loop advances 128 (two 64-k blocks) per step through a
+// three-stage LDS ring, each stage filled two steps ahead by direct
+// global->LDS loads (global_load_lds_dwordx4, 1 KB per wave instruction):
+//  * A: 128 rows x 128 bytes.  Chunk c (16 bytes) of row r is stored at
+//    chunk c ^ ((r >> 1) & 7): the 16 rows one ds_read_b128 phase serves land
+//    on 16 distinct 16-byte bank groups, with no padding, so each wave's 1 KB
+//    DMA stays contiguous.
+//  * B: the packed words themselves (two 1 KB blocks per wavefront = its 64
+//    rows x 128 k), copied verbatim; each lane expands its words into ternary
+//    bytes in registers right before the MFMAs that use them.
+// Lane (n, g) of a wave takes row n's k-block kb + g; word d of it feeds MFMA
+// d of the step, whose 32 k are the two lane groups' 16-k runs; A is read in
+// the same (g, d) order.  Rows past M and k past K are read from clamped
+// (in-bounds) addresses: rows past M are never stored, and every k past K
+// meets a zero weight (pad code 01 inside the last block, code 01 forced for
+// blocks past the end).
+constexpr int kPreBM = 128, kPreBN = 256;
+constexpr int kPreStages = 3;
+constexpr int kPreAStage = kPreBM * 128;          // 16 KB
+constexpr int kPreBStage = 4 * 2 * 1024;          // 8 KB
+constexpr int kPreStage = kPreAStage + kPreBStage;
+constexpr int kPreDmaPerStep = 6;                 // per wave: 4 A + 2 B instructions
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector memory
+// operations are outstanding; expcnt and lgkmcnt are left unconstrained.
+template <int vm>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(vm >= 0 && vm < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14));
+}
+
+template <bool GROUPED>
+__global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kPreStages * kPreStage];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    Problem p;
+    int64_t tile_n, tile_m;
+    if constexpr (GROUPED) {
+        const Unit un = a.units[blockIdx.x];
+        p = a.problems[un.problem];
+        tile_n = un.group;
+        tile_m = blockIdx.y;
+    } else {
+        p = a.p;
+        const int64_t tile = xcd_tile(blockIdx.x, a.ntiles_n * a.ntiles_m);
+        tile_m = tile / a.ntiles_n;
+        tile_n = tile - tile_m * a.ntiles_n;
+    }
+    const int64_t M = a.M, N = p.N, K = p.K, Kb = p.Kb;
+    const int64_t m0 = tile_m * kPreBM;
+    const int64_t Gn = ceil_div(N, 64);
+    const int64_t group = tile_n * 4 + wave;
+    const bool group_ok = group < Gn;
+    const int ln = lane & 31, lg = lane >> 5;   // 32x32 MFMA lane coordinates
+    const int64_t nsteps = ceil_div(Kb, 2);
+
+    // A DMA sources of this lane (4 per step), fixed over K but for kbase.
+    const int8_t* asrc[4];
+    int acol[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int P = (j * 4 + wave) * 64 + lane;       // physical 16-byte slot
+        const int r = P >> 3;
+        acol[j] = ((P & 7) ^ ((r >> 1) & 7)) * 16;      // logical byte column
+        const int64_t m = m0 + r < M ? m0 + r : M - 1;
+        asrc[j] = p.xq + m * K + acol[j];
+    }
+    // B DMA source: this wave's group (clamped when past the end), 1 KB per k-block.
+    const uint4* bsrc = p.packed + (group_ok ? group : 0) * Kb * 64 + lane;
+
+    auto issue = [&](int stage, int64_t step) {
+        uint8_t* st = lds + stage * kPreStage;
+        const int64_t kbase = step * 128;
+        const bool full = kbase + 128 <= K;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int8_t* src = asrc[j] + kbase;
+            if (!full && kbase + acol[j] >= K) src = asrc[j] + (K - 16 - acol[j]);
+            __builtin_amdgcn_global_load_lds(src, st + (j * 4 + wave) * 1024, 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int64_t kb = step * 2 + j;
+            kb = kb < Kb ? kb : Kb - 1;                 // block past the end: zeroed at use
+            __builtin_amdgcn_global_load_lds(bsrc + kb * 64, st + kPreAStage + (wave * 2 + j) * 1024,
+                                             16, 0, 0);
+        }
+    };
+
+    v16i acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][t][e] = 0;
+
+    issue(0, 0);
+    if (nsteps > 1) issue(1, 1);
+    for (int64_t s = 0; s < nsteps; ++s) {
+        // This wave's DMAs for step s have landed (step s+1's may still be in
+        // flight); the barrier makes that true for every wave.  Every LDS read
+        // of stage (s+2)%3 (step s-1) fed an MFMA before this point, so the
+        // stage is free.  A plain s_barrier: __syncthreads() would also drain
+        // the DMAs of step s+1.
+        if (s + 1 < nsteps) wait_vmcnt<kPreDmaPerStep>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (s + 2 < nsteps) issue((int)((s + 2) % kPreStages), s + 2);
+        const uint8_t* A = lds + (s % kPreStages) * kPreStage;
+        const uint8_t* B = A + kPreAStage + wave * 2048;
+        const bool kb_ok = s * 2 + lg < Kb;
+        uint4 bw[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            bw[t] = *reinterpret_cast<const uint4*>(B + lg * 1024 + (t * 32 + ln) * 16);
+            if (!kb_ok) bw[t] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+        }
+        // Two register sets for the A fragments and the expanded B words:
+        // group d+1's LDS reads and expansion run while group d's eight MFMAs
+        // execute.
+        v4i af[2][4], bf[2][2];
+        auto load_a = [&](v4i (&dst)[4], int d) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = i * 32 + ln;
+                dst[i] = *reinterpret_cast<const v4i*>(A + r * 128 + (((lg * 4 + d) ^ ((r >> 1) & 7)) << 4));
+            }
+        };
+        auto expand_b = [&](v4i (&dst)[2], int d) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t w = d == 0 ? bw[t].x : d == 1 ? bw[t].y : d == 2 ? bw[t].z : bw[t].w;
+                dst[t].x = (int)codes_to_ternary(w & 0x03030303u);
+                dst[t].y = (int)codes_to_ternary((w >> 2) & 0x03030303u);
+                dst[t].z = (int)codes_to_ternary((w >> 4) & 0x03030303u);
+                dst[t].w = (int)codes_to_ternary((w >> 6) & 0x03030303u);
+            }
+        };
+        load_a(af[0], 0);
+        expand_b(bf[0], 0);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const int c = d & 1;
+            if (d < 3) load_a(af[c ^ 1], d + 1);
+            __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of this group's MFMAs
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[c][i], bf[c][t], acc[i][t], 0, 0, 0);
+            if (d < 3) expand_b(bf[c ^ 1], d + 1);
+        }
+    }
+
+    // Epilogue: element 4j + q of tile (i, t) is row 32i + 8j + 4lg + q, column 32t + ln.
+    if (!group_ok) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t m = m0 + i * 32 + j * 8 + lg * 4 + q;
+                if (m >= M) continue;
+                const float sc = dequant_scale(p.eta[m], p.gamma);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int64_t n = group * 64 + t * 32 + ln;
+                    if (n >= N) continue;
+                    const int v = acc[i][t][j * 4 + q];
+                    p.y[m * N + n] = dequant(v, sc);
+                    if (p.y_int) p.y_int[m * N + n] = v;
+                }
+            }
+        }
+    }
+}
+
 template <int MT, int WM, int WN>
 static int launch_cfg(const GemmArgs& a, int64_t ntn, int64_t ntm, bool grouped, hipStream_t stream) {
     dim3 grid((unsigned)ntn, (unsigned)ntm);
@@ -154,14 +353,25 @@ static int launch_cfg(const GemmArgs& a, int64_t ntn, int64_t ntm, bool grouped,
 }
 
 // Column tile width (output rows of W per workgroup) of the variant used for M.
-static int gemm_bn(int64_t M) { return M <= 64 ? 256 : 128; }
+static int gemm_bn(int64_t M) { return M <= 64 ? 256 : kPreBN; }
 
 static int dispatch(GemmArgs& a, int64_t ntn, bool grouped, hipStream_t stream) {
     const int64_t M = a.M;
     if (M <= 16) return launch_cfg<1, 1, 4>(a, ntn, 1, grouped, stream);
     if (M <= 32) return launch_cfg<2, 1, 4>(a, ntn, 1, grouped, stream);
     if (M <= 64) return launch_cfg<4, 1, 4>(a, ntn, 1, grouped, stream);
-    return launch_cfg<4, 2, 2>(a, ntn, ceil_div(M, 128), grouped, stream);
+    const int64_t ntm = ceil_div(M, kPreBM);
+    if (grouped) {
+        hipLaunchKernelGGL((gemm_prefill_kernel<true>), dim3((unsigned)ntn, (unsigned)ntm), dim3(256),
+                           0, stream, a);
+    } else {
+        a.ntiles_n = ntn;
+        a.ntiles_m = ntm;
+        hipLaunchKernelGGL((gemm_prefill_kernel<false>), dim3((unsigned)(ntn * ntm)), dim3(256), 0,
+                           stream, a);
+    }
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
 }
 
 int launch_gemm(const Problem& p, int64_t M, hipStream_t stream) {

@@ -144,3 +144,9 @@ def test_single_hip_runtime_in_process():
     import re
     maps = open("/proc/self/maps").read()
     assert len(set(re.findall(r"\S*libamdhip64\S*", maps))) == 1
+
+
+def test_no_undefined_library_symbols():
+    # every kernel stub and helper of the library is defined in the .so
+    out = subprocess.check_output(["nm", "-D", "--undefined-only", bl.LIB_PATH], text=True)
+    assert not [l for l in out.splitlines() if "_ZN2bl" in l]
