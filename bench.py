@@ -136,6 +136,93 @@ def cpu_baseline(sw, S, budget_s: float = 12.0):
                       f"{t_total:.1f} s timed"}
 
 
+COPY_BYTES = 1 << 30
+
+
+def profile_run(torch, L, sw, args) -> int:
+    """Kernels for rocprofv3: full steps, contraction-only launches, a calibration copy."""
+    for _ in range(max(1, args.steps)):
+        sw.step(1)
+    plan_c, _table = contraction_only_plan(sw, 1)
+    for _ in range(max(1, args.steps)):
+        L.bitlinear_forward_grouped(plan_c)
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)   # reads and writes exactly COPY_BYTES each
+    torch.cuda.synchronize()
+    log(f"profile run done: contraction bytes per launch {sw.contraction_bytes(1)}")
+    return 0
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(root: str) -> str:
+    """Markdown summary of rocprofv3 output under root: kernel stats (from a
+    --kernel-trace --stats run in root/trace) and per-dispatch FETCH_SIZE /
+    WRITE_SIZE (from --pmc runs in root/fetch and root/write), the latter
+    scaled by the counters of the 1 GiB calibration copy."""
+    import glob
+    out = []
+    stats = glob.glob(os.path.join(root, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        rows = _csv_rows(stats[0])
+        out.append("| kernel | calls | avg us | min us | max us | total % |")
+        out.append("|---|---|---|---|---|---|")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:12]:
+            name = r["Name"][:90].replace("|", "/")
+            out.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                       f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                       f"{float(r['Percentage']):.2f} |")
+    for kind in ("fetch", "write"):
+        files = glob.glob(os.path.join(root, kind, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            continue
+        rows = _csv_rows(files[0])
+        per = {}
+        for r in rows:
+            key = "copy" if "copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower() \
+                else ("contraction" if "gemv_dot4_kernel" in r["Kernel_Name"] else None)
+            if key:
+                per.setdefault(key, []).append(float(r["Counter_Value"]))
+        if "copy" in per and "contraction" in per:
+            copy_kib = max(per["copy"])
+            factor = (COPY_BYTES / 1024) / copy_kib
+            vals = sorted(per["contraction"])
+            med = vals[len(vals) // 2]
+            out.append(f"\n{kind.upper()}_SIZE: calibration copy reads {copy_kib:.0f} KiB for "
+                       f"{COPY_BYTES / 1024:.0f} KiB moved (factor {factor:.4f}); contraction kernel "
+                       f"median {med:.0f} KiB per dispatch -> {med * factor * 1024 / 1e9:.4f} GB scaled "
+                       f"({len(vals)} dispatches)")
+    return "\n".join(out)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_dot4_grouped_decode70b_m1_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode contraction kernel from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE runs, or None once the kernel's sources have
+    changed since those counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["kernel_sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["kernel_source_sha256"]:
+            return None
+        return rec["traffic_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,7 +232,14 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-m16", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="short run for rocprofv3: the M=1 sweep, the contraction kernel alone and a "
+                         "1 GiB copy whose counters calibrate FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--summarize", metavar="DIR", help="summarize rocprofv3 output under DIR")
     args = ap.parse_args()
+    if args.summarize:
+        print(summarize_profile(args.summarize))
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -162,6 +256,8 @@ def main() -> int:
     Ms = (1,) if args.no_m16 else (1, 16)
     sw = DecodeSweep(layers=args.layers, Ms=Ms, progress=log)
     log(f"packed weights resident: {sw.weight_bytes() / 1e9:.3f} GB")
+    if args.profile_run:
+        return profile_run(torch, L, sw, args)
 
     # ---- headline: full step at M = 1
     for _ in range(args.warmup):
@@ -224,7 +320,8 @@ def main() -> int:
                    "tokens_per_step": 1, "packed_weight_bytes": sw.weight_bytes(),
                    "algorithmic_bytes_per_step": step_bytes, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
                      "kernel": "gemv_dot4_kernel<1, grouped> (contraction + fused dequant)",
                      "kernel_ms": round(kern_ms, 4), "algorithmic_bytes": kern_bytes},
         "cpu_baseline": cpu,

@@ -157,28 +157,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a) {
 // Prefill variant (M > 64): 128 x 256 workgroup tile, four wavefronts side by
 // side in N; each owns all 128 rows x 64 columns as 4 x 2 tiles of
 // v_mfma_i32_32x32x32_i8, so every weight word is expanded exactly once per
-// workgroup.  The K loop advances 128 (two 64-k blocks) per step through a
-// three-stage LDS ring, each stage filled two steps ahead by direct
-// global->LDS loads (global_load_lds_dwordx4, 1 KB per wave instruction):
-//  * A: 128 rows x 128 bytes.  Chunk c (16 bytes) of row r is stored at
-//    chunk c ^ ((r >> 1) & 7): the 16 rows one ds_read_b128 phase serves land
-//    on 16 distinct 16-byte bank groups, with no padding, so each wave's 1 KB
-//    DMA stays contiguous.
-//  * B: the packed words themselves (two 1 KB blocks per wavefront = its 64
-//    rows x 128 k), copied verbatim; each lane expands its words into ternary
-//    bytes in registers right before the MFMAs that use them.
-// Lane (n, g) of a wave takes row n's k-block kb + g; word d of it feeds MFMA
-// d of the step, whose 32 k are the two lane groups' 16-k runs; A is read in
-// the same (g, d) order.  Rows past M and k past K are read from clamped
-// (in-bounds) addresses: rows past M are never stored, and every k past K
-// meets a zero weight (pad code 01 inside the last block, code 01 forced for
-// blocks past the end).
+// workgroup.  The K loop advances 128 (two 64-k blocks) per step and keeps
+// three steps in flight ahead of the one being computed:
+//  * A: a four-stage LDS ring of 128 rows x 128 bytes, filled by direct
+//    global->LDS loads (global_load_lds_dwordx4, 1 KB per wave instruction).
+//    Chunk c (16 bytes) of row r is stored at chunk c ^ ((r >> 1) & 7): the 16
+//    rows one ds_read_b128 phase serves land on 16 distinct bank groups, with
+//    no padding, so each wave's 1 KB DMA stays contiguous.
+//  * B: the packed words go straight to registers (a four-slot ring); each
+//    lane expands them into ternary bytes right before the MFMAs that use
+//    them.  Lane (n, g) holds row n's k-block kb + g; word d feeds MFMA group
+//    d, whose 32 k are the two lane groups' 16-k runs; A is read in the same
+//    (g, d) order.
+// Rows past M and k past K are read from clamped (in-bounds) addresses: rows
+// past M are never stored, and every k past K meets a zero weight (pad code
+// 01 inside the last block, code 01 forced for blocks past the end).
 constexpr int kPreBM = 128, kPreBN = 256;
-constexpr int kPreStages = 3;
-constexpr int kPreAStage = kPreBM * 128;          // 16 KB
-constexpr int kPreBStage = 4 * 2 * 1024;          // 8 KB
-constexpr int kPreStage = kPreAStage + kPreBStage;
-constexpr int kPreDmaPerStep = 6;                 // per wave: 4 A + 2 B instructions
+constexpr int kPreStages = 4;
+constexpr int kPreAStage = kPreBM * 128;   // 16 KB
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
@@ -190,9 +186,98 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14));
 }
 
+struct PrefillCtx {
+    uint8_t* lds;
+    const int8_t* asrc[4];
+    int acol[4];
+    const uint4* brow;
+    int64_t K, Kb, nsteps;
+    int wave, lane, ln, lg;
+};
+
+// Queue step `step`: this wave's four 1 KB A DMAs into LDS stage `stage` and
+// this lane's two B chunks into registers.  6 vector memory instructions.
+__device__ __forceinline__ void prefill_issue(const PrefillCtx& c, int stage, uint4 (&bq)[2],
+                                              int64_t step) {
+    uint8_t* st = c.lds + stage * kPreAStage;
+    const int64_t kbase = step * 128;
+    const bool full = kbase + 128 <= c.K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int8_t* src = c.asrc[j] + kbase;
+        if (!full && kbase + c.acol[j] >= c.K) src = c.asrc[j] + (c.K - 16 - c.acol[j]);
+        __builtin_amdgcn_global_load_lds(src, st + (j * 4 + c.wave) * 1024, 16, 0, 0);
+    }
+    int64_t kb = step * 2 + c.lg;
+    kb = kb < c.Kb ? kb : c.Kb - 1;   // a block past the end is zeroed at use
+#pragma unroll
+    for (int t = 0; t < 2; ++t) bq[t] = c.brow[kb * 64 + t * 32];
+}
+
+// One K-step of MFMAs from LDS stage `stage` and the B words `bq`.
+__device__ __forceinline__ void prefill_compute(const PrefillCtx& c, int stage, const uint4 (&bq)[2],
+                                                int64_t step, v16i (&acc)[4][2]) {
+    const uint8_t* A = c.lds + stage * kPreAStage;
+    const bool kb_ok = step * 2 + c.lg < c.Kb;
+    uint4 bw[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        bw[t] = kb_ok ? bq[t] : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+    // Two register sets for the A fragments and the expanded B words: group
+    // d+1's LDS reads and expansion run while group d's eight MFMAs execute.
+    v4i af[2][4], bf[2][2];
+    auto load_a = [&](v4i (&dst)[4], int d) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = i * 32 + c.ln;
+            dst[i] = *reinterpret_cast<const v4i*>(A + r * 128 + (((c.lg * 4 + d) ^ ((r >> 1) & 7)) << 4));
+        }
+    };
+    auto expand_b = [&](v4i (&dst)[2], int d) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t w = d == 0 ? bw[t].x : d == 1 ? bw[t].y : d == 2 ? bw[t].z : bw[t].w;
+            dst[t].x = (int)codes_to_ternary(w & 0x03030303u);
+            dst[t].y = (int)codes_to_ternary((w >> 2) & 0x03030303u);
+            dst[t].z = (int)codes_to_ternary((w >> 4) & 0x03030303u);
+            dst[t].w = (int)codes_to_ternary((w >> 6) & 0x03030303u);
+        }
+    };
+    load_a(af[0], 0);
+    expand_b(bf[0], 0);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int cur = d & 1;
+        if (d < 3) load_a(af[cur ^ 1], d + 1);
+        __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of this group's MFMAs
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][t], acc[i][t], 0, 0, 0);
+        if (d < 3) expand_b(bf[cur ^ 1], d + 1);
+    }
+}
+
+// Step `step` of the ring: wait for its data (exactly: the steps issued after
+// it may stay in flight), make that true for every wave, refill the stage
+// freed by step-1 with step+3, compute.  Every LDS read of that stage fed an
+// MFMA before the barrier.  A plain s_barrier: __syncthreads() would also
+// drain the DMAs still in flight.
+__device__ __forceinline__ void prefill_step(const PrefillCtx& c, int stage, const uint4 (&bcur)[2],
+                                             uint4 (&bnext)[2], int64_t step, v16i (&acc)[4][2]) {
+    if (step >= c.nsteps) return;
+    if (step + 2 < c.nsteps) wait_vmcnt<12>();
+    else if (step + 1 < c.nsteps) wait_vmcnt<6>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (step + 3 < c.nsteps) prefill_issue(c, (stage + 3) & 3, bnext, step + 3);
+    prefill_compute(c, stage, bcur, step, acc);
+}
+
 template <bool GROUPED>
 __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kPreStages * kPreStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kPreStages * kPreAStage];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -212,44 +297,27 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
     }
     const int64_t M = a.M, N = p.N, K = p.K, Kb = p.Kb;
     const int64_t m0 = tile_m * kPreBM;
-    const int64_t Gn = ceil_div(N, 64);
     const int64_t group = tile_n * 4 + wave;
-    const bool group_ok = group < Gn;
-    const int ln = lane & 31, lg = lane >> 5;   // 32x32 MFMA lane coordinates
-    const int64_t nsteps = ceil_div(Kb, 2);
+    const bool group_ok = group < ceil_div(N, 64);
 
-    // A DMA sources of this lane (4 per step), fixed over K but for kbase.
-    const int8_t* asrc[4];
-    int acol[4];
+    PrefillCtx c;
+    c.lds = lds;
+    c.K = K;
+    c.Kb = Kb;
+    c.nsteps = ceil_div(Kb, 2);
+    c.wave = wave;
+    c.lane = lane;
+    c.ln = lane & 31;
+    c.lg = lane >> 5;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int P = (j * 4 + wave) * 64 + lane;       // physical 16-byte slot
         const int r = P >> 3;
-        acol[j] = ((P & 7) ^ ((r >> 1) & 7)) * 16;      // logical byte column
+        c.acol[j] = ((P & 7) ^ ((r >> 1) & 7)) * 16;    // logical byte column
         const int64_t m = m0 + r < M ? m0 + r : M - 1;
-        asrc[j] = p.xq + m * K + acol[j];
+        c.asrc[j] = p.xq + m * K + c.acol[j];
     }
-    // B DMA source: this wave's group (clamped when past the end), 1 KB per k-block.
-    const uint4* bsrc = p.packed + (group_ok ? group : 0) * Kb * 64 + lane;
-
-    auto issue = [&](int stage, int64_t step) {
-        uint8_t* st = lds + stage * kPreStage;
-        const int64_t kbase = step * 128;
-        const bool full = kbase + 128 <= K;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int8_t* src = asrc[j] + kbase;
-            if (!full && kbase + acol[j] >= K) src = asrc[j] + (K - 16 - acol[j]);
-            __builtin_amdgcn_global_load_lds(src, st + (j * 4 + wave) * 1024, 16, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            int64_t kb = step * 2 + j;
-            kb = kb < Kb ? kb : Kb - 1;                 // block past the end: zeroed at use
-            __builtin_amdgcn_global_load_lds(bsrc + kb * 64, st + kPreAStage + (wave * 2 + j) * 1024,
-                                             16, 0, 0);
-        }
-    };
+    c.brow = p.packed + (group_ok ? group : 0) * Kb * 64 + c.ln;
 
     v16i acc[4][2];
 #pragma unroll
@@ -259,66 +327,20 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][t][e] = 0;
 
-    issue(0, 0);
-    if (nsteps > 1) issue(1, 1);
-    for (int64_t s = 0; s < nsteps; ++s) {
-        // This wave's DMAs for step s have landed (step s+1's may still be in
-        // flight); the barrier makes that true for every wave.  Every LDS read
-        // of stage (s+2)%3 (step s-1) fed an MFMA before this point, so the
-        // stage is free.  A plain s_barrier: __syncthreads() would also drain
-        // the DMAs of step s+1.
-        if (s + 1 < nsteps) wait_vmcnt<kPreDmaPerStep>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (s + 2 < nsteps) issue((int)((s + 2) % kPreStages), s + 2);
-        const uint8_t* A = lds + (s % kPreStages) * kPreStage;
-        const uint8_t* B = A + kPreAStage + wave * 2048;
-        const bool kb_ok = s * 2 + lg < Kb;
-        uint4 bw[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            bw[t] = *reinterpret_cast<const uint4*>(B + lg * 1024 + (t * 32 + ln) * 16);
-            if (!kb_ok) bw[t] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-        }
-        // Two register sets for the A fragments and the expanded B words:
-        // group d+1's LDS reads and expansion run while group d's eight MFMAs
-        // execute.
-        v4i af[2][4], bf[2][2];
-        auto load_a = [&](v4i (&dst)[4], int d) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = i * 32 + ln;
-                dst[i] = *reinterpret_cast<const v4i*>(A + r * 128 + (((lg * 4 + d) ^ ((r >> 1) & 7)) << 4));
-            }
-        };
-        auto expand_b = [&](v4i (&dst)[2], int d) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const uint32_t w = d == 0 ? bw[t].x : d == 1 ? bw[t].y : d == 2 ? bw[t].z : bw[t].w;
-                dst[t].x = (int)codes_to_ternary(w & 0x03030303u);
-                dst[t].y = (int)codes_to_ternary((w >> 2) & 0x03030303u);
-                dst[t].z = (int)codes_to_ternary((w >> 4) & 0x03030303u);
-                dst[t].w = (int)codes_to_ternary((w >> 6) & 0x03030303u);
-            }
-        };
-        load_a(af[0], 0);
-        expand_b(bf[0], 0);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const int c = d & 1;
-            if (d < 3) load_a(af[c ^ 1], d + 1);
-            __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of this group's MFMAs
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[c][i], bf[c][t], acc[i][t], 0, 0, 0);
-            if (d < 3) expand_b(bf[c ^ 1], d + 1);
-        }
+    uint4 b0[2], b1[2], b2[2], b3[2];
+    if (0 < c.nsteps) prefill_issue(c, 0, b0, 0);
+    if (1 < c.nsteps) prefill_issue(c, 1, b1, 1);
+    if (2 < c.nsteps) prefill_issue(c, 2, b2, 2);
+    for (int64_t s = 0; s < c.nsteps; s += 4) {
+        prefill_step(c, 0, b0, b3, s + 0, acc);
+        prefill_step(c, 1, b1, b0, s + 1, acc);
+        prefill_step(c, 2, b2, b1, s + 2, acc);
+        prefill_step(c, 3, b3, b2, s + 3, acc);
     }
 
     // Epilogue: element 4j + q of tile (i, t) is row 32i + 8j + 4lg + q, column 32t + ln.
     if (!group_ok) return;
+    const int ln = c.ln, lg = c.lg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
