@@ -43,7 +43,9 @@ int check_sizes(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t forward_ws_bytes(int64_t M, int64_t N, int64_t K) {
-    return M <= kGemvMaxM ? gemv_ws_bytes(M, N, K) : 0;
+    if (M <= kGemvMaxM) return gemv_ws_bytes(M, N, K);
+    if (M <= kSkinnyMaxM) return skinny_ws_bytes(M, N, K);
+    return 0;
 }
 
 Problem make_problem(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
@@ -66,6 +68,7 @@ int run_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float
     if (M == 0) return BITLINEAR_OK;
     const Problem p = make_problem(xq, eta, packed, gamma, N, K, y, y_int);
     if (M <= kGemvMaxM) return launch_gemv(p, M, ws, stream);
+    if (M <= kSkinnyMaxM) return launch_skinny(p, M, ws, stream);
     return launch_gemm(p, M, stream);
 }
 
@@ -84,8 +87,16 @@ TableLayout table_layout(int64_t count, int64_t nunits, int64_t nrows) {
 
 // Work units of the grouped contraction for one problem.
 int64_t problem_units(int64_t M, int64_t N) {
-    if (M <= kGemvMaxM) return ceil_div(N, 64);
+    if (M <= kGemvMaxM) return ceil_div(N, 64);      // one wavefront per 64-row group
+    if (M <= kSkinnyMaxM) return ceil_div(N, kSkinnyRows);   // one workgroup per 256 rows
     return ceil_div(N, gemm_tile_n(M));
+}
+
+// Contraction kernel of a grouped plan: 0 dot4 GEMV, 1 prefill MFMA, 2 skinny MFMA.
+int32_t plan_kernel(int64_t M) {
+    if (M <= kGemvMaxM) return 0;
+    if (M <= kSkinnyMaxM) return 2;
+    return 1;
 }
 
 struct PlanHost {
@@ -279,7 +290,7 @@ int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t 
     plan->quant_rows = (int64_t)h.rows.size();
     plan->count = count;
     plan->M = (int32_t)M;
-    plan->kernel = M <= kGemvMaxM ? 0 : 1;
+    plan->kernel = plan_kernel(M);
     plan->max_K = max_K;
     return BITLINEAR_OK;
 }
@@ -299,6 +310,7 @@ int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) 
     if (plan->quant_rows) rc = launch_quantize_grouped(rows, plan->quant_rows, s);
     if (rc) return rc;
     if (plan->kernel == 0) return launch_gemv_grouped(problems, units, plan->units, plan->M, s);
+    if (plan->kernel == 2) return launch_skinny_grouped(problems, units, plan->units, plan->M, s);
     return launch_gemm_grouped(problems, units, plan->units, plan->M, s);
 }
 

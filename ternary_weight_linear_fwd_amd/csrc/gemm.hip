@@ -1,4 +1,4 @@
-// gemm.hip -- ternary x int8 contraction on the gfx950 matrix cores (M > 4).
+// gemm.hip -- prefill ternary x int8 contraction on the gfx950 matrix cores (M > 64).
 //
 // Where many tokens share the weights (prefill, batched decode) the
 // contraction of [P2] "3. Additive Integer Accumulation" is a dense integer
@@ -47,112 +47,6 @@ __device__ inline int64_t xcd_tile(int64_t b, int64_t T) {
     return xcd * q + (xcd < r ? xcd : r) + slot;
 }
 
-template <int MT, int WM, int WN, bool GROUPED>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a) {
-    constexpr int THREADS = 64 * WM * WN;
-    constexpr int BM = WM * 16 * MT;
-    constexpr int BN = WN * 64;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * kLdsRowBytes];
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int wm = wave / WN, wn = wave % WN;
-
-    Problem p;
-    int64_t tile_n, tile_m;
-    if constexpr (GROUPED) {
-        const Unit un = a.units[blockIdx.x];
-        p = a.problems[un.problem];
-        tile_n = un.group;
-        tile_m = blockIdx.y;
-    } else {
-        p = a.p;
-        tile_n = blockIdx.x;
-        tile_m = blockIdx.y;
-    }
-    const int64_t M = a.M, N = p.N, K = p.K, Kb = p.Kb;
-    const int64_t m0 = tile_m * BM;
-    const int64_t Gn = ceil_div(N, 64);
-    const int64_t group = tile_n * WN + wn;     // this wave's 64-row group
-    const bool group_ok = group < Gn;
-
-    const int nl = lane & 15, lg = lane >> 4;   // MFMA lane coordinates
-    v4i acc[MT][4];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][t] = v4i{0, 0, 0, 0};
-
-    const uint4* wbase = p.packed + group * Kb * 64;
-
-    for (int64_t kb = 0; kb < Kb; kb += 4) {
-        // ---- B chunks for this step (registers)
-        uint4 bch[4];
-        const int64_t kbl = kb + lg;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (group_ok && kbl < Kb)
-                bch[t] = ldnt_u4(wbase + kbl * 64 + t * 16 + nl);
-            else
-                bch[t] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-        }
-        // ---- A tile -> LDS
-        const int64_t kbase = kb * 64;
-        for (int c = tid; c < BM * 16; c += THREADS) {
-            const int r = c >> 4, col = c & 15;
-            const int64_t m = m0 + r, k = kbase + col * 16;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (m < M && k < K) v = *reinterpret_cast<const uint4*>(p.xq + m * K + k);
-            *reinterpret_cast<uint4*>(&lds_a[r * kLdsRowBytes + col * 16]) = v;
-        }
-        __syncthreads();
-        // ---- MFMAs
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            v4i af[MT];
-#pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                const int r = wm * 16 * MT + i * 16 + nl;
-                af[i] = *reinterpret_cast<const v4i*>(&lds_a[r * kLdsRowBytes + lg * 64 + d * 16]);
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint32_t w = d == 0 ? bch[t].x : d == 1 ? bch[t].y : d == 2 ? bch[t].z : bch[t].w;
-                v4i bf;
-                bf.x = (int)codes_to_ternary(w & 0x03030303u);
-                bf.y = (int)codes_to_ternary((w >> 2) & 0x03030303u);
-                bf.z = (int)codes_to_ternary((w >> 4) & 0x03030303u);
-                bf.w = (int)codes_to_ternary((w >> 6) & 0x03030303u);
-#pragma unroll
-                for (int i = 0; i < MT; ++i)
-                    acc[i][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf, acc[i][t], 0, 0, 0);
-            }
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue: lane holds rows 4*lg + r (r = 0..3) and column nl of each tile
-    if (!group_ok) return;
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t m = m0 + wm * 16 * MT + i * 16 + lg * 4 + r;
-            if (m >= M) continue;
-            const float s = dequant_scale(p.eta[m], p.gamma);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int64_t n = group * 64 + t * 16 + nl;
-                if (n >= N) continue;
-                const int v = acc[i][t][r];
-                p.y[m * N + n] = dequant(v, s);
-                if (p.y_int) p.y_int[m * N + n] = v;
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Prefill variant (M > 64): 128 x 256 workgroup tile, four wavefronts side by
 // side in N; each owns all 128 rows x 64 columns as 4 x 2 tiles of
@@ -172,9 +66,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_mfma_kernel(GemmArgs a) {
 // Rows past M and k past K are read from clamped (in-bounds) addresses: rows
 // past M are never stored, and every k past K meets a zero weight (pad code
 // 01 inside the last block, code 01 forced for blocks past the end).
-constexpr int kPreBM = 128, kPreBN = 256;
+constexpr int kPreBN = 256;
 constexpr int kPreStages = 4;
-constexpr int kPreAStage = kPreBM * 128;   // 16 KB
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 
@@ -186,27 +79,39 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14));
 }
 
+// One 16-byte-per-lane direct global->LDS load (the wave's 64 lanes fill
+// 1 KB at lds_dst).  Kept as a plain (non-template) function: the host
+// compilation pass rejects template instantiations that name this builtin.
+__device__ __forceinline__ void dma_16(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+}
+
+template <int MT>
 struct PrefillCtx {
+    static constexpr int BM = 32 * MT;            // rows per workgroup tile
+    static constexpr int AStage = BM * 128;       // bytes of one A stage
+    static constexpr int NA = AStage / 4096;      // A DMA instructions per wave per step
     uint8_t* lds;
-    const int8_t* asrc[4];
-    int acol[4];
+    const int8_t* asrc[NA];
+    int acol[NA];
     const uint4* brow;
     int64_t K, Kb, nsteps;
     int wave, lane, ln, lg;
 };
 
-// Queue step `step`: this wave's four 1 KB A DMAs into LDS stage `stage` and
-// this lane's two B chunks into registers.  6 vector memory instructions.
-__device__ __forceinline__ void prefill_issue(const PrefillCtx& c, int stage, uint4 (&bq)[2],
+// Queue step `step`: this wave's NA 1 KB A DMAs into LDS stage `stage` and
+// this lane's two B chunks into registers: NA + 2 vector memory instructions.
+template <int MT>
+__device__ __forceinline__ void prefill_issue(const PrefillCtx<MT>& c, int stage, uint4 (&bq)[2],
                                               int64_t step) {
-    uint8_t* st = c.lds + stage * kPreAStage;
+    uint8_t* st = c.lds + stage * PrefillCtx<MT>::AStage;
     const int64_t kbase = step * 128;
     const bool full = kbase + 128 <= c.K;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < PrefillCtx<MT>::NA; ++j) {
         const int8_t* src = c.asrc[j] + kbase;
         if (!full && kbase + c.acol[j] >= c.K) src = c.asrc[j] + (c.K - 16 - c.acol[j]);
-        __builtin_amdgcn_global_load_lds(src, st + (j * 4 + c.wave) * 1024, 16, 0, 0);
+        dma_16(src, st + (j * 4 + c.wave) * 1024);
     }
     int64_t kb = step * 2 + c.lg;
     kb = kb < c.Kb ? kb : c.Kb - 1;   // a block past the end is zeroed at use
@@ -215,9 +120,10 @@ __device__ __forceinline__ void prefill_issue(const PrefillCtx& c, int stage, ui
 }
 
 // One K-step of MFMAs from LDS stage `stage` and the B words `bq`.
-__device__ __forceinline__ void prefill_compute(const PrefillCtx& c, int stage, const uint4 (&bq)[2],
-                                                int64_t step, v16i (&acc)[4][2]) {
-    const uint8_t* A = c.lds + stage * kPreAStage;
+template <int MT>
+__device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, int stage, const uint4 (&bq)[2],
+                                                int64_t step, v16i (&acc)[MT][2]) {
+    const uint8_t* A = c.lds + stage * PrefillCtx<MT>::AStage;
     const bool kb_ok = step * 2 + c.lg < c.Kb;
     uint4 bw[2];
 #pragma unroll
@@ -225,10 +131,10 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx& c, int stage, 
         bw[t] = kb_ok ? bq[t] : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
     // Two register sets for the A fragments and the expanded B words: group
     // d+1's LDS reads and expansion run while group d's eight MFMAs execute.
-    v4i af[2][4], bf[2][2];
-    auto load_a = [&](v4i (&dst)[4], int d) {
+    v4i af[2][MT], bf[2][2];
+    auto load_a = [&](v4i (&dst)[MT], int d) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MT; ++i) {
             const int r = i * 32 + c.ln;
             dst[i] = *reinterpret_cast<const v4i*>(A + r * 128 + (((c.lg * 4 + d) ^ ((r >> 1) & 7)) << 4));
         }
@@ -253,7 +159,7 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx& c, int stage, 
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MT; ++i)
                 acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][t], acc[i][t], 0, 0, 0);
         if (d < 3) expand_b(bf[cur ^ 1], d + 1);
     }
@@ -264,20 +170,24 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx& c, int stage, 
 // freed by step-1 with step+3, compute.  Every LDS read of that stage fed an
 // MFMA before the barrier.  A plain s_barrier: __syncthreads() would also
 // drain the DMAs still in flight.
-__device__ __forceinline__ void prefill_step(const PrefillCtx& c, int stage, const uint4 (&bcur)[2],
-                                             uint4 (&bnext)[2], int64_t step, v16i (&acc)[4][2]) {
+template <int MT>
+__device__ __forceinline__ void prefill_step(const PrefillCtx<MT>& c, int stage, const uint4 (&bcur)[2],
+                                             uint4 (&bnext)[2], int64_t step, v16i (&acc)[MT][2]) {
+    constexpr int ops = PrefillCtx<MT>::NA + 2;   // vector memory instructions per step
     if (step >= c.nsteps) return;
-    if (step + 2 < c.nsteps) wait_vmcnt<12>();
-    else if (step + 1 < c.nsteps) wait_vmcnt<6>();
+    if (step + 2 < c.nsteps) wait_vmcnt<2 * ops>();
+    else if (step + 1 < c.nsteps) wait_vmcnt<ops>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (step + 3 < c.nsteps) prefill_issue(c, (stage + 3) & 3, bnext, step + 3);
-    prefill_compute(c, stage, bcur, step, acc);
+    if (step + 3 < c.nsteps) prefill_issue<MT>(c, (stage + 3) & 3, bnext, step + 3);
+    prefill_compute<MT>(c, stage, bcur, step, acc);
 }
 
-template <bool GROUPED>
+template <int MT, bool GROUPED>
 __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kPreStages * kPreAStage];
+    using Ctx = PrefillCtx<MT>;
+    constexpr int kPreBM = Ctx::BM;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kPreStages * Ctx::AStage];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -300,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
     const int64_t group = tile_n * 4 + wave;
     const bool group_ok = group < ceil_div(N, 64);
 
-    PrefillCtx c;
+    Ctx c;
     c.lds = lds;
     c.K = K;
     c.Kb = Kb;
@@ -310,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
     c.ln = lane & 31;
     c.lg = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < Ctx::NA; ++j) {
         const int P = (j * 4 + wave) * 64 + lane;       // physical 16-byte slot
         const int r = P >> 3;
         c.acol[j] = ((P & 7) ^ ((r >> 1) & 7)) * 16;    // logical byte column
@@ -319,30 +229,30 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
     }
     c.brow = p.packed + (group_ok ? group : 0) * Kb * 64 + c.ln;
 
-    v16i acc[4][2];
+    v16i acc[MT][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][t][e] = 0;
 
     uint4 b0[2], b1[2], b2[2], b3[2];
-    if (0 < c.nsteps) prefill_issue(c, 0, b0, 0);
-    if (1 < c.nsteps) prefill_issue(c, 1, b1, 1);
-    if (2 < c.nsteps) prefill_issue(c, 2, b2, 2);
+    if (0 < c.nsteps) prefill_issue<MT>(c, 0, b0, 0);
+    if (1 < c.nsteps) prefill_issue<MT>(c, 1, b1, 1);
+    if (2 < c.nsteps) prefill_issue<MT>(c, 2, b2, 2);
     for (int64_t s = 0; s < c.nsteps; s += 4) {
-        prefill_step(c, 0, b0, b3, s + 0, acc);
-        prefill_step(c, 1, b1, b0, s + 1, acc);
-        prefill_step(c, 2, b2, b1, s + 2, acc);
-        prefill_step(c, 3, b3, b2, s + 3, acc);
+        prefill_step<MT>(c, 0, b0, b3, s + 0, acc);
+        prefill_step<MT>(c, 1, b1, b0, s + 1, acc);
+        prefill_step<MT>(c, 2, b2, b1, s + 2, acc);
+        prefill_step<MT>(c, 3, b3, b2, s + 3, acc);
     }
 
     // Epilogue: element 4j + q of tile (i, t) is row 32i + 8j + 4lg + q, column 32t + ln.
     if (!group_ok) return;
     const int ln = c.ln, lg = c.lg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MT; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -363,34 +273,33 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
     }
 }
 
-template <int MT, int WM, int WN>
-static int launch_cfg(const GemmArgs& a, int64_t ntn, int64_t ntm, bool grouped, hipStream_t stream) {
-    dim3 grid((unsigned)ntn, (unsigned)ntm);
-    if (grouped)
-        hipLaunchKernelGGL((gemm_mfma_kernel<MT, WM, WN, true>), grid, dim3(64 * WM * WN), 0, stream, a);
-    else
-        hipLaunchKernelGGL((gemm_mfma_kernel<MT, WM, WN, false>), grid, dim3(64 * WM * WN), 0, stream, a);
-    BL_LAUNCH_CHECK();
-    return BITLINEAR_OK;
-}
+// Column tile width (output rows of W per workgroup) of the prefill kernel.
+static int gemm_bn(int64_t M) { (void)M; return kPreBN; }
 
-// Column tile width (output rows of W per workgroup) of the variant used for M.
-static int gemm_bn(int64_t M) { return M <= 64 ? 256 : kPreBN; }
+// Prefill tile height.  64-row tiles (158 VGPRs, 32 KB LDS: three workgroups
+// per CU, 768 slots on 256 CUs) balance far better at prefill sizes such as
+// M = 2048; 128-row tiles (two per CU) reuse each expanded weight word twice
+// as often and only pay off once the grid is many rounds deep.
+static int prefill_mt(int64_t M, int64_t N) {
+    const int64_t t64 = ceil_div(M, 64) * ceil_div(N, kPreBN);
+    return t64 <= 4 * 768 ? 2 : 4;
+}
 
 static int dispatch(GemmArgs& a, int64_t ntn, bool grouped, hipStream_t stream) {
     const int64_t M = a.M;
-    if (M <= 16) return launch_cfg<1, 1, 4>(a, ntn, 1, grouped, stream);
-    if (M <= 32) return launch_cfg<2, 1, 4>(a, ntn, 1, grouped, stream);
-    if (M <= 64) return launch_cfg<4, 1, 4>(a, ntn, 1, grouped, stream);
-    const int64_t ntm = ceil_div(M, kPreBM);
-    if (grouped) {
-        hipLaunchKernelGGL((gemm_prefill_kernel<true>), dim3((unsigned)ntn, (unsigned)ntm), dim3(256),
-                           0, stream, a);
+    if (grouped) {   // grouped prefill keeps 128-row tiles (grid.y = row tiles)
+        hipLaunchKernelGGL((gemm_prefill_kernel<4, true>), dim3((unsigned)ntn, (unsigned)ceil_div(M, 128)),
+                           dim3(256), 0, stream, a);
     } else {
+        const int mt = prefill_mt(M, a.p.N);
         a.ntiles_n = ntn;
-        a.ntiles_m = ntm;
-        hipLaunchKernelGGL((gemm_prefill_kernel<false>), dim3((unsigned)(ntn * ntm)), dim3(256), 0,
-                           stream, a);
+        a.ntiles_m = ceil_div(M, 32 * mt);
+        if (mt == 2)
+            hipLaunchKernelGGL((gemm_prefill_kernel<2, false>), dim3((unsigned)(ntn * a.ntiles_m)),
+                               dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL((gemm_prefill_kernel<4, false>), dim3((unsigned)(ntn * a.ntiles_m)),
+                               dim3(256), 0, stream, a);
     }
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;

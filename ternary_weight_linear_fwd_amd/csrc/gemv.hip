@@ -177,6 +177,14 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(const int32_t* __r
     if (y_int) y_int[i] = acc;
 }
 
+int launch_splitk_epilogue(const int32_t* partial, int S, int64_t M, const Problem& p,
+                           hipStream_t stream) {
+    hipLaunchKernelGGL(splitk_epilogue_kernel, dim3((unsigned)ceil_div(M * p.N, 256)), dim3(256), 0,
+                       stream, partial, S, M, (int64_t)p.N, p.eta, p.gamma, p.y, p.y_int);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
+
 int gemv_split_slices(int64_t M, int64_t N, int64_t K) {
     (void)M;
     const int64_t G = ceil_div(N, 64), Kb = ceil_div(K, 64);
@@ -218,12 +226,7 @@ int launch_gemv(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
         default: return BITLINEAR_EUNSUPPORTED;
     }
     BL_LAUNCH_CHECK();
-    if (a.sk.S > 1) {
-        hipLaunchKernelGGL(splitk_epilogue_kernel, dim3((unsigned)ceil_div(M * p.N, 256)),
-                           dim3(256), 0, stream, a.sk.partial, a.sk.S, M, (int64_t)p.N, p.eta,
-                           p.gamma, p.y, p.y_int);
-        BL_LAUNCH_CHECK();
-    }
+    if (a.sk.S > 1) return launch_splitk_epilogue(a.sk.partial, a.sk.S, M, p, stream);
     return BITLINEAR_OK;
 }
 

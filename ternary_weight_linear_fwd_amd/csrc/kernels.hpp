@@ -67,7 +67,20 @@ int launch_gemv(const Problem& p, int64_t M, void* ws, hipStream_t stream);
 int launch_gemv_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
                         hipStream_t stream);
 
-// ---- int8 MFMA contraction for M > 4 (gemm.hip)
+// Sum split-K partials [S][M][N] in slice order and apply the dequant epilogue.
+int launch_splitk_epilogue(const int32_t* partial, int S, int64_t M, const Problem& p,
+                           hipStream_t stream);
+
+// ---- decode contraction on int8 MFMA for 4 < M <= 64 (skinny.hip)
+constexpr int kSkinnyMaxM = 64;
+constexpr int kSkinnyRows = 256;   // output rows per workgroup
+int skinny_split_slices(int64_t M, int64_t N, int64_t K);
+size_t skinny_ws_bytes(int64_t M, int64_t N, int64_t K);
+int launch_skinny(const Problem& p, int64_t M, void* ws, hipStream_t stream);
+int launch_skinny_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
+                          hipStream_t stream);
+
+// ---- prefill contraction on int8 MFMA for M > 64 (gemm.hip)
 int launch_gemm(const Problem& p, int64_t M, hipStream_t stream);
 int gemm_tile_n(int64_t M);  // output rows per workgroup (column tile) for M
 int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,

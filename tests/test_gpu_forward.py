@@ -93,3 +93,11 @@ def test_determinism():
     a = forward(xq, eta, packed, 0.02, N)
     b = forward(xq, eta, packed, 0.02, N)
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
+
+
+# Shapes with more than 3072 tiles of 64 x 256 select the 128-row prefill
+# variant (smaller ones take 64-row tiles); both with ragged M, N and K.
+@pytest.mark.parametrize("M,N,K", [(130, 33000, 80), (257, 32832, 208), (200, 65600, 48),
+                                   (1000, 200000, 32), (1537, 131136, 16)])
+def test_prefill_tall_tiles(M, N, K):
+    run_case(M, N, K, seed=M + N + K, latent=False)
