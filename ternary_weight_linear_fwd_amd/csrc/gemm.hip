@@ -2,31 +2,45 @@
 //
 // Where many tokens share the weights (prefill, batched decode) the
 // contraction of [P2] "3. Additive Integer Accumulation" is a dense integer
-// product, so it runs on v_mfma_i32_16x16x64_i8 with int32 accumulation
-// (exact: |y_int| <= 127 * K < 2^31).
+// product; it runs on v_mfma_i32_32x32x32_i8 with int32 accumulation.
 //
-// Tiling.  A workgroup of WM x WN wavefronts computes a (WM*16*MT) x (WN*64)
-// output tile; each wavefront owns MT x 4 MFMA tiles of 16 x 16.  The K loop
-// advances 256 (four 64-k blocks) per step:
-//  * A (activations, int8): the workgroup copies its rows x 256 bytes into LDS
-//    with a 272-byte row stride (16-byte pad: the 16 rows a ds_read_b128
-//    serves fall in distinct banks).
-//  * B (weights): lane (n, g) of a wavefront loads the 16-byte chunk of row n
-//    for k-block kb + g straight from the packed layout (four 256-byte runs
-//    per wave load) and expands each 32-bit word into 16 ternary bytes in
-//    VGPRs (shift, mask, one byte-permute per 4 weights); no LDS for B.
-//  * Word d of that chunk feeds MFMA number d of the step for lane group g,
-//    so the four MFMAs of a step together cover the 256 k exactly once; A is
-//    read in the same (g, d) order.  The order of k inside a reduction is
-//    free, so only the A/B agreement matters.
-// Epilogue: y = float(acc) * ((eta[m] * gamma) / 127), fused.
+// Workgroup tile: BM = 32*MT token rows x 256 weight rows (output columns).
+// Four wavefronts sit side by side in N; each owns all BM rows x 64 columns
+// as MT x 2 MFMA tiles of 32 x 32, so every packed weight word is expanded
+// once per workgroup.  The K loop advances 128 (two 64-k blocks) per step
+// through a ring of three LDS stages, keeping two steps in flight ahead of
+// the one being computed.  Both operands arrive by direct global->LDS
+// loads (global_load_lds_dwordx4, 1 KB per wave instruction) whose completion
+// the kernel tracks itself: an explicit vmcnt wait and one barrier per step,
+// with no register destinations for the compiler to wait on.
+//  * A (int8 activations): BM rows x 128 bytes per stage.  Chunk c (16 bytes)
+//    of row r is stored at chunk c ^ ((r >> 1) & 7): the 16 rows one
+//    ds_read_b128 phase serves land on distinct banks, and each wave's 1 KB
+//    DMA stays contiguous.
+//  * B (packed codes): each wavefront copies its own two 1 KB blocks (64 rows
+//    x 64 k) exactly as they lie in the packed layout.
+// Lane (n, g) reads row n's 16-byte chunk of k-block 2*step + g; word d of it
+// feeds MFMA group d, whose 32 k are the two lane groups' 16-k runs, and A is
+// read in the same (g, d) order (the order of k inside a reduction is free;
+// only the A/B agreement matters).
+//
+// The codes go to the MFMA as they are: with c = w + 1 in {0, 1, 2} (field j
+// of a word is (w >> 2j) & 0x03030303),
+//     sum_k x_k w_k = sum_k x_k c_k - sum_k x_k .
+// The row sums sum_k x_k are taken from the same LDS fragments (v_dot4
+// against ones; wavefront w sums word group w of every step), so every k
+// whose code is 01 -- pads inside the last block, blocks past the end (forced
+// to 01), and k past K read from clamped addresses -- contributes equally to
+// both terms and cancels.  Raw codes also toggle far fewer multiplier bits
+// than -1/0/+1 bytes, which lets the matrix cores hold a higher clock.  int32 arithmetic wraps, so the difference is exact whenever the
+// result fits (|y_int| <= 127 K < 2^31).
+// Epilogue: y = float(y_int) * ((eta[m] * gamma) / 127), fused.
 #include "kernels.hpp"
 
 namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-
-constexpr int kLdsRowBytes = 272;  // 256 data bytes + 16 pad
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 struct GemmArgs {
     Problem p;                // single mode
@@ -38,38 +52,28 @@ struct GemmArgs {
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
-// XCD b % 8), each with its own L2.  Give each XCD a contiguous run of tiles
-// (column index fastest) so that its L2 serves a few A row blocks to all of
-// them and each B tile to the row blocks that run at the same time.
+// XCD b % 8), each with its own 4 MB L2.  Each XCD takes a contiguous run of
+// the tile order, and the order walks the grid in bands of `band` row tiles,
+// row index fastest inside a band, so the tiles an XCD runs at one time cover
+// a compact block (about 10 x 10 tiles of 64 x 256): its L2 then serves their
+// activation rows and weight columns to all of them.
 __device__ inline int64_t xcd_tile(int64_t b, int64_t T) {
     constexpr int64_t X = 8;
     const int64_t xcd = b % X, slot = b / X, q = T / X, r = T % X;
     return xcd * q + (xcd < r ? xcd : r) + slot;
 }
 
-// ---------------------------------------------------------------------------
-// Prefill variant (M > 64): 128 x 256 workgroup tile, four wavefronts side by
-// side in N; each owns all 128 rows x 64 columns as 4 x 2 tiles of
-// v_mfma_i32_32x32x32_i8, so every weight word is expanded exactly once per
-// workgroup.  The K loop advances 128 (two 64-k blocks) per step and keeps
-// three steps in flight ahead of the one being computed:
-//  * A: a four-stage LDS ring of 128 rows x 128 bytes, filled by direct
-//    global->LDS loads (global_load_lds_dwordx4, 1 KB per wave instruction).
-//    Chunk c (16 bytes) of row r is stored at chunk c ^ ((r >> 1) & 7): the 16
-//    rows one ds_read_b128 phase serves land on 16 distinct bank groups, with
-//    no padding, so each wave's 1 KB DMA stays contiguous.
-//  * B: the packed words go straight to registers (a four-slot ring); each
-//    lane expands them into ternary bytes right before the MFMAs that use
-//    them.  Lane (n, g) holds row n's k-block kb + g; word d feeds MFMA group
-//    d, whose 32 k are the two lane groups' 16-k runs; A is read in the same
-//    (g, d) order.
-// Rows past M and k past K are read from clamped (in-bounds) addresses: rows
-// past M are never stored, and every k past K meets a zero weight (pad code
-// 01 inside the last block, code 01 forced for blocks past the end).
-constexpr int kPreBN = 256;
-constexpr int kPreStages = 4;
+__device__ inline void tile_coords(int64_t b, int64_t ntm, int64_t ntn, int64_t band, int64_t& tm,
+                                   int64_t& tn) {
+    const int64_t t = xcd_tile(b, ntm * ntn);
+    const int64_t bi = t / (band * ntn);
+    const int64_t rows = ntm - bi * band < band ? ntm - bi * band : band;
+    const int64_t within = t - bi * band * ntn;
+    tm = bi * band + within % rows;
+    tn = within / rows;
+}
 
-typedef int v16i __attribute__((ext_vector_type(16)));
+constexpr int kPreBN = 256;
 
 // s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector memory
 // operations are outstanding; expcnt and lgkmcnt are left unconstrained.
@@ -80,77 +84,104 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // One 16-byte-per-lane direct global->LDS load (the wave's 64 lanes fill
-// 1 KB at lds_dst).  Kept as a plain (non-template) function: the host
-// compilation pass rejects template instantiations that name this builtin.
+// 1 KB at lds_dst).  This builtin keeps the LDS destination as a typed
+// address, so the compiler knows which LDS object the load writes and does
+// not make reads of the other stages wait for it.  Kept as a plain
+// (non-template) function: the host compilation pass rejects template
+// instantiations that name it.
 __device__ __forceinline__ void dma_16(const void* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+    __builtin_amdgcn_load_to_lds(const_cast<void*>(src),
+                                 (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
 template <int MT>
 struct PrefillCtx {
-    static constexpr int BM = 32 * MT;            // rows per workgroup tile
-    static constexpr int AStage = BM * 128;       // bytes of one A stage
+    static constexpr int BM = 32 * MT;            // token rows per workgroup tile
+    static constexpr int AStage = BM * 128;       // bytes of A per stage
+    static constexpr int Stage = AStage + 8192;   // + four wavefronts x two 1 KB B blocks
     static constexpr int NA = AStage / 4096;      // A DMA instructions per wave per step
-    uint8_t* lds;
+    static constexpr int Ops = NA + 2;            // vector memory instructions per wave per step
     const int8_t* asrc[NA];
     int acol[NA];
-    const uint4* brow;
+    const uint8_t* bsrc;   // this lane's 16 bytes of k-block 0 of the wavefront's row group
     int64_t K, Kb, nsteps;
     int wave, lane, ln, lg;
 };
 
-// Queue step `step`: this wave's NA 1 KB A DMAs into LDS stage `stage` and
-// this lane's two B chunks into registers: NA + 2 vector memory instructions.
+// Queue step `step` into LDS stage `stage`: this wave's NA activation DMAs and
+// its two weight-block DMAs.
 template <int MT>
-__device__ __forceinline__ void prefill_issue(const PrefillCtx<MT>& c, int stage, uint4 (&bq)[2],
-                                              int64_t step) {
-    uint8_t* st = c.lds + stage * PrefillCtx<MT>::AStage;
+__device__ __forceinline__ void prefill_issue(const PrefillCtx<MT>& c, uint8_t* st, int64_t step) {
+    using Ctx = PrefillCtx<MT>;
     const int64_t kbase = step * 128;
     const bool full = kbase + 128 <= c.K;
 #pragma unroll
-    for (int j = 0; j < PrefillCtx<MT>::NA; ++j) {
+    for (int j = 0; j < Ctx::NA; ++j) {
         const int8_t* src = c.asrc[j] + kbase;
         if (!full && kbase + c.acol[j] >= c.K) src = c.asrc[j] + (c.K - 16 - c.acol[j]);
         dma_16(src, st + (j * 4 + c.wave) * 1024);
     }
-    int64_t kb = step * 2 + c.lg;
-    kb = kb < c.Kb ? kb : c.Kb - 1;   // a block past the end is zeroed at use
 #pragma unroll
-    for (int t = 0; t < 2; ++t) bq[t] = c.brow[kb * 64 + t * 32];
+    for (int h = 0; h < 2; ++h) {
+        int64_t kb = step * 2 + h;
+        kb = kb < c.Kb ? kb : c.Kb - 1;   // a block past the end is replaced at use
+        dma_16(c.bsrc + kb * 1024, st + Ctx::AStage + (c.wave * 2 + h) * 1024);
+    }
 }
 
-// One K-step of MFMAs from LDS stage `stage` and the B words `bq`.
-template <int MT>
-__device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, int stage, const uint4 (&bq)[2],
-                                                int64_t step, v16i (&acc)[MT][2]) {
-    const uint8_t* A = c.lds + stage * PrefillCtx<MT>::AStage;
-    const bool kb_ok = step * 2 + c.lg < c.Kb;
-    uint4 bw[2];
+// One K-step of MFMAs from the LDS stage at A.  Wavefront w also adds word
+// group w of the step's A rows into the row sums `sx` (one extra fragment
+// read per row tile, four v_dot4 each).  TAIL: the step may be the last one,
+// whose second k-block can lie past the end.
+template <int MT, bool TAIL>
+__device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, const uint8_t* A, int64_t step,
+                                                v16i (&acc)[MT][2], int (&sx)[MT]) {
+    using Ctx = PrefillCtx<MT>;
+    // The masks bound every LDS offset visibly, so that the compiler can prove
+    // each read stays inside this stage's object and tell it apart from the
+    // loads in flight into the other stages.
+    const uint8_t* Bl = A + Ctx::AStage + ((c.wave & 3) * 2 + (c.lg & 1)) * 1024;
+    const v4i* Bv = reinterpret_cast<const v4i*>(Bl) + (c.ln & 31);
+    v4i bw[2];
+    bw[0] = Bv[0];
+    bw[1] = Bv[32];
+    if constexpr (TAIL) {
+        if (step * 2 + 1 >= c.Kb && c.lg == 1) {   // k-block past the end: code 01
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-        bw[t] = kb_ok ? bq[t] : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-    // Two register sets for the A fragments and the expanded B words: group
-    // d+1's LDS reads and expansion run while group d's eight MFMAs execute.
+            for (int t = 0; t < 2; ++t) bw[t] = v4i{0x55555555, 0x55555555, 0x55555555, 0x55555555};
+        }
+    }
+    auto a_frag = [&](int i, int d) {
+        const int r = i * 32 + (c.ln & 31);
+        return *reinterpret_cast<const v4i*>(A + r * 128 + ((((c.lg & 1) * 4 + (d & 3)) ^ ((r >> 1) & 7)) << 4));
+    };
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const v4i f = a_frag(i, c.wave);
+        sx[i] = __builtin_amdgcn_sdot4(f.x, 0x01010101, sx[i], false);
+        sx[i] = __builtin_amdgcn_sdot4(f.y, 0x01010101, sx[i], false);
+        sx[i] = __builtin_amdgcn_sdot4(f.z, 0x01010101, sx[i], false);
+        sx[i] = __builtin_amdgcn_sdot4(f.w, 0x01010101, sx[i], false);
+    }
+    // Two register sets for the A fragments and the B codes: group d+1's LDS
+    // reads and field extraction run while group d's MFMAs execute.
     v4i af[2][MT], bf[2][2];
     auto load_a = [&](v4i (&dst)[MT], int d) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int r = i * 32 + c.ln;
-            dst[i] = *reinterpret_cast<const v4i*>(A + r * 128 + (((c.lg * 4 + d) ^ ((r >> 1) & 7)) << 4));
-        }
+        for (int i = 0; i < MT; ++i) dst[i] = a_frag(i, d);
     };
-    auto expand_b = [&](v4i (&dst)[2], int d) {
+    auto fields = [&](v4i (&dst)[2], int d) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const uint32_t w = d == 0 ? bw[t].x : d == 1 ? bw[t].y : d == 2 ? bw[t].z : bw[t].w;
-            dst[t].x = (int)codes_to_ternary(w & 0x03030303u);
-            dst[t].y = (int)codes_to_ternary((w >> 2) & 0x03030303u);
-            dst[t].z = (int)codes_to_ternary((w >> 4) & 0x03030303u);
-            dst[t].w = (int)codes_to_ternary((w >> 6) & 0x03030303u);
+            const uint32_t w = (uint32_t)bw[t][d];
+            dst[t].x = (int)(w & 0x03030303u);
+            dst[t].y = (int)((w >> 2) & 0x03030303u);
+            dst[t].z = (int)((w >> 4) & 0x03030303u);
+            dst[t].w = (int)((w >> 6) & 0x03030303u);
         }
     };
     load_a(af[0], 0);
-    expand_b(bf[0], 0);
+    fields(bf[0], 0);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const int cur = d & 1;
@@ -161,33 +192,48 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, int sta
 #pragma unroll
             for (int i = 0; i < MT; ++i)
                 acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][t], acc[i][t], 0, 0, 0);
-        if (d < 3) expand_b(bf[cur ^ 1], d + 1);
+        if (d < 3) fields(bf[cur ^ 1], d + 1);
     }
 }
 
-// Step `step` of the ring: wait for its data (exactly: the steps issued after
-// it may stay in flight), make that true for every wave, refill the stage
-// freed by step-1 with step+3, compute.  Every LDS read of that stage fed an
-// MFMA before the barrier.  A plain s_barrier: __syncthreads() would also
-// drain the DMAs still in flight.
+// A step of the ring that is not among the last two: wait until its data has
+// landed (the next step's loads stay in flight), make that true for every
+// wave, refill the stage that step-1 read (every wave is past it) with
+// step+2, compute.  Straight-line code, so that the compiler can see which
+// stage each LDS read and each load in flight touch and adds no waits of its
+// own.
 template <int MT>
-__device__ __forceinline__ void prefill_step(const PrefillCtx<MT>& c, int stage, const uint4 (&bcur)[2],
-                                             uint4 (&bnext)[2], int64_t step, v16i (&acc)[MT][2]) {
-    constexpr int ops = PrefillCtx<MT>::NA + 2;   // vector memory instructions per step
+__device__ __forceinline__ void prefill_step(const PrefillCtx<MT>& c, const uint8_t* cur, uint8_t* refill,
+                                             int64_t step, v16i (&acc)[MT][2], int (&sx)[MT]) {
+    wait_vmcnt<PrefillCtx<MT>::Ops>();
+    __builtin_amdgcn_s_barrier();   // not __syncthreads(): that would drain the loads in flight
+    prefill_issue<MT>(c, refill, step + 2);
+    prefill_compute<MT, false>(c, cur, step, acc, sx);
+}
+
+// Any step, including the last ones (nothing left to refill, or past the end).
+template <int MT>
+__device__ __forceinline__ void prefill_step_tail(const PrefillCtx<MT>& c, const uint8_t* cur, uint8_t* refill,
+                                                  int64_t step, v16i (&acc)[MT][2], int (&sx)[MT]) {
     if (step >= c.nsteps) return;
-    if (step + 2 < c.nsteps) wait_vmcnt<2 * ops>();
-    else if (step + 1 < c.nsteps) wait_vmcnt<ops>();
+    if (step + 1 < c.nsteps) wait_vmcnt<PrefillCtx<MT>::Ops>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (step + 3 < c.nsteps) prefill_issue<MT>(c, (stage + 3) & 3, bnext, step + 3);
-    prefill_compute<MT>(c, stage, bcur, step, acc);
+    if (step + 2 < c.nsteps) prefill_issue<MT>(c, refill, step + 2);
+    prefill_compute<MT, true>(c, cur, step, acc, sx);
 }
 
 template <int MT, bool GROUPED>
-__global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefill_kernel(GemmArgs a) {
     using Ctx = PrefillCtx<MT>;
-    constexpr int kPreBM = Ctx::BM;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kPreStages * Ctx::AStage];
+    constexpr int BM = Ctx::BM;
+    // Three stages, each its own LDS object, so that the compiler can tell a
+    // read of one stage from the loads in flight into the others.
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[Ctx::Stage];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[Ctx::Stage];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage2[Ctx::Stage];
+    __shared__ int rowsum_part[8][BM];   // [wave * 2 + lane group][row]
+    __shared__ int rowsum[BM];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -201,17 +247,14 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
         tile_m = blockIdx.y;
     } else {
         p = a.p;
-        const int64_t tile = xcd_tile(blockIdx.x, a.ntiles_n * a.ntiles_m);
-        tile_m = tile / a.ntiles_n;
-        tile_n = tile - tile_m * a.ntiles_n;
+        tile_coords(blockIdx.x, a.ntiles_m, a.ntiles_n, 16 / MT, tile_m, tile_n);
     }
     const int64_t M = a.M, N = p.N, K = p.K, Kb = p.Kb;
-    const int64_t m0 = tile_m * kPreBM;
+    const int64_t m0 = tile_m * BM;
     const int64_t group = tile_n * 4 + wave;
     const bool group_ok = group < ceil_div(N, 64);
 
     Ctx c;
-    c.lds = lds;
     c.K = K;
     c.Kb = Kb;
     c.nsteps = ceil_div(Kb, 2);
@@ -227,26 +270,46 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
         const int64_t m = m0 + r < M ? m0 + r : M - 1;
         c.asrc[j] = p.xq + m * K + c.acol[j];
     }
-    c.brow = p.packed + (group_ok ? group : 0) * Kb * 64 + c.ln;
+    c.bsrc = reinterpret_cast<const uint8_t*>(p.packed) + (group_ok ? group : 0) * Kb * 1024 + lane * 16;
 
     v16i acc[MT][2];
+    int sx[MT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i) {
+        sx[i] = 0;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][t][e] = 0;
-
-    uint4 b0[2], b1[2], b2[2], b3[2];
-    if (0 < c.nsteps) prefill_issue<MT>(c, 0, b0, 0);
-    if (1 < c.nsteps) prefill_issue<MT>(c, 1, b1, 1);
-    if (2 < c.nsteps) prefill_issue<MT>(c, 2, b2, 2);
-    for (int64_t s = 0; s < c.nsteps; s += 4) {
-        prefill_step<MT>(c, 0, b0, b3, s + 0, acc);
-        prefill_step<MT>(c, 1, b1, b0, s + 1, acc);
-        prefill_step<MT>(c, 2, b2, b1, s + 2, acc);
-        prefill_step<MT>(c, 3, b3, b2, s + 3, acc);
     }
+
+    // Steps 0 and 1 are always queued (past the end they read clamped, in-bounds
+    // addresses and are never used), so that no branch precedes the main loop.
+    prefill_issue<MT>(c, stage0, 0);
+    prefill_issue<MT>(c, stage1, 1);
+    int64_t step = 0;
+    for (; step + 5 <= c.nsteps; step += 3) {
+        prefill_step<MT>(c, stage0, stage2, step, acc, sx);
+        prefill_step<MT>(c, stage1, stage0, step + 1, acc, sx);
+        prefill_step<MT>(c, stage2, stage1, step + 2, acc, sx);
+    }
+    // The last two to four steps.
+    prefill_step_tail<MT>(c, stage0, stage2, step, acc, sx);
+    prefill_step_tail<MT>(c, stage1, stage0, step + 1, acc, sx);
+    prefill_step_tail<MT>(c, stage2, stage1, step + 2, acc, sx);
+    prefill_step_tail<MT>(c, stage0, stage2, step + 3, acc, sx);
+
+    // Row sums: partials of (wave, lane group) -> one total per tile row.
+#pragma unroll
+    for (int i = 0; i < MT; ++i) rowsum_part[wave * 2 + c.lg][i * 32 + c.ln] = sx[i];
+    __syncthreads();
+    if (tid < BM) {
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) t += rowsum_part[w][tid];
+        rowsum[tid] = t;
+    }
+    __syncthreads();
 
     // Epilogue: element 4j + q of tile (i, t) is row 32i + 8j + 4lg + q, column 32t + ln.
     if (!group_ok) return;
@@ -257,15 +320,17 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill_kernel(GemmArgs a) {
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t m = m0 + i * 32 + j * 8 + lg * 4 + q;
+                const int r = i * 32 + j * 8 + lg * 4 + q;
+                const int64_t m = m0 + r;
                 if (m >= M) continue;
-                const float sc = dequant_scale(p.eta[m], p.gamma);
+                const float sc_m = dequant_scale(p.eta[m], p.gamma);
+                const int xs = rowsum[r];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int64_t n = group * 64 + t * 32 + ln;
                     if (n >= N) continue;
-                    const int v = acc[i][t][j * 4 + q];
-                    p.y[m * N + n] = dequant(v, sc);
+                    const int v = (int)((uint32_t)acc[i][t][j * 4 + q] - (uint32_t)xs);
+                    p.y[m * N + n] = dequant(v, sc_m);
                     if (p.y_int) p.y_int[m * N + n] = v;
                 }
             }
