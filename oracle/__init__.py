@@ -52,6 +52,8 @@ class Oracle:
         L.oracle_dequant.argtypes = [P, P, ctypes.c_float, I64, I64, P]
         L.oracle_forward.argtypes = [P, P, ctypes.c_float, I64, I64, I64, P, P, P, P,
                                      ctypes.c_int]
+        L.oracle_rmsnorm.argtypes = [P, I64, I64, P, P, P]
+        L.oracle_rmsnorm_quantize_act.argtypes = [P, I64, I64, P, P, P, P]
         L.oracle_packed_row_bytes.argtypes = [I64]
         L.oracle_packed_row_bytes.restype = I64
         self.lib = L
@@ -102,6 +104,29 @@ class Oracle:
         eta = np.empty(M, np.float32)
         _check(self.lib.oracle_quantize_act(_p(x), M, K, _p(xq), _p(eta)), "quantize_act")
         return xq, eta
+
+    def rmsnorm(self, x: np.ndarray):
+        """RMSNorm without affine parameters: (x_norm [M][K], ms [M], norm [M]),
+        ms being the mean of the squares and norm = 1 / sqrt(ms + 1e-6)."""
+        x = _c(x, np.float32)
+        M, K = x.shape
+        xn = np.empty((M, K), np.float32)
+        ms = np.empty(M, np.float32)
+        norm = np.empty(M, np.float32)
+        _check(self.lib.oracle_rmsnorm(_p(x), M, K, _p(xn), _p(ms), _p(norm)), "rmsnorm")
+        return xn, ms, norm
+
+    def rmsnorm_quantize_act(self, x: np.ndarray):
+        """RMSNorm, then the absmax quantizer: (xq, eta, ms, norm)."""
+        x = _c(x, np.float32)
+        M, K = x.shape
+        xq = np.empty((M, K), np.int8)
+        eta = np.empty(M, np.float32)
+        ms = np.empty(M, np.float32)
+        norm = np.empty(M, np.float32)
+        _check(self.lib.oracle_rmsnorm_quantize_act(_p(x), M, K, _p(xq), _p(eta), _p(ms),
+                                                    _p(norm)), "rmsnorm_quantize_act")
+        return xq, eta, ms, norm
 
     def ternary_contract(self, xq: np.ndarray, Wt: np.ndarray, threads: int = 1) -> np.ndarray:
         xq = _c(xq, np.int8)
@@ -228,3 +253,11 @@ def forward(x, Wt, gamma, threads=1):
 
 def forward_q(xq, eta, Wt, gamma, threads=1):
     return default().forward_q(xq, eta, Wt, gamma, threads)
+
+
+def rmsnorm(x):
+    return default().rmsnorm(x)
+
+
+def rmsnorm_quantize_act(x):
+    return default().rmsnorm_quantize_act(x)

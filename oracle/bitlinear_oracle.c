@@ -32,8 +32,12 @@
  *  - Dequant: s = (eta * gamma) / 127 in float32, y = float(y_int) * s.
  *  - Canonical 2-bit code: -1 -> 00, 0 -> 01, +1 -> 10; weight j of a byte sits
  *    in bits 2j..2j+1; a row holds ceil(K/4) bytes and pads with code 01.
+ *  - RMSNorm (the optional step before quantization): the mean of x^2 is the
+ *    exact mean rounded once to float32; norm = 1 / sqrt(ms + 1e-6) as an IEEE
+ *    square root and an IEEE division; x_norm = x * norm.
  */
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <math.h>
 #include <pthread.h>
@@ -43,9 +47,10 @@
 
 /* ------------------------------------------------------------------------ */
 /* Exact arithmetic on non-negative integers held as little-endian 32-bit    */
-/* limbs.  Used only by the gamma computation.                               */
+/* limbs.  Used only by the gamma and mean-of-squares computations.          */
 /* ------------------------------------------------------------------------ */
-#define OR_LIMBS 14 /* 448 bits: the exact sum of up to 2^40 |floats| needs 318 */
+#define OR_LIMBS 20 /* 640 bits: the exact sum of up to 2^40 |floats| needs 318
+                       bits, of up to 2^31 squared floats 586 */
 
 typedef struct { uint32_t w[OR_LIMBS]; } or_big;
 
@@ -75,6 +80,51 @@ static int big_bitlen(const or_big* a) {
 static int big_bit(const or_big* a, int pos) {
     if (pos < 0 || pos >= OR_LIMBS * 32) return 0;
     return (a->w[pos / 32] >> (pos % 32)) & 1u;
+}
+
+/* 1 if any bit of a below position pos is set */
+static int big_any_below(const or_big* a, int pos) {
+    for (int i = 0; i < pos && i < OR_LIMBS * 32; ++i)
+        if (big_bit(a, i)) return 1;
+    return 0;
+}
+
+/*
+ * The float32 nearest to S * 2^unit / D (S a non-negative big integer, D in
+ * [1, 2^40)), ties to even, with subnormal results and overflow to +Inf.
+ * Plain long division, one quotient bit at a time from the top: the first
+ * quotient 1 fixes the exponent and with it the last significand position
+ * (23 places lower, but never below the 2^-149 subnormal step); the next bit
+ * rounds, and every bit after it, with the final remainder, is sticky.
+ */
+static float big_ratio_to_f32(const or_big* S, int unit, uint64_t D) {
+    const int L = big_bitlen(S);
+    if (L == 0) return 0.0f;
+    uint64_t rem = 0, sig = 0;
+    int started = 0, p_lsb = 0, rb = 0, sticky = 0;
+    for (int pos = L - 1;; --pos) {
+        rem = (rem << 1) | (uint64_t)big_bit(S, pos);   /* zero bits once pos < 0 */
+        int qb = 0;
+        if (rem >= D) { rem -= D; qb = 1; }
+        const int a = pos + unit;                       /* this quotient bit weighs 2^a */
+        if (!started) {
+            if (a <= -151) return 0.0f;                 /* below half the smallest subnormal */
+            if (!qb) continue;
+            started = 1;
+            p_lsb = a - 23 > -149 ? a - 23 : -149;
+        }
+        if (a >= p_lsb) {
+            sig = (sig << 1) | (uint64_t)qb;
+        } else if (a == p_lsb - 1) {
+            rb = qb;
+            sticky = rem != 0 || big_any_below(S, pos);
+            break;
+        }
+    }
+    if (rb && (sticky || (sig & 1u))) ++sig;             /* round half to even */
+    if (sig == (1u << 24)) { sig >>= 1; ++p_lsb; }       /* carry into the next binade */
+    if (p_lsb + 23 > 127) return INFINITY;               /* beyond the largest float32 */
+    return (float)ldexp((double)sig, p_lsb);             /* exact: sig < 2^24, in range */
 }
 
 /*
@@ -231,6 +281,74 @@ int oracle_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float*
         }
     }
     return 0;
+}
+
+/*
+ * RMSNorm without affine parameters, the step before activation quantization.
+ * [P1] pipeline box 1 ("RMSNorm") and step 1 of BitLinear158.forward in
+ * "Production PyTorch Implementation: BitLinear b1.58 Layer" (norm = rsqrt of
+ * the mean of x^2 over the last dim plus 1e-6; x_norm = x * norm); [P1] "2.
+ * Absmax Dynamic Activation Quantization" (normalization without learnable
+ * affine parameters precedes the quantizer); [P2] "2. Absmax Activation
+ * Quantization" (normalization before quantization).
+ *
+ * Readings (the pages leave these open):
+ *  - the mean of the squares is the exact mean, rounded once to the nearest
+ *    float32 (ties to even): every finite float32 is sig * 2^(t - 149), so its
+ *    square is sig^2 * 2^(2t - 298) and the row sum is an exact integer count
+ *    of 2^-298 units;
+ *  - rsqrt is evaluated as two IEEE float32 operations, a square root and a
+ *    division: norm = 1 / sqrt(ms + 1e-6), each step rounded to nearest even;
+ *  - x_norm = x * norm in float32.
+ * ms_out and norm_out (each [M], may be NULL) receive the per-row mean of the
+ * squares and the factor.
+ */
+#define OR_RMS_EPS 1e-6f
+
+int oracle_rmsnorm(const float* x, int64_t M, int64_t K, float* xn, float* ms_out,
+                   float* norm_out) {
+    if (!x || !xn || M < 0 || K <= 0) return -1;
+    if (K >> 40) return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        const float* row = x + m * K;
+        or_big S;
+        big_zero(&S);
+        for (int64_t k = 0; k < K; ++k) {
+            uint32_t bits;
+            memcpy(&bits, &row[k], 4);
+            bits &= 0x7fffffffu;
+            uint32_t e = bits >> 23, f = bits & 0x7fffffu;
+            if (e == 255) return -2;                     /* Inf/NaN: outside the contract */
+            uint64_t sig = e ? (f | 0x800000u) : f;
+            int ex = e ? (int)e - 1 : 0;                 /* |x| = sig * 2^(ex-149) */
+            uint64_t sq = sig * sig;                     /* < 2^48: x^2 = sq * 2^(2ex-298) */
+            if (sq) {
+                big_add_shifted(&S, (uint32_t)(sq & 0xffffffffu), 2 * ex);
+                big_add_shifted(&S, (uint32_t)(sq >> 32), 2 * ex + 32);
+            }
+        }
+        const float ms = big_ratio_to_f32(&S, -298, (uint64_t)K);
+        const float t = ms + OR_RMS_EPS;                 /* mean + 1e-6 */
+        const float s = sqrtf(t);                        /* IEEE square root */
+        const float norm = 1.0f / s;                     /* IEEE division */
+        for (int64_t k = 0; k < K; ++k) xn[m * K + k] = row[k] * norm;
+        if (ms_out) ms_out[m] = ms;
+        if (norm_out) norm_out[m] = norm;
+    }
+    return 0;
+}
+
+/* RMSNorm followed by the absmax quantizer on the normalized rows. */
+int oracle_rmsnorm_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta,
+                                float* ms_out, float* norm_out) {
+    if (!x || !xq || !eta || M < 0 || K <= 0) return -1;
+    if (M == 0) return 0;
+    float* xn = (float*)malloc((size_t)M * (size_t)K * sizeof(float));
+    if (!xn) return -6;
+    int rc = oracle_rmsnorm(x, M, K, xn, ms_out, norm_out);
+    if (!rc) rc = oracle_quantize_act(xn, M, K, xq, eta);
+    free(xn);
+    return rc;
 }
 
 /*

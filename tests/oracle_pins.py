@@ -438,4 +438,148 @@ def pin_demo_shapes(O):
     assert np.array_equal(y_int, xq.astype(np.int64) @ Wt.astype(np.int64).T)
 
 
+# ------------------------------------------------------------------ RMSNorm
+# RMSNorm without affine parameters before the quantizer (first page, step 1 of
+# BitLinear158.forward): norm = 1 / sqrt(mean(x^2) + 1e-6), x_norm = x * norm.
+# The mean is exact and rounded once; sqrt and 1/s are IEEE float32 steps.
+
+def _rms_eps() -> np.float32:
+    return f32(page_constants()["rms_eps"][0][0])
+
+
+def _sqrt_f32(t: np.float32) -> np.float32:
+    """Correctly rounded float32 square root, decided by exact comparison of
+    squares (no library square root is trusted)."""
+    tf = Fraction(float(t))
+    if tf == 0:
+        return f32(0)
+    c = np.float32(np.sqrt(np.float64(t)))
+    cands = sorted({c, np.nextafter(c, f32(0)), np.nextafter(c, f32(np.inf))})
+    best = None
+    for v in cands:
+        # |v - sqrt(t)| compared through (v^2 - t) / (v + sqrt(t)); equivalently
+        # compare the candidates' midpoints: sqrt(t) lies above mid iff t > mid^2
+        if best is None:
+            best = v
+            continue
+        mid = (Fraction(float(best)) + Fraction(float(v))) / 2
+        if tf > mid * mid:
+            best = v
+        elif tf == mid * mid and int(np.float32(v).view(np.uint32)) % 2 == 0:
+            best = v
+    return np.float32(best)
+
+
+def _rms_chain(row: np.ndarray):
+    """(ms, norm, x_norm) of one row by exact rational arithmetic."""
+    S = sum((Fraction(float(v)) ** 2 for v in row), Fraction(0))
+    ms = nearest_f32(S / len(row)) if S else f32(0)
+    t = np.float32(_fl32(Fraction(float(ms)) + Fraction(float(_rms_eps()))))
+    s = _sqrt_f32(t)
+    norm = np.float32(_fl32(1 / Fraction(float(s))))
+    xn = np.array([_fl32(Fraction(float(v)) * Fraction(float(norm))) for v in row], np.float32)
+    return ms, norm, xn
+
+
+def pin_rms_hand(O):
+    # x = [768, 1024, 0, 0]: sum of squares 1638400, mean 409600 = 640^2, so
+    # s = 640 and norm = fl(1/640); x_norm = 768 / 640 and 1024 / 640 up to one
+    # rounding: eta = fl(1024 * fl(1/640)) = fl(1.6) since 1024 is a power of
+    # two, and round(127 * 1.2 / 1.6) = round(95.25) = 95.
+    x = np.array([[768, 1024, 0, 0]], np.float32)
+    xq, eta, ms, norm = O.rmsnorm_quantize_act(x)
+    assert ms[0] == f32(409600)
+    assert Fraction(float(norm[0])) == _fl32(Fraction(1, 640))
+    assert Fraction(float(eta[0])) == _fl32(Fraction(8, 5))
+    assert xq.tolist() == [[95, 127, 0, 0]]
+
+
+def pin_rms_constant_rows(O):
+    # A row of +-2^j (j >= 4): mean of squares 2^(2j) exactly, 1e-6 is below
+    # half an ulp of it, sqrt = 2^j, norm = 2^-j, so x_norm = +-1 exactly.
+    rng = np.random.default_rng(11)
+    for j in (4, 5, 10, 40):
+        for K in (1, 3, 64, 1000):
+            sign = np.where(rng.random(K) < 0.5, -1.0, 1.0).astype(np.float32)
+            x = (sign * np.float32(2.0 ** j))[None, :]
+            xn, ms, norm = O.rmsnorm(x)
+            assert ms[0] == f32(2.0 ** (2 * j)) and norm[0] == f32(2.0 ** -j)
+            assert np.array_equal(xn[0], sign)
+            xq, eta, _, _ = O.rmsnorm_quantize_act(x)
+            assert eta[0] == f32(1) and np.array_equal(xq[0], (sign * 127).astype(np.int8))
+
+
+def pin_rms_exact_sum(O):
+    # One large element and many ones: a float32 running sum absorbs every one
+    # (2^24 + 1 = 2^24); the exact mean keeps them.  K = 1024, step 2^-9 there.
+    big = [4096.0]
+    for ones, want in ((1023, 16385.0),                  # 511.5 steps: tie, up to even
+                       (1022, 16384 + 511 / 512),        # 511 steps: exact
+                       (1021, 16384 + 510 / 512)):       # 510.5 steps: tie, down to even
+        row = np.array(big + [1.0] * ones + [0.0] * (1023 - ones), np.float32)
+        _, ms, _ = O.rmsnorm(row[None, :])
+        assert ms[0] == f32(want), (ones, ms[0], want)
+        assert Fraction(float(ms[0])) == Fraction(float(nearest_f32(Fraction(2 ** 24 + ones, 1024))))
+
+
+def pin_rms_rational(O):
+    # Random rows over a wide exponent range, zeros and subnormals included,
+    # against the exact rational chain.
+    rng = np.random.default_rng(12)
+    for K in (1, 2, 5, 17, 64):
+        for _ in range(6):
+            mant = rng.uniform(1, 2, K) * np.where(rng.random(K) < 0.5, -1, 1)
+            expo = rng.integers(-60, 60, K)
+            row = (mant * np.exp2(expo)).astype(np.float32)
+            row[rng.random(K) < 0.15] = 0
+            if K > 2:
+                row[0] = np.float32(3e-41)               # a subnormal
+            xn, ms, norm = O.rmsnorm(row[None, :])
+            ems, enorm, exn = _rms_chain(row)
+            assert ms[0] == ems and norm[0] == enorm, (K, ms[0], ems, norm[0], enorm)
+            assert np.array_equal(xn[0], exn)
+    # Tiny rows whose mean of squares is a float32 subnormal (or rounds to 0).
+    for K in (1, 3, 8):
+        for lo in (-75, -70, -66):
+            row = (rng.uniform(1, 2, K) * np.exp2(rng.integers(lo, lo + 4, K))).astype(np.float32)
+            _, ms, _ = O.rmsnorm(row[None, :])
+            ems, _, _ = _rms_chain(row)
+            assert ms[0] == ems, (K, lo, ms[0], ems)
+            assert ms[0] < np.finfo(np.float32).tiny
+
+
+def pin_rms_extremes(O):
+    # Squares beyond float32: the mean rounds to +Inf, norm to 0, the row to 0.
+    x = np.full((1, 16), 1e20, np.float32)
+    xq, eta, ms, norm = O.rmsnorm_quantize_act(x)
+    assert np.isinf(ms[0]) and norm[0] == 0 and not xq.any() and eta[0] == f32(1e-5)
+    # All zeros: mean 0, norm = 1 / sqrt(1e-6), nothing to quantize.
+    z = np.zeros((1, 16), np.float32)
+    xq, eta, ms, norm = O.rmsnorm_quantize_act(z)
+    want = np.float32(_fl32(1 / Fraction(float(_sqrt_f32(_rms_eps())))))
+    assert ms[0] == 0 and norm[0] == want and not xq.any() and eta[0] == f32(1e-5)
+
+
+def pin_rms_invariants(O):
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((6, 300)) * np.exp2(rng.integers(-8, 8, (6, 1)))).astype(np.float32)
+    x[2, 7] = 3e4                                        # mixed magnitudes
+    xn, ms, norm = O.rmsnorm(x)
+    xq, eta, ms2, norm2 = O.rmsnorm_quantize_act(x)
+    assert np.array_equal(ms, ms2) and np.array_equal(norm, norm2)
+    for m in range(x.shape[0]):
+        # rounding is monotone, so the largest |x_norm| is fl(max|x| * norm)
+        amax = np.float32(np.abs(x[m]).max())
+        assert Fraction(float(eta[m])) == _fl32(Fraction(float(amax)) * Fraction(float(norm[m])))
+        # the exact mean does not depend on the order of the terms
+        p = rng.permutation(x.shape[1])
+        _, msp, _ = O.rmsnorm(x[m, p][None, :])
+        assert msp[0] == ms[m]
+        # scaling by 4 scales the mean by 16 exactly while ms >= 32 (1e-6 then
+        # vanishes in the sum), so x_norm is unchanged
+        if ms[m] >= 32:
+            xn4, ms4, _ = O.rmsnorm((x[m] * 4)[None, :])
+            assert ms4[0] == ms[m] * 16 and np.array_equal(xn4[0], xn[m])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -50,6 +50,23 @@ MUTANTS = {
                             "for (int64_t k = 0; k + 1 < j->K; ++k) {\n                if (wr[k]"),
     "contract_transposed_store": ("j->y[m * j->N + n] = (int32_t)acc;",
                                   "j->y[n * j->M + m] = (int32_t)acc;"),
+    # RMSNorm
+    "rms_mean_over_k_minus_1": ("const float ms = big_ratio_to_f32(&S, -298, (uint64_t)K);",
+                                "const float ms = big_ratio_to_f32(&S, -298, (uint64_t)(K > 1 ? K - 1 : 1));"),
+    "rms_abs_not_square": ("uint64_t sq = sig * sig;", "uint64_t sq = sig;"),
+    "rms_no_eps": ("const float t = ms + OR_RMS_EPS;", "const float t = ms;"),
+    "rms_eps_1e5": ("#define OR_RMS_EPS 1e-6f", "#define OR_RMS_EPS 1e-5f"),
+    "rms_no_sqrt": ("const float s = sqrtf(t);", "const float s = t;"),
+    "rms_divide_by_s": ("xn[m * K + k] = row[k] * norm;", "xn[m * K + k] = row[k] / s;"),
+    "rms_float_running_sum": ("const float ms = big_ratio_to_f32(&S, -298, (uint64_t)K);",
+                              "float fs = 0.0f;\n"
+                              "        for (int64_t q = 0; q < K; ++q) fs += row[q] * row[q];\n"
+                              "        const float ms = fs / (float)K;"),
+    "ratio_truncates": ("if (rb && (sticky || (sig & 1u))) ++sig;             /* round half to even */", ""),
+    "ratio_no_sticky": ("sticky = rem != 0 || big_any_below(S, pos);", "sticky = 0;"),
+    "ratio_25_bit_significand": ("p_lsb = a - 23 > -149 ? a - 23 : -149;",
+                                 "p_lsb = a - 24 > -149 ? a - 24 : -149;"),
+    "ratio_flush_subnormal": ("if (a <= -151) return 0.0f;", "if (a <= -127) return 0.0f;"),
     # dequant
     "dequant_drops_gamma": ("float eg = eta[m] * gamma;", "float eg = eta[m];"),
     "dequant_divides_by_128": ("float s = eg / OR_QB;", "float s = eg / 128.0f;"),
