@@ -106,6 +106,34 @@ def bench_prefill(torch, L, S, reps: int):
     return out
 
 
+def bench_rmsnorm(torch, L, S, reps: int):
+    """The fused RMSNorm + absmax quantizer next to the plain quantizer on the
+    prefill activations (M = 2048) and decode rows; HBM bytes = 4MK read +
+    MK written + 4M scales."""
+    out = []
+    cases = [(f"prefill x K={S.C3_SHAPES[w][0]}", S.c3_inputs(w)[1]) for w in (0, 1)]
+    cases += [(f"decode x M={M} K={K}", S.random_x(9000 + M + K, M, K)) for M, K in ((16, 8192), (16, 28672))]
+    for name, x in cases:
+        M, K = x.shape
+        xd = torch.from_numpy(x).cuda()
+        xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        eta = torch.empty(M, dtype=torch.float32, device="cuda")
+        rms = lambda: L.bitlinear_rmsnorm_quantize_act(xd, M, K, xq, eta)
+        plain = lambda: L.bitlinear_quantize_act(xd, M, K, xq, eta)
+        for _ in range(3):
+            rms()
+            plain()
+        ms_r = time_events(torch, rms, reps)
+        ms_q = time_events(torch, plain, reps)
+        nbytes = 5 * M * K + 4 * M
+        out.append({"rows": f"{name} (M={M})", "rmsnorm_quant_us": round(ms_r * 1e3, 2),
+                    "rmsnorm_quant_gbs": round(nbytes / (ms_r * 1e-3) / 1e9, 1),
+                    "quant_us": round(ms_q * 1e3, 2),
+                    "quant_gbs": round(nbytes / (ms_q * 1e-3) / 1e9, 1)})
+        del xd, xq, eta
+    return out
+
+
 def cpu_baseline(sw, S, budget_s: float = 12.0):
     """The oracle (unchanged) on a bounded sample of the sweep: layer 0's seven
     projections at M = 1 (quantize + contract + dequant), run repeatedly until
@@ -294,6 +322,12 @@ def main() -> int:
         extra["prefill"] = bench_prefill(torch, L, S, max(10, args.steps))
         for r in extra["prefill"]:
             log(f"prefill {r['gemm']}: {r['us']} us, {r['tops']} TOP/s ({r['frac']:.1%})")
+
+    if not args.no_prefill:
+        extra["rmsnorm_quant"] = bench_rmsnorm(torch, L, S, max(10, args.steps))
+        for r in extra["rmsnorm_quant"]:
+            log(f"rmsnorm+quant {r['rows']}: {r['rmsnorm_quant_us']} us "
+                f"({r['rmsnorm_quant_gbs']} GB/s); quant alone {r['quant_us']} us")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -102,6 +102,25 @@ int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, flo
                            int32_t* xsum, void* stream);
 
 /*
+ * RMSNorm without affine parameters, then the per-token absmax INT8
+ * quantization of the normalized rows, in one pass over x.
+ * [P1] pipeline box 1 ("RMSNorm") and step 1 of BitLinear158.forward in
+ * "Production PyTorch Implementation: BitLinear b1.58 Layer" (norm =
+ * rsqrt(mean(x^2) + 1e-6), x_norm = x * norm); [P1] "2. Absmax Dynamic
+ * Activation Quantization" (normalization without affine parameters before
+ * the quantizer); [P2] "2. Absmax Activation Quantization".
+ *   ms[m]   = the exact mean over k of x[m][k]^2, rounded once to float32
+ *   norm    = 1 / sqrt(ms[m] + 1e-6)  (IEEE float32 add, square root, division)
+ *   x_norm  = x * norm (float32); eta, xq, xsum as bitlinear_quantize_act
+ *             computes them from x_norm
+ *   x    [M][K] float32 (in)        xq   [M][K] int8 (out)
+ *   eta  [M] float32 (out)          xsum [M] int32 (out, may be NULL)
+ *   ms   [M] float32 (out, may be NULL)
+ */
+int bitlinear_rmsnorm_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta,
+                                   int32_t* xsum, float* ms, void* stream);
+
+/*
  * Absmean ternary weight quantization and packing.
  * [P1] "1. Absmean Weight Quantization" and the WeightQuantizerSTE listing;
  * [P2] "1. Absmean Weight Quantization"; [P4] "The Weight Quantization
@@ -167,6 +186,15 @@ int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed,
 int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, int64_t M,
                           int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
                           void* stream);
+
+/*
+ * Fused forward with the RMSNorm prologue: normalize and quantize (into the
+ * workspace), contract, dequantize.  Same arguments and workspace as
+ * bitlinear_forward_f32.  [P1] BitLinear158.forward steps 1, 2, 4 and 5.
+ */
+int bitlinear_forward_rmsnorm_f32(const float* x, const uint8_t* packed, float gamma, int64_t M,
+                                  int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /*
  * Grouped forward: many independent BitLinear problems of the same token

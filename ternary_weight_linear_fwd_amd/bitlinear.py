@@ -62,11 +62,14 @@ _SIGS = {
     "bitlinear_packed_bytes": ([_I64, _I64], _SZ),
     "bitlinear_workspace_bytes": ([_I64, _I64, _I64], _SZ),
     "bitlinear_quantize_act": ([_P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
+    "bitlinear_rmsnorm_quantize_act": ([_P, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "bitlinear_pack_weights": ([_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "bitlinear_pack_ternary": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "bitlinear_unpack_weights": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "bitlinear_forward": ([_P, _P, _P, _F, _I64, _I64, _I64, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "bitlinear_forward_f32": ([_P, _P, _F, _I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
+    "bitlinear_forward_rmsnorm_f32": ([_P, _P, _F, _I64, _I64, _I64, _P, _P, _SZ, _P],
+                                      ctypes.c_int),
     "bitlinear_grouped_table_bytes": ([ctypes.POINTER(BitLinearProblem), _I32, _I64], _SZ),
     "bitlinear_grouped_plan_init": ([ctypes.POINTER(BitLinearProblem), _I32, _I64, _P, _SZ,
                                      ctypes.POINTER(BitLinearGroupedPlan), _P], ctypes.c_int),
@@ -170,6 +173,20 @@ def bitlinear_forward_f32(x, packed, gamma: float, M: int, N: int, K: int, y, ws
     _check(_lib.bitlinear_forward_f32(_ptr(x), _ptr(packed), float(gamma), M, N, K, _ptr(y),
                                       _ptr(ws), ws_bytes, _stream(stream)),
            "bitlinear_forward_f32")
+
+
+def bitlinear_rmsnorm_quantize_act(x, M: int, K: int, xq, eta, xsum=None, ms=None,
+                                   stream=None) -> None:
+    _check(_lib.bitlinear_rmsnorm_quantize_act(_ptr(x), M, K, _ptr(xq), _ptr(eta), _ptr(xsum),
+                                               _ptr(ms), _stream(stream)),
+           "bitlinear_rmsnorm_quantize_act")
+
+
+def bitlinear_forward_rmsnorm_f32(x, packed, gamma: float, M: int, N: int, K: int, y, ws,
+                                  ws_bytes: int, stream=None) -> None:
+    _check(_lib.bitlinear_forward_rmsnorm_f32(_ptr(x), _ptr(packed), float(gamma), M, N, K,
+                                              _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+           "bitlinear_forward_rmsnorm_f32")
 
 
 def make_problems(specs: Sequence[dict]):

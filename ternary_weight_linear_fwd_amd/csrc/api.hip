@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "kernels.hpp"
+#include "rmsnorm.hpp"
 
 using namespace bl;
 
@@ -158,7 +159,7 @@ const char* bitlinear_status_string(int status) {
     }
 }
 
-int bitlinear_abi_version(void) { return 10000; }
+int bitlinear_abi_version(void) { return 10100; }
 
 const char* bitlinear_last_error(void) { return g_last_error; }
 
@@ -183,6 +184,16 @@ int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, flo
     if (!aligned(x, 16) || !aligned(xq, 16)) return BITLINEAR_EINVAL;
     clear_hip_error();
     return launch_quantize(x, M, K, xq, eta, xsum, (hipStream_t)stream);
+}
+
+int bitlinear_rmsnorm_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta,
+                                   int32_t* xsum, float* ms, void* stream) {
+    int rc = check_sizes(M, 1, K);
+    if (rc) return rc;
+    if (!x || !xq || !eta) return BITLINEAR_EINVAL;
+    if (!aligned(x, 16) || !aligned(xq, 16)) return BITLINEAR_EINVAL;
+    clear_hip_error();
+    return launch_rmsnorm_quantize(x, M, K, xq, eta, xsum, ms, (hipStream_t)stream);
 }
 
 int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma,
@@ -237,8 +248,9 @@ int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed,
     return run_forward(xq, eta, packed, gamma, M, N, K, y, y_int, ws, (hipStream_t)stream);
 }
 
-int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, int64_t M, int64_t N,
-                          int64_t K, float* y, void* ws, size_t ws_bytes, void* stream) {
+static int forward_f32_common(const float* x, const uint8_t* packed, float gamma, int64_t M,
+                              int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
+                              void* stream, bool rmsnorm) {
     int rc = check_sizes(M, N, K);
     if (rc) return rc;
     if (!x || !packed || !y) return BITLINEAR_EINVAL;
@@ -252,9 +264,21 @@ int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, in
     void* rest = (char*)ws + xq_bytes + eta_bytes;
     hipStream_t s = (hipStream_t)stream;
     clear_hip_error();
-    rc = launch_quantize(x, M, K, xq, eta, nullptr, s);
+    rc = rmsnorm ? launch_rmsnorm_quantize(x, M, K, xq, eta, nullptr, nullptr, s)
+                 : launch_quantize(x, M, K, xq, eta, nullptr, s);
     if (rc) return rc;
     return run_forward(xq, eta, packed, gamma, M, N, K, y, nullptr, rest, s);
+}
+
+int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, int64_t M, int64_t N,
+                          int64_t K, float* y, void* ws, size_t ws_bytes, void* stream) {
+    return forward_f32_common(x, packed, gamma, M, N, K, y, ws, ws_bytes, stream, false);
+}
+
+int bitlinear_forward_rmsnorm_f32(const float* x, const uint8_t* packed, float gamma, int64_t M,
+                                  int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    return forward_f32_common(x, packed, gamma, M, N, K, y, ws, ws_bytes, stream, true);
 }
 
 size_t bitlinear_grouped_table_bytes(const bitlinear_problem* problems_host, int32_t count,

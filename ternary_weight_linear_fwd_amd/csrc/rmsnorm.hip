@@ -1,0 +1,303 @@
+// rmsnorm.hip -- RMSNorm without affine parameters fused with the per-token
+// absmax INT8 quantizer, one read of x.
+//
+// [P1] pipeline box 1 ("RMSNorm") and step 1 of BitLinear158.forward in
+// "Production PyTorch Implementation: BitLinear b1.58 Layer": norm =
+// rsqrt(mean(x^2) + 1e-6), x_norm = x * norm, then the absmax quantizer of
+// step 2 on x_norm; [P1] "2. Absmax Dynamic Activation Quantization" (the
+// normalization has no learnable affine parameters); [P2] "2. Absmax
+// Activation Quantization" (normalization precedes quantization).
+//
+// Float semantics, fixed so that the result is a function of x alone:
+//   ms     = the exact mean of the squares, rounded once to float32 (RNE)
+//   norm   = 1 / sqrt(ms + 1e-6): an IEEE add, square root and division
+//            (the square root corrected to the correctly rounded one)
+//   x_norm = x * norm;   eta = max(max_k |x_norm|, 1e-5);   xq as usual.
+// Rounding is monotone, so max_k |x_norm| = fl(max_k |x| * norm): eta needs
+// only the row's max |x|, and x_norm is formed on the fly while quantizing.
+//
+// The exact mean, cheaply.  Every float32 square is exact in float64, and a
+// float64 sum of K non-negative terms in any order is within (K-1) * 2^-53 of
+// the true sum (relative), the division by K adds one more rounding.  Each row
+// therefore forms S in float64 with the same butterfly reductions as max |x|;
+// when the interval S/K * (1 +- (K+4) 2^-52) holds no float32 rounding
+// boundary, the float32 nearest to S/K is the correctly rounded exact mean.
+// Otherwise (exact ties, results within ~2^-40 of a boundary, very long rows)
+// the row takes the exact path: every square sig^2 * 2^(2t-298) (|x| = sig *
+// 2^(t-149)) is added, split in two 24-bit halves, to a per-exponent 64-bit
+// LDS bin, and one thread assembles the 640-bit sum, divides it by K limb by
+// limb and rounds the quotient.
+#include "quant_row.hpp"
+#include "rmsnorm.hpp"
+
+namespace bl {
+
+constexpr float kRmsEps = 1e-6f;
+constexpr int kBins = 254;   // t = 0 .. 253
+constexpr int kLimbs = 21;   // 672 bits >= 2 * 253 + 24 + 55
+
+// Correctly rounded float32 square root.  The device square root may be off
+// by one unit; the candidate is moved to the neighbour whose rounding interval
+// holds sqrt(t), decided exactly: a midpoint of two adjacent floats has at most
+// 25 significant bits, so its square is exact in float64 (no ties can occur).
+__device__ inline float sqrt_rn(float t) {
+    float s = __fsqrt_rn(t);
+    if (!(t > 0.0f) || isinf(t)) return s;
+    const double td = (double)t;
+    for (int it = 0; it < 2; ++it) {
+        const float up = nextafterf(s, INFINITY), dn = nextafterf(s, 0.0f);
+        const double mu = 0.5 * ((double)s + (double)up), md = 0.5 * ((double)s + (double)dn);
+        if (td > mu * mu) s = up;
+        else if (td < md * md) s = dn;
+        else break;
+    }
+    return s;
+}
+
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// The rounding interval of a non-negative float32 r: the exact values that
+// round (to nearest, ties to even) to r lie within [lo, hi]; ties sit on the
+// bounds, which the caller treats as ambiguous.
+__device__ inline void f32_rounding_interval(float r, double& lo, double& hi) {
+    const double over = 0x1p128 - 0x1p103;   // midpoint of FLT_MAX and 2^128
+    const double dr = (double)r;
+    if (isinf(r)) {
+        lo = over;
+        hi = INFINITY;
+        return;
+    }
+    lo = r == 0.0f ? -1.0 : 0.5 * (dr + (double)nextafterf(r, 0.0f));
+    hi = r == 3.40282347e38f ? over : 0.5 * (dr + (double)nextafterf(r, INFINITY));
+}
+
+// big += v * 2^s  (v < 2^56, s + 88 <= 32 * kLimbs)
+__device__ inline void big_add(uint32_t* big, uint64_t v, int s) {
+    const int limb = s >> 5, bit = s & 31;
+    const uint64_t a = (v & 0xffffffffull) << bit;   // bits [0, 63)
+    const uint64_t b = (v >> 32) << bit;             // bits [32, 32 + 55)
+    uint64_t acc = (uint64_t)big[limb] + (a & 0xffffffffull);
+    big[limb] = (uint32_t)acc;
+    acc = (acc >> 32) + (a >> 32) + (b & 0xffffffffull) + big[limb + 1];
+    big[limb + 1] = (uint32_t)acc;
+    acc = (acc >> 32) + (b >> 32) + big[limb + 2];
+    big[limb + 2] = (uint32_t)acc;
+    acc >>= 32;
+    for (int i = limb + 3; acc && i < kLimbs; ++i) {
+        acc += big[i];
+        big[i] = (uint32_t)acc;
+        acc >>= 32;
+    }
+}
+
+__device__ inline int big_getbit(const uint32_t* big, int p) { return (big[p >> 5] >> (p & 31)) & 1; }
+
+// The float32 nearest to (sum over bins) / K, by exact integer arithmetic (one
+// thread).  bins[t] = {sum of hi halves, sum of lo halves}: the squares in bin t
+// add up to (hi * 2^24 + lo) * 2^(2t - 298).
+__device__ float exact_mean_f32(const unsigned long long (*bins)[2], uint32_t* big, uint64_t K) {
+    for (int i = 0; i < kLimbs; ++i) big[i] = 0;
+    for (int t = 0; t < kBins; ++t) {
+        const uint64_t hi = bins[t][0], lo = bins[t][1];
+        if (lo) big_add(big, lo, 2 * t);
+        if (hi) big_add(big, hi, 2 * t + 24);
+    }
+    // Q = floor(S / K) limb by limb (rem < K < 2^31), in units of 2^-298.
+    uint64_t rem = 0;
+    for (int i = kLimbs - 1; i >= 0; --i) {
+        const uint64_t cur = (rem << 32) | big[i];
+        big[i] = (uint32_t)(cur / K);
+        rem = cur % K;
+    }
+    int L = -1;   // top set bit of Q
+    for (int i = kLimbs - 1; i >= 0 && L < 0; --i)
+        if (big[i]) L = 32 * i + 31 - __builtin_clz(big[i]);
+    if (L < 0) return 0.0f;                       // S / K < 2^-298
+    const int a_lead = L - 298;                   // the leading bit weighs 2^a_lead
+    int p_lsb = a_lead - 23 > -149 ? a_lead - 23 : -149;
+    const int b_lsb = p_lsb + 298;                // >= 149: rounding bits are integer bits of Q
+    uint32_t sig = 0;
+    for (int p = L; p >= b_lsb; --p) sig = (sig << 1) | (uint32_t)big_getbit(big, p);
+    const int rb = big_getbit(big, b_lsb - 1);
+    bool sticky = rem != 0;
+    const int below = b_lsb - 1;                  // bits [0, below) are sticky
+    for (int i = 0; i < (below >> 5) && !sticky; ++i) sticky = big[i] != 0;
+    if (!sticky && (below & 31)) sticky = (big[below >> 5] & ((1u << (below & 31)) - 1u)) != 0;
+    if (rb && (sticky || (sig & 1u))) ++sig;      // round half to even
+    if (sig == (1u << 24)) {
+        sig >>= 1;
+        ++p_lsb;
+    }
+    if (p_lsb + 23 > 127) return INFINITY;
+    if (sig < (1u << 23)) return __uint_as_float(sig);   // subnormal: p_lsb == -149
+    return __uint_as_float(((uint32_t)(p_lsb + 23 + 127) << 23) | (sig & 0x7fffffu));
+}
+
+__device__ inline void bin_square(unsigned long long (*bins)[2], float v) {
+    const uint32_t bits = __float_as_uint(v) & 0x7fffffffu;
+    const uint32_t e = bits >> 23, f = bits & 0x7fffffu;
+    const uint64_t sig = e ? (f | 0x800000u) : f;
+    if (!sig) return;
+    const int t = e ? ((int)e - 1 < kBins ? (int)e - 1 : kBins - 1) : 0;   // Inf/NaN stay in range
+    const uint64_t sq = sig * sig;
+    atomicAdd(&bins[t][0], (unsigned long long)(sq >> 24));
+    atomicAdd(&bins[t][1], (unsigned long long)(sq & 0xffffffull));
+}
+
+__device__ inline void bin_square4(unsigned long long (*bins)[2], float4 v) {
+    bin_square(bins, v.x);
+    bin_square(bins, v.y);
+    bin_square(bins, v.z);
+    bin_square(bins, v.w);
+}
+
+__device__ inline double sq_sum4(float4 v) {
+    const double a = v.x, b = v.y, c = v.z, d = v.w;
+    return a * a + b * b + c * c + d * d;   // each square exact; the sum rounds
+}
+
+__device__ inline float4 mul4(float4 v, float s) {
+    return make_float4(__fmul_rn(v.x, s), __fmul_rn(v.y, s), __fmul_rn(v.z, s), __fmul_rn(v.w, s));
+}
+
+// One row of K floats (K % 4 == 0, 16-byte aligned).  R float4 per thread stay
+// in registers between the passes; R == 0 re-reads x.
+template <int THREADS, int R>
+__device__ void rmsnorm_quant_row(const float* __restrict__ x, int64_t K, int8_t* __restrict__ xq,
+                                  float* __restrict__ eta_out, int32_t* __restrict__ xsum_out,
+                                  float* __restrict__ ms_out) {
+    constexpr int W = THREADS / 64;
+    __shared__ float redf[W];
+    __shared__ double redd[W];
+    __shared__ int redi[W];
+    __shared__ unsigned long long bins[kBins][2];
+    __shared__ uint32_t big[kLimbs];
+    __shared__ float ms_sh;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    uint32_t* q4 = reinterpret_cast<uint32_t*>(xq);
+    const int64_t n4 = K >> 2;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+
+    float amax = 0.0f;
+    double ss = 0.0;
+    float4 cache[R > 0 ? R : 1];
+    if constexpr (R > 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t i = t + (int64_t)r * THREADS;
+            cache[r] = i < n4 ? ldnt_f4(&x4[i]) : make_float4(0, 0, 0, 0);
+            const float4 v = cache[r];
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            ss += sq_sum4(v);
+        }
+    } else {
+        for (int64_t i = t; i < n4; i += THREADS) {
+            const float4 v = x4[i];
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            ss += sq_sum4(v);
+        }
+    }
+    amax = wave_max(amax);
+    ss = wave_sum_f64(ss);
+    if (lane == 0) {
+        redf[wave] = amax;
+        redd[wave] = ss;
+    }
+    __syncthreads();
+    amax = redf[0];
+    ss = redd[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+        amax = fmaxf(amax, redf[w]);
+        ss += redd[w];
+    }
+
+    // Fast path: the float64 estimate decides the rounding unless it lies near
+    // a boundary.  Every thread evaluates the same test on the same values.
+    const double Kd = (double)K;
+    const double q = ss / Kd;
+    float ms = (float)q;
+    const double d = (Kd + 4.0) * 0x1p-52;
+    double lo, hi;
+    f32_rounding_interval(ms, lo, hi);
+    const bool ambiguous = !(q - q * d > lo && q + q * d < hi);
+    if (ambiguous) {   // uniform: the exact path
+        for (int i = t; i < 2 * kBins; i += THREADS) (&bins[0][0])[i] = 0ull;
+        __syncthreads();
+        if constexpr (R > 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (t + (int64_t)r * THREADS < n4) bin_square4(bins, cache[r]);
+        } else {
+            for (int64_t i = t; i < n4; i += THREADS) bin_square4(bins, x4[i]);
+        }
+        __syncthreads();
+        if (t == 0) ms_sh = exact_mean_f32(bins, big, (uint64_t)K);
+        __syncthreads();
+        ms = ms_sh;
+    }
+
+    const float norm = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, kRmsEps)));
+    const float an = __fmul_rn(amax, norm);
+    const float eta = an < kScaleFloor ? kScaleFloor : an;
+
+    int sum = 0;
+    if constexpr (R > 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t i = t + (int64_t)r * THREADS;
+            if (i < n4) q4[i] = quant4(mul4(cache[r], norm), eta, sum);
+        }
+    } else {
+        for (int64_t i = t; i < n4; i += THREADS) q4[i] = quant4(mul4(x4[i], norm), eta, sum);
+    }
+    if (t == 0) {
+        eta_out[0] = eta;
+        if (ms_out) ms_out[0] = ms;
+    }
+    if (xsum_out) {
+        sum = wave_sum(sum);
+        if (lane == 0) redi[wave] = sum;
+        __syncthreads();
+        if (t == 0) {
+            int s = 0;
+#pragma unroll
+            for (int w = 0; w < W; ++w) s += redi[w];
+            xsum_out[0] = s;
+        }
+    }
+}
+
+template <int THREADS, int R>
+__global__ __launch_bounds__(THREADS) void rmsnorm_quant_rows_kernel(
+    const float* __restrict__ x, int64_t K, int8_t* __restrict__ xq, float* __restrict__ eta,
+    int32_t* __restrict__ xsum, float* __restrict__ ms) {
+    const int64_t m = blockIdx.x;
+    rmsnorm_quant_row<THREADS, R>(x + m * K, K, xq + m * K, eta + m, xsum ? xsum + m : nullptr,
+                                  ms ? ms + m : nullptr);
+}
+
+int launch_rmsnorm_quantize(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta,
+                            int32_t* xsum, float* ms, hipStream_t stream) {
+    if (M == 0) return BITLINEAR_OK;
+    const int64_t n4 = K / 4;
+    dim3 grid((unsigned)M);
+#define BL_RL(T, R) \
+    hipLaunchKernelGGL((rmsnorm_quant_rows_kernel<T, R>), grid, dim3(T), 0, stream, x, K, xq, eta, xsum, ms)
+    if (n4 <= 256) BL_RL(256, 1);
+    else if (n4 <= 512) BL_RL(256, 2);
+    else if (n4 <= 1024) BL_RL(256, 4);
+    else if (n4 <= 2048) BL_RL(256, 8);
+    else if (n4 <= 4096) BL_RL(512, 8);
+    else if (n4 <= 8192) BL_RL(1024, 8);
+    else BL_RL(1024, 0);
+#undef BL_RL
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
+
+}  // namespace bl

@@ -55,7 +55,7 @@ def test_status_strings():
     for code in (-1, -2, -3, -4, -5):
         assert bl.bitlinear_status_string(code).startswith("BITLINEAR_E")
     assert bl.bitlinear_status_string(7) == "BITLINEAR_UNKNOWN"
-    assert bl.bitlinear_abi_version() == 10000
+    assert bl.bitlinear_abi_version() == 10100
 
 
 def test_packed_bytes():
@@ -104,6 +104,12 @@ def test_validation_before_any_device_work():
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, FAKE + 8, 1 << 20, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_rmsnorm_quantize_act", None, 1, 64, FAKE, FAKE, None, None, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_rmsnorm_quantize_act", FAKE, 1, 64, FAKE, None, None, None, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_rmsnorm_quantize_act", FAKE, 1, 40, FAKE, FAKE, None, None, None) == L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_rmsnorm_quantize_act", FAKE, 1, 64, FAKE + 2, FAKE, None, None, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward_rmsnorm_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_forward_rmsnorm_f32", FAKE, None, ctypes.c_float(1.0), 4, 64, 64, FAKE, FAKE, 1 << 20, None) == L.BITLINEAR_EINVAL
 
 
 def test_grouped_planner_validation():

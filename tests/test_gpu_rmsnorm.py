@@ -1,0 +1,105 @@
+"""GPU parity: RMSNorm without affine parameters fused with the absmax INT8
+quantizer, bit-exact against the oracle (the mean of the squares, eta, xq and
+the row sums), and the fused forward with that prologue."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import assert_y_close, bl, empty, pack_weights, say, to_dev, torch_cuda
+from ternary_weight_linear_fwd_amd import synthetic as S
+
+pytestmark = pytest.mark.gpu
+
+
+def rmsnorm_quantize(x: np.ndarray):
+    torch = torch_cuda()
+    M, K = x.shape
+    xd = to_dev(x.astype(np.float32))
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    eta = torch.empty(M, dtype=torch.float32, device="cuda")
+    xsum = torch.empty(M, dtype=torch.int32, device="cuda")
+    ms = torch.empty(M, dtype=torch.float32, device="cuda")
+    bl().bitlinear_rmsnorm_quantize_act(xd, M, K, xq, eta, xsum, ms)
+    torch.cuda.synchronize()
+    return xq.cpu().numpy(), eta.cpu().numpy(), xsum.cpu().numpy(), ms.cpu().numpy()
+
+
+def check(x):
+    say(f"rmsnorm_quantize M={x.shape[0]} K={x.shape[1]}")
+    xq, eta, xsum, ms = rmsnorm_quantize(x)
+    rq, reta, rms, _ = oracle.rmsnorm_quantize_act(x)
+    assert np.array_equal(ms.view(np.uint32), rms.view(np.uint32)), (ms[:4], rms[:4])
+    assert np.array_equal(eta.view(np.uint32), reta.view(np.uint32))
+    assert np.array_equal(xq, rq), np.argwhere(xq != rq)[:5]
+    assert np.array_equal(xsum, rq.astype(np.int64).sum(axis=1))
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (1, 48), (3, 80), (2, 1024), (5, 1040), (1, 2048),
+                                 (7, 4096), (2, 8192), (3, 8208), (1, 16384), (2, 28672),
+                                 (1, 32784)])
+def test_shapes(M, K):
+    check(S.random_x(M * 100019 + K, M, K))
+
+
+def test_config_shapes():
+    for M in (1, 8):
+        check(S.c2_x(S.C2_PROJS[0], M))
+        check(S.c2_x(S.C2_PROJS[6], M))
+    for p in (0, 1):
+        _, x = S.c3_inputs(p)
+        check(x)
+    for M in (1, 16):
+        check(S.c4_x(0, S.C4_PROJS[0], M))
+        check(S.c4_x(0, S.C4_PROJS[6], M))
+    for M in (32, 128):
+        check(S.c5_x(S.C5_PROJS[0], M))
+        check(S.c5_x(S.C5_PROJS[6], M))
+
+
+def test_exact_path_rows():
+    # Rows whose float64 estimate sits on a float32 rounding boundary take the
+    # exact path: a large element and many ones (ties both ways and an exact
+    # value), constant power-of-two rows, zeros, subnormal means, overflow.
+    rows = []
+    for ones in (1023, 1022, 1021):
+        rows.append([4096.0] + [1.0] * ones + [0.0] * (1023 - ones))
+    rows.append([16.0] * 1024)
+    rows.append([-2.0 ** 40] * 512 + [2.0 ** 40] * 512)
+    rows.append([0.0] * 1024)
+    rows.append([2.0 ** -70] * 1024)
+    rows.append([3e-41] * 7 + [0.0] * 1017)
+    rows.append([1e20] * 1024)
+    check(np.array(rows, np.float32))
+
+
+def test_wide_range_rows():
+    rng = np.random.default_rng(77)
+    for K in (16, 64, 1040, 8192):
+        mant = rng.uniform(1, 2, (4, K)) * np.where(rng.random((4, K)) < 0.5, -1, 1)
+        expo = rng.integers(-60, 60, (4, K))
+        x = (mant * np.exp2(expo)).astype(np.float32)
+        x[rng.random((4, K)) < 0.1] = 0
+        check(x)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 200, 208), (4, 333, 1040), (16, 256, 1024),
+                                   (40, 130, 2048), (130, 300, 1040)])
+def test_fused_forward(M, N, K):
+    say(f"forward_rmsnorm_f32 M={M} N={N} K={K}")
+    torch = torch_cuda()
+    L = bl()
+    x = S.random_x(5000 + M, M, K, "t3")
+    W = S.random_latent(6000 + N, N, K)
+    packed, g = pack_weights(W)
+    Wt, g_ref = oracle.quantize_weights(W)
+    assert g == g_ref
+    rq, reta, _, _ = oracle.rmsnorm_quantize_act(x)
+    y_ref, _ = oracle.forward_q(rq, reta, Wt, g_ref)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws_bytes = L.bitlinear_workspace_bytes(M, N, K)
+    ws = empty(ws_bytes)
+    L.bitlinear_forward_rmsnorm_f32(to_dev(x), packed, float(g), M, N, K, y, ws, ws_bytes)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    assert_y_close(y, y_ref)
+    assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
