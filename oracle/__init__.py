@@ -54,6 +54,10 @@ class Oracle:
                                      ctypes.c_int]
         L.oracle_rmsnorm.argtypes = [P, I64, I64, P, P, P]
         L.oracle_rmsnorm_quantize_act.argtypes = [P, I64, I64, P, P, P, P]
+        L.oracle_pack3.argtypes = [P, I64, I64, P]
+        L.oracle_unpack3.argtypes = [P, I64, I64, P]
+        L.oracle_packed3_row_bytes.argtypes = [I64]
+        L.oracle_packed3_row_bytes.restype = I64
         L.oracle_packed_row_bytes.argtypes = [I64]
         L.oracle_packed_row_bytes.restype = I64
         self.lib = L
@@ -94,6 +98,22 @@ class Oracle:
         assert packed.shape[1] == (K + 3) // 4
         out = np.empty((N, K), np.int8)
         _check(self.lib.oracle_unpack(_p(packed), N, K, _p(out)), "unpack")
+        return out
+
+    def pack3(self, Wt: np.ndarray) -> np.ndarray:
+        """Compact base-3 format: [N][ceil(K/5)] bytes, five weights per byte."""
+        Wt = _c(Wt, np.int8)
+        N, K = Wt.shape
+        out = np.empty((N, (K + 4) // 5), np.uint8)
+        _check(self.lib.oracle_pack3(_p(Wt), N, K, _p(out)), "pack3")
+        return out
+
+    def unpack3(self, packed: np.ndarray, K: int) -> np.ndarray:
+        packed = _c(packed, np.uint8)
+        N = packed.shape[0]
+        assert packed.shape[1] == (K + 4) // 5
+        out = np.empty((N, K), np.int8)
+        _check(self.lib.oracle_unpack3(_p(packed), N, K, _p(out)), "unpack3")
         return out
 
     def quantize_act(self, x: np.ndarray):
@@ -261,3 +281,11 @@ def rmsnorm(x):
 
 def rmsnorm_quantize_act(x):
     return default().rmsnorm_quantize_act(x)
+
+
+def pack3(Wt):
+    return default().pack3(Wt)
+
+
+def unpack3(packed, K):
+    return default().unpack3(packed, K)

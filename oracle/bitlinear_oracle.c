@@ -253,6 +253,56 @@ int oracle_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wt) {
 }
 
 /*
+ * Compact ternary packing, five weights per byte (3^5 = 243 <= 256, 1.6 bits
+ * per weight).  [P2] "Scaling Laws..." context paragraph on memory bandwidth
+ * (1.58 bits per parameter under compact ternary packing, 2 bits otherwise);
+ * [P3] "Common Misconceptions" (log2(3) ~ 1.58 bits of information per
+ * ternary weight).  The pages name the packing but not its layout; reading
+ * taken: digit d = w + 1 in {0, 1, 2} as in the 2-bit code, byte b of row n
+ * holds k = 5b + j as the base-3 digit of weight 3^j, v = sum_j d_j 3^j in
+ * [0, 242]; a row holds ceil(K/5) bytes and pads with digit 1 (weight 0).
+ */
+int64_t oracle_packed3_row_bytes(int64_t K) { return (K + 4) / 5; }
+
+int oracle_pack3(const int8_t* Wt, int64_t N, int64_t K, uint8_t* packed) {
+    if (!Wt || !packed || N <= 0 || K <= 0) return -1;
+    const int64_t rb = oracle_packed3_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < rb; ++b) {
+            int v = 0, place = 1;
+            for (int j = 0; j < 5; ++j, place *= 3) {
+                int64_t k = 5 * b + j;
+                int digit;
+                if (k >= K) digit = 1;                    /* pad: zero weight */
+                else if (Wt[n * K + k] == 1) digit = 2;
+                else if (Wt[n * K + k] == 0) digit = 1;
+                else if (Wt[n * K + k] == -1) digit = 0;
+                else return -3;                           /* not ternary */
+                v += digit * place;
+            }
+            packed[n * rb + b] = (uint8_t)v;
+        }
+    return 0;
+}
+
+int oracle_unpack3(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wt) {
+    if (!Wt || !packed || N <= 0 || K <= 0) return -1;
+    const int64_t rb = oracle_packed3_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < rb; ++b) {
+            int v = packed[n * rb + b];
+            if (v >= 243) return -4;                      /* never produced */
+            for (int j = 0; j < 5; ++j) {
+                int digit = v % 3;
+                v /= 3;
+                int64_t k = 5 * b + j;
+                if (k < K) Wt[n * K + k] = (int8_t)(digit - 1);
+            }
+        }
+    return 0;
+}
+
+/*
  * Per-token absmax INT8 activation quantization.
  * [P1] "2. Absmax Dynamic Activation Quantization" (Q_b = 127) and the
  * ActivationQuantizerSTE listing (max over the last dim, clamp 1e-5,

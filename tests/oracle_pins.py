@@ -438,6 +438,65 @@ def pin_demo_shapes(O):
     assert np.array_equal(y_int, xq.astype(np.int64) @ Wt.astype(np.int64).T)
 
 
+# ------------------------------------------------------------ base-3 packing
+# Five ternary weights per byte (second page: 1.58 bits per weight under
+# compact ternary packing; third page: log2(3) bits of information).  Reading
+# of the layout: digit w + 1, weight k = 5b + j at 3^j, pad digit 1.
+
+def _base3_value(ws) -> int:
+    """Value of the digits w+1 read as a base-3 numeral, least significant
+    first, by Python's own base conversion."""
+    return int("".join(str(int(w) + 1) for w in reversed(ws)), 3)
+
+
+def pin_pack3_closed_forms(O):
+    W = np.array([[-1] * 5, [1] * 5, [0] * 5, [1, -1, 0, -1, -1]], np.int8)
+    assert O.pack3(W).ravel().tolist() == [0, 242, 121, 11]
+    # a partial last byte pads with zero weights (digit 1)
+    assert O.pack3(np.array([[1, 0, 0, 0, 0, -1, 1]], np.int8)).tolist() == [[122, 123]]
+    assert O.pack3(np.zeros((3, 11), np.int8)).shape == (3, 3)
+
+
+def pin_pack3_exhaustive(O):
+    # every ternary 5-vector: the byte is its base-3 numeral, and the map is a
+    # bijection onto 0..242
+    vecs = np.array(np.meshgrid(*[[-1, 0, 1]] * 5, indexing="ij")).reshape(5, -1).T.astype(np.int8)
+    b = O.pack3(vecs).ravel()
+    assert sorted(b.tolist()) == list(range(243))
+    for v, byte in zip(vecs, b):
+        assert int(byte) == _base3_value(v)
+    assert np.array_equal(O.unpack3(b.reshape(-1, 1), 5), vecs)
+
+
+def pin_pack3_roundtrip_and_density(O):
+    rng = np.random.default_rng(21)
+    for N, K in ((1, 1), (3, 7), (17, 80), (5, 1001)):
+        Wt = rng.integers(-1, 2, (N, K)).astype(np.int8)
+        p3 = O.pack3(Wt)
+        assert p3.shape == (N, -(-K // 5)) and int(p3.max()) <= 242
+        assert np.array_equal(O.unpack3(p3, K), Wt)
+        assert np.array_equal(O.unpack3(p3, K), O.unpack(O.pack(Wt), K))
+        if K % 20 == 0:
+            assert p3.size * 5 == O.pack(Wt).size * 4   # 1.6 against 2 bits per weight
+
+
+def pin_pack3_rejects(O):
+    import oracle as _o
+    for bad in (243, 255):
+        try:
+            O.unpack3(np.array([[bad]], np.uint8), 5)
+        except _o.OracleError:
+            pass
+        else:
+            raise AssertionError(f"byte {bad} accepted")
+    try:
+        O.pack3(np.array([[2, 0, 0, 0, 0]], np.int8))
+    except _o.OracleError:
+        pass
+    else:
+        raise AssertionError("non-ternary weight accepted")
+
+
 # ------------------------------------------------------------------ RMSNorm
 # RMSNorm without affine parameters before the quantizer (first page, step 1 of
 # BitLinear158.forward): norm = 1 / sqrt(mean(x^2) + 1e-6), x_norm = x * norm.

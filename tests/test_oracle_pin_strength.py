@@ -50,6 +50,15 @@ MUTANTS = {
                             "for (int64_t k = 0; k + 1 < j->K; ++k) {\n                if (wr[k]"),
     "contract_transposed_store": ("j->y[m * j->N + n] = (int32_t)acc;",
                                   "j->y[n * j->M + m] = (int32_t)acc;"),
+    # base-3 packing
+    "pack3_digit_order_reversed": ("int v = 0, place = 1;\n            for (int j = 0; j < 5; ++j, place *= 3) {",
+                                   "int v = 0, place = 81;\n            for (int j = 0; j < 5; ++j, place /= 3) {"),
+    "pack3_pad_digit_zero": ("if (k >= K) digit = 1;                    /* pad: zero weight */",
+                             "if (k >= K) digit = 0;                    /* pad: zero weight */"),
+    "pack3_codes_swapped": ("else if (Wt[n * K + k] == 1) digit = 2;", "else if (Wt[n * K + k] == 1) digit = 0;"),
+    "unpack3_accepts_243": ("if (v >= 243) return -4;", "if (v >= 244) return -4;"),
+    "pack3_row_bytes": ("int64_t oracle_packed3_row_bytes(int64_t K) { return (K + 4) / 5; }",
+                        "int64_t oracle_packed3_row_bytes(int64_t K) { return K / 5 + 1; }"),
     # RMSNorm
     "rms_mean_over_k_minus_1": ("const float ms = big_ratio_to_f32(&S, -298, (uint64_t)K);",
                                 "const float ms = big_ratio_to_f32(&S, -298, (uint64_t)(K > 1 ? K - 1 : 1));"),
