@@ -134,6 +134,47 @@ def bench_rmsnorm(torch, L, S, reps: int):
     return out
 
 
+def bench_lut(torch, L, reps: int):
+    """Decode (M = 1) on the largest 70B-shaped projections: the dot4 path on
+    the 2-bit layout next to the lookup-table path on the 2-bit and on the
+    base-3 layout.  Weight GB/s counts each layout's own bytes; weights/s is
+    the format-independent rate."""
+    out = []
+    for K, N in ((8192, 28672), (28672, 8192)):
+        gen = torch.Generator(device="cuda").manual_seed(K + N)
+        Wt = (torch.randint(0, 3, (N, K), generator=gen, device="cuda", dtype=torch.int32) - 1).to(torch.int8)
+        p2 = torch.empty(L.bitlinear_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+        p3 = torch.empty(L.bitlinear_packed3_bytes(N, K), dtype=torch.uint8, device="cuda")
+        L.bitlinear_pack_ternary(Wt, N, K, p2)
+        L.bitlinear_pack_ternary3(Wt, N, K, p3)
+        del Wt
+        xq = torch.randint(-127, 128, (1, K), generator=gen, device="cuda", dtype=torch.int32).to(torch.int8)
+        eta = torch.ones(1, dtype=torch.float32, device="cuda")
+        y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        ws_bytes = max(L.bitlinear_workspace_bytes(1, N, K),
+                       L.bitlinear_lut_workspace_bytes(1, N, K, L.BITLINEAR_FORMAT_2BIT),
+                       L.bitlinear_lut_workspace_bytes(1, N, K, L.BITLINEAR_FORMAT_BASE3))
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        runs = {
+            "dot4_2bit": (lambda: L.bitlinear_forward(xq, eta, p2, 0.02, 1, N, K, y, None, ws, ws_bytes), p2),
+            "lut_2bit": (lambda: L.bitlinear_forward_lut(xq, eta, p2, L.BITLINEAR_FORMAT_2BIT, 0.02, 1, N, K,
+                                                         y, None, ws, ws_bytes), p2),
+            "lut_base3": (lambda: L.bitlinear_forward_lut(xq, eta, p3, L.BITLINEAR_FORMAT_BASE3, 0.02, 1, N,
+                                                          K, y, None, ws, ws_bytes), p3),
+        }
+        row = {"gemv": f"M=1 K={K} N={N}"}
+        for name, (fn, packed) in runs.items():
+            for _ in range(3):
+                fn()
+            ms = time_events(torch, fn, reps)
+            row[name] = {"us": round(ms * 1e3, 2),
+                         "weight_gbs": round(packed.numel() / (ms * 1e-3) / 1e9, 1),
+                         "gweights_per_s": round(N * K / (ms * 1e-3) / 1e9, 1)}
+        out.append(row)
+        del p2, p3, xq, eta, y, ws
+    return out
+
+
 def cpu_baseline(sw, S, budget_s: float = 12.0):
     """The oracle (unchanged) on a bounded sample of the sweep: layer 0's seven
     projections at M = 1 (quantize + contract + dequant), run repeatedly until
@@ -328,6 +369,13 @@ def main() -> int:
         for r in extra["rmsnorm_quant"]:
             log(f"rmsnorm+quant {r['rows']}: {r['rmsnorm_quant_us']} us "
                 f"({r['rmsnorm_quant_gbs']} GB/s); quant alone {r['quant_us']} us")
+
+    if not args.no_prefill:
+        extra["lut_decode"] = bench_lut(torch, L, max(10, args.steps))
+        for r in extra["lut_decode"]:
+            log(f"decode {r['gemv']}: " + "; ".join(
+                f"{k} {v['us']} us {v['weight_gbs']} GB/s {v['gweights_per_s']} Gw/s"
+                for k, v in r.items() if k != "gemv"))
 
     cpu = None
     if not args.no_cpu_baseline:

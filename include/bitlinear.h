@@ -143,8 +143,8 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed
  * with gamma supplied separately).
  *   Wt     [N][K] int8 (in)
  *   packed bitlinear_packed_bytes(N, K) bytes (out)
- *   bad    int32 device scalar (out, may be NULL): set to the number of
- *          entries outside {-1, 0, 1} (those are packed as 0)
+ *   bad    int32 device scalar (out, may be NULL): set (on the stream) to the
+ *          number of entries outside {-1, 0, 1} (those are packed as 0)
  * Asynchronous; a caller that needs BITLINEAR_EBADCODE reads `bad` after
  * synchronizing.
  */
@@ -195,6 +195,49 @@ int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, in
 int bitlinear_forward_rmsnorm_f32(const float* x, const uint8_t* packed, float gamma, int64_t M,
                                   int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/*
+ * Compact base-3 weights, five per byte (3^5 = 243 <= 256: 1.6 bits per
+ * weight against 2).  [P2] the bandwidth paragraph before "Scaling Laws and
+ * Empirical Benchmarks" (1.58 bits per parameter under compact ternary
+ * packing); [P3] "Common Misconceptions" (log2(3) bits per ternary weight).
+ * Canonical byte: v = sum_j (w[5b + j] + 1) * 3^j, pads weight 0.
+ * Base-3 device layout ("base-3 layout"): rows grouped by 64, K cut into
+ * blocks of 80; block (g, b) of 1024 bytes holds 16 bytes per row in order,
+ * byte p of row r being the canonical byte of k = 80b + 5p .. 80b + 5p + 4.
+ * Rows past N and k past K hold weight 0.  Bytes above 242 never occur.
+ *   bitlinear_packed3_bytes(N, K) = ceil(N/64) * ceil(K/80) * 1024.
+ * pack_weights3, pack_ternary3 and unpack_weights3 mirror the 2-bit calls
+ * (same gamma, workspace and `bad` conventions; unpack counts bytes above 242
+ * inside [0, N) x [0, K) and decodes them as zero weights).
+ */
+size_t bitlinear_packed3_bytes(int64_t N, int64_t K);
+int bitlinear_pack_weights3(const float* W, int64_t N, int64_t K, uint8_t* packed3, float* gamma,
+                            float* gamma_host, void* ws, size_t ws_bytes, void* stream);
+int bitlinear_pack_ternary3(const int8_t* Wt, int64_t N, int64_t K, uint8_t* packed3, int32_t* bad,
+                            void* stream);
+int bitlinear_unpack_weights3(const uint8_t* packed3, int64_t N, int64_t K, int8_t* Wt,
+                              int32_t* bad, void* stream);
+
+/*
+ * Lookup-table forward: the same contraction and dequantization as
+ * bitlinear_forward, computed by table lookups instead of additions.
+ * [P3] "What Most People Miss" (precomputed outcomes of small activation
+ * blocks, looked up by the weights); [P5] "Kernel Implementation: The Lookup
+ * Table Approach".  Each weight byte indexes a per-block table of its
+ * activation group's partial sums (5 activations in the base-3 layout, 4 in
+ * the 2-bit layout).  Any M is accepted; the path is built for decode (small
+ * M).  Results are identical to bitlinear_forward's.
+ *   format  BITLINEAR_FORMAT_2BIT (packed: device layout) or
+ *           BITLINEAR_FORMAT_BASE3 (packed: base-3 layout)
+ *   ws      workspace of bitlinear_lut_workspace_bytes(M, N, K, format) bytes
+ */
+#define BITLINEAR_FORMAT_2BIT 0
+#define BITLINEAR_FORMAT_BASE3 1
+size_t bitlinear_lut_workspace_bytes(int64_t M, int64_t N, int64_t K, int format);
+int bitlinear_forward_lut(const int8_t* xq, const float* eta, const uint8_t* packed, int format,
+                          float gamma, int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Grouped forward: many independent BitLinear problems of the same token

@@ -70,6 +70,13 @@ _SIGS = {
     "bitlinear_forward_f32": ([_P, _P, _F, _I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
     "bitlinear_forward_rmsnorm_f32": ([_P, _P, _F, _I64, _I64, _I64, _P, _P, _SZ, _P],
                                       ctypes.c_int),
+    "bitlinear_packed3_bytes": ([_I64, _I64], _SZ),
+    "bitlinear_pack_weights3": ([_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "bitlinear_pack_ternary3": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "bitlinear_unpack_weights3": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "bitlinear_lut_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], _SZ),
+    "bitlinear_forward_lut": ([_P, _P, _P, ctypes.c_int, _F, _I64, _I64, _I64, _P, _P, _P, _SZ,
+                               _P], ctypes.c_int),
     "bitlinear_grouped_table_bytes": ([ctypes.POINTER(BitLinearProblem), _I32, _I64], _SZ),
     "bitlinear_grouped_plan_init": ([ctypes.POINTER(BitLinearProblem), _I32, _I64, _P, _SZ,
                                      ctypes.POINTER(BitLinearGroupedPlan), _P], ctypes.c_int),
@@ -187,6 +194,45 @@ def bitlinear_forward_rmsnorm_f32(x, packed, gamma: float, M: int, N: int, K: in
     _check(_lib.bitlinear_forward_rmsnorm_f32(_ptr(x), _ptr(packed), float(gamma), M, N, K,
                                               _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
            "bitlinear_forward_rmsnorm_f32")
+
+
+BITLINEAR_FORMAT_2BIT = 0
+BITLINEAR_FORMAT_BASE3 = 1
+
+
+def bitlinear_packed3_bytes(N: int, K: int) -> int:
+    return _lib.bitlinear_packed3_bytes(N, K)
+
+
+def bitlinear_pack_weights3(W, N: int, K: int, packed3, gamma=None, gamma_host=None, ws=None,
+                            ws_bytes: int = 0, stream=None) -> None:
+    """gamma_host: a ctypes.c_float to receive gamma (the call then synchronizes), or None."""
+    if isinstance(gamma_host, ctypes.c_float):
+        gamma_host = ctypes.addressof(gamma_host)
+    _check(_lib.bitlinear_pack_weights3(_ptr(W), N, K, _ptr(packed3), _ptr(gamma), gamma_host,
+                                        _ptr(ws), ws_bytes, _stream(stream)),
+           "bitlinear_pack_weights3")
+
+
+def bitlinear_pack_ternary3(Wt, N: int, K: int, packed3, bad=None, stream=None) -> None:
+    _check(_lib.bitlinear_pack_ternary3(_ptr(Wt), N, K, _ptr(packed3), _ptr(bad),
+                                        _stream(stream)), "bitlinear_pack_ternary3")
+
+
+def bitlinear_unpack_weights3(packed3, N: int, K: int, Wt, bad=None, stream=None) -> None:
+    _check(_lib.bitlinear_unpack_weights3(_ptr(packed3), N, K, _ptr(Wt), _ptr(bad),
+                                          _stream(stream)), "bitlinear_unpack_weights3")
+
+
+def bitlinear_lut_workspace_bytes(M: int, N: int, K: int, fmt: int) -> int:
+    return _lib.bitlinear_lut_workspace_bytes(M, N, K, fmt)
+
+
+def bitlinear_forward_lut(xq, eta, packed, fmt: int, gamma: float, M: int, N: int, K: int, y,
+                          y_int=None, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check(_lib.bitlinear_forward_lut(_ptr(xq), _ptr(eta), _ptr(packed), int(fmt), float(gamma),
+                                      M, N, K, _ptr(y), _ptr(y_int), _ptr(ws), ws_bytes,
+                                      _stream(stream)), "bitlinear_forward_lut")
 
 
 def make_problems(specs: Sequence[dict]):

@@ -10,6 +10,8 @@
 #include <vector>
 
 #include "kernels.hpp"
+#include "lut.hpp"
+#include "pack.hpp"
 #include "rmsnorm.hpp"
 
 using namespace bl;
@@ -222,6 +224,7 @@ int bitlinear_pack_ternary(const int8_t* Wt, int64_t N, int64_t K, uint8_t* pack
     if (!Wt || !packed) return BITLINEAR_EINVAL;
     if (!aligned(Wt, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
     clear_hip_error();
+    if (bad && (rc = launch_zero_i32(bad, (hipStream_t)stream))) return rc;
     return launch_pack_ternary(Wt, N, K, packed, bad, (hipStream_t)stream);
 }
 
@@ -232,7 +235,76 @@ int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t
     if (!Wt || !packed) return BITLINEAR_EINVAL;
     if (!aligned(Wt, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
     clear_hip_error();
+    if (bad && (rc = launch_zero_i32(bad, (hipStream_t)stream))) return rc;
     return launch_unpack(packed, N, K, Wt, bad, (hipStream_t)stream);
+}
+
+size_t bitlinear_packed3_bytes(int64_t N, int64_t K) {
+    if (check_sizes(0, N, K) != BITLINEAR_OK) return 0;
+    return packed3_bytes(N, K);
+}
+
+int bitlinear_pack_weights3(const float* W, int64_t N, int64_t K, uint8_t* packed3, float* gamma,
+                            float* gamma_host, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sizes(0, N, K);
+    if (rc) return rc;
+    if (!W || !packed3) return BITLINEAR_EINVAL;
+    if (!aligned(W, 16) || !aligned(packed3, 16)) return BITLINEAR_EINVAL;
+    if (!ws || !aligned(ws, 256) || ws_bytes < gamma_ws_bytes()) return BITLINEAR_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    clear_hip_error();
+    rc = launch_pack_weights3(W, N, K, packed3, gamma, ws, s);
+    if (rc) return rc;
+    if (gamma_host) {
+        const float* g = (const float*)((const char*)ws + kGammaBins * sizeof(unsigned long long));
+        BL_HIP_CHECK(hipMemcpyAsync(gamma_host, g, sizeof(float), hipMemcpyDeviceToHost, s));
+        BL_HIP_CHECK(hipStreamSynchronize(s));
+    }
+    return BITLINEAR_OK;
+}
+
+int bitlinear_pack_ternary3(const int8_t* Wt, int64_t N, int64_t K, uint8_t* packed3, int32_t* bad,
+                            void* stream) {
+    int rc = check_sizes(0, N, K);
+    if (rc) return rc;
+    if (!Wt || !packed3) return BITLINEAR_EINVAL;
+    if (!aligned(packed3, 16)) return BITLINEAR_EINVAL;
+    clear_hip_error();
+    if (bad && (rc = launch_zero_i32(bad, (hipStream_t)stream))) return rc;
+    return launch_pack_ternary3(Wt, N, K, packed3, bad, (hipStream_t)stream);
+}
+
+int bitlinear_unpack_weights3(const uint8_t* packed3, int64_t N, int64_t K, int8_t* Wt,
+                              int32_t* bad, void* stream) {
+    int rc = check_sizes(0, N, K);
+    if (rc) return rc;
+    if (!Wt || !packed3) return BITLINEAR_EINVAL;
+    if (!aligned(packed3, 16)) return BITLINEAR_EINVAL;
+    clear_hip_error();
+    if (bad && (rc = launch_zero_i32(bad, (hipStream_t)stream))) return rc;
+    return launch_unpack3(packed3, N, K, Wt, bad, (hipStream_t)stream);
+}
+
+size_t bitlinear_lut_workspace_bytes(int64_t M, int64_t N, int64_t K, int format) {
+    if (check_sizes(M, N, K) != BITLINEAR_OK) return 0;
+    if (format != kFormat2Bit && format != kFormatBase3) return 0;
+    return align256(lut_ws_bytes(M, N, K, format));
+}
+
+int bitlinear_forward_lut(const int8_t* xq, const float* eta, const uint8_t* packed, int format,
+                          float gamma, int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int,
+                          void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sizes(M, N, K);
+    if (rc) return rc;
+    if (format != kFormat2Bit && format != kFormatBase3) return BITLINEAR_EINVAL;
+    if (!xq || !eta || !packed || !y) return BITLINEAR_EINVAL;
+    if (!aligned(packed, 16)) return BITLINEAR_EINVAL;
+    const size_t need = lut_ws_bytes(M, N, K, format);
+    if (need && (!ws || !aligned(ws, 256) || ws_bytes < need)) return BITLINEAR_EWORKSPACE;
+    if (M == 0) return BITLINEAR_OK;
+    clear_hip_error();
+    Problem p = make_problem(xq, eta, packed, gamma, N, K, y, y_int);
+    return launch_lut(p, M, format, ws, (hipStream_t)stream);
 }
 
 int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,

@@ -15,6 +15,8 @@
 // -1 -> 00, 0 -> 01, +1 -> 10) write the device layout documented in
 // bitlinear.h, one thread per 32-bit word (16 weights of one row).
 #include "kernels.hpp"
+#include "ternary.hpp"
+#include "pack.hpp"
 
 namespace bl {
 
@@ -120,12 +122,6 @@ __global__ void gamma_final_kernel(const unsigned long long* __restrict__ bins, 
     if (gamma_out) gamma_out[0] = g;
 }
 
-// Code of one ternarized weight: t = W / gamma (IEEE), w = clamp(rne(t), -1, 1), code = w + 1.
-__device__ inline uint32_t ternary_code(float w, float gamma) {
-    const float t = __fdiv_rn(w, gamma);
-    const float r = fminf(fmaxf(rintf(t), -1.0f), 1.0f);
-    return (uint32_t)((int)r + 1);
-}
 
 // Place the 16 codes of one word: k_local = 4j + i goes to bits 8i + 2j.
 __device__ inline uint32_t place16(const uint32_t c[16]) {
@@ -222,8 +218,8 @@ static int64_t layout_words(int64_t N, int64_t K) {
     return ceil_div(N, 64) * ceil_div(K, 64) * 256;
 }
 
-int launch_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma_dev,
-                        void* ws, hipStream_t stream) {
+int launch_gamma(const float* W, int64_t N, int64_t K, float* gamma_dev, void* ws,
+                 hipStream_t stream) {
     unsigned long long* bins = (unsigned long long*)ws;
     float* gamma_ws = (float*)((char*)ws + kGammaBins * sizeof(unsigned long long));
     int rc = launch_fill_zero(bins, kGammaBins * sizeof(unsigned long long), stream);
@@ -236,10 +232,25 @@ int launch_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, f
     hipLaunchKernelGGL(gamma_final_kernel, dim3(1), dim3(64), 0, stream, bins,
                        (uint64_t)N * (uint64_t)K, gamma_ws, gamma_dev);
     BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
+
+int launch_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, float* gamma_dev,
+                        void* ws, hipStream_t stream) {
+    int rc = launch_gamma(W, N, K, gamma_dev, ws, stream);
+    if (rc) return rc;
+    const float* gamma_ws = (const float*)((const char*)ws + kGammaBins * sizeof(unsigned long long));
     const int64_t nwords = layout_words(N, K);
     hipLaunchKernelGGL(ternarize_pack_kernel, dim3((unsigned)ceil_div(nwords, 256)), dim3(256), 0,
-                       stream, W, N, K, ceil_div(K, 64), (const float*)gamma_ws, (uint32_t*)packed,
-                       nwords);
+                       stream, W, N, K, ceil_div(K, 64), gamma_ws, (uint32_t*)packed, nwords);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
+
+__global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
+
+int launch_zero_i32(int32_t* p, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, stream, p);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
 }

@@ -58,6 +58,16 @@ def test_status_strings():
     assert bl.bitlinear_abi_version() == 10100
 
 
+def test_packed3_and_lut_workspace_bytes():
+    assert bl.bitlinear_packed3_bytes(1, 16) == 1024
+    assert bl.bitlinear_packed3_bytes(64, 80) == 1024
+    assert bl.bitlinear_packed3_bytes(65, 96) == 4 * 1024
+    assert bl.bitlinear_packed3_bytes(8192, 8240) == 8192 * 8240 // 5    # 1.6 bits per weight
+    assert bl.bitlinear_packed3_bytes(0, 16) == 0 and bl.bitlinear_packed3_bytes(8, 20) == 0
+    assert bl.bitlinear_lut_workspace_bytes(1, 64, 64, 2) == 0
+    assert bl.bitlinear_lut_workspace_bytes(1, 8192, 8192, 1) % 256 == 0
+
+
 def test_packed_bytes():
     assert bl.bitlinear_packed_bytes(64, 64) == 1024
     assert bl.bitlinear_packed_bytes(2048, 2048) == 2048 * 2048 // 4
@@ -104,6 +114,14 @@ def test_validation_before_any_device_work():
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, FAKE + 8, 1 << 20, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_pack_ternary3", None, 64, 64, FAKE, None, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_pack_ternary3", FAKE, 64, 20, FAKE, None, None) == L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_unpack_weights3", FAKE, 64, 64, None, None, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_pack_weights3", FAKE, 64, 64, FAKE, None, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_forward_lut", FAKE, FAKE, FAKE, 2, ctypes.c_float(1.0), 1, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward_lut", FAKE, FAKE, FAKE, 1, ctypes.c_float(1.0), 1, 64, 72, FAKE, None, None, 0, None) == L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_forward_lut", FAKE, None, FAKE, 0, ctypes.c_float(1.0), 1, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward_lut", FAKE, FAKE, FAKE, 1, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_rmsnorm_quantize_act", None, 1, 64, FAKE, FAKE, None, None, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_rmsnorm_quantize_act", FAKE, 1, 64, FAKE, None, None, None, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_rmsnorm_quantize_act", FAKE, 1, 40, FAKE, FAKE, None, None, None) == L.BITLINEAR_EUNSUPPORTED
