@@ -45,6 +45,7 @@ class Oracle:
         I64 = ctypes.c_int64
         L.oracle_absmean_gamma.argtypes = [P, I64, I64, P]
         L.oracle_ternarize.argtypes = [P, I64, I64, ctypes.c_float, P]
+        L.oracle_absmedian_gamma.argtypes = [P, I64, I64, P]
         L.oracle_pack.argtypes = [P, I64, I64, P]
         L.oracle_unpack.argtypes = [P, I64, I64, P]
         L.oracle_quantize_act.argtypes = [P, I64, I64, P, P]
@@ -70,6 +71,20 @@ class Oracle:
         out = np.zeros(1, np.float32)
         _check(self.lib.oracle_absmean_gamma(_p(W), N, K, _p(out)), "absmean_gamma")
         return out[0]
+
+    def absmedian_gamma(self, W: np.ndarray) -> np.float32:
+        """Median of |W| (mean of the two middle values for an even count,
+        rounded once to float32), clamped below at 1e-5."""
+        W = _c(W, np.float32)
+        N, K = W.shape
+        out = np.zeros(1, np.float32)
+        _check(self.lib.oracle_absmedian_gamma(_p(W), N, K, _p(out)), "absmedian_gamma")
+        return out[0]
+
+    def quantize_weights_absmedian(self, W: np.ndarray):
+        """(W~, gamma) with the absmedian scale."""
+        g = self.absmedian_gamma(W)
+        return self.ternarize(W, g), g
 
     def ternarize(self, W: np.ndarray, gamma) -> np.ndarray:
         W = _c(W, np.float32)
@@ -289,3 +304,11 @@ def pack3(Wt):
 
 def unpack3(packed, K):
     return default().unpack3(packed, K)
+
+
+def absmedian_gamma(W):
+    return default().absmedian_gamma(W)
+
+
+def quantize_weights_absmedian(W):
+    return default().quantize_weights_absmedian(W)

@@ -194,6 +194,54 @@ int oracle_absmean_gamma(const float* W, int64_t N, int64_t K, float* gamma_out)
 }
 
 /*
+ * Absmedian weight scale: the median of |W| over the whole matrix in place of
+ * the mean.  [P2] the paragraph after "Real-World Production Benchmarks"
+ * (BitNet b1.58 Reloaded: adjusting the quantization baseline to the median,
+ * "Absmedian", rather than the mean).  Readings: the median of the N*K
+ * magnitudes; for an even count it is the mean of the two middle ones, that
+ * mean rounded once to float32 (ties to even); clamped below at 1e-5 like
+ * gamma; ternarization then divides by it exactly as with the absmean scale.
+ * Non-negative float32 magnitudes order like their bit patterns, so the
+ * magnitudes are sorted as unsigned integers.
+ */
+static int or_cmp_u32(const void* a, const void* b) {
+    uint32_t x = *(const uint32_t*)a, y = *(const uint32_t*)b;
+    return x < y ? -1 : x > y;
+}
+
+int oracle_absmedian_gamma(const float* W, int64_t N, int64_t K, float* gamma_out) {
+    if (!W || !gamma_out || N <= 0 || K <= 0) return -1;
+    const uint64_t D = (uint64_t)K * (uint64_t)N;   /* entries */
+    if (D >> 40) return -1;
+    uint32_t* mag = (uint32_t*)malloc(D * sizeof(uint32_t));
+    if (!mag) return -6;
+    for (uint64_t i = 0; i < D; ++i) {
+        uint32_t bits;
+        memcpy(&bits, &W[i], 4);
+        bits &= 0x7fffffffu;
+        if ((bits >> 23) == 255) { free(mag); return -2; }   /* Inf/NaN: outside the contract */
+        mag[i] = bits;
+    }
+    qsort(mag, D, sizeof(uint32_t), or_cmp_u32);
+    const uint32_t lo = mag[(D - 1) / 2], hi = mag[D / 2];   /* equal when D is odd */
+    free(mag);
+    /* (lo + hi) / 2 exactly: both are sig * 2^(t-149); add the two in 2^-149 units */
+    or_big S;
+    big_zero(&S);
+    const uint32_t two[2] = {lo, hi};
+    for (int i = 0; i < 2; ++i) {
+        uint32_t e = two[i] >> 23, f = two[i] & 0x7fffffu;
+        uint32_t sig = e ? (f | 0x800000u) : f;
+        int te = e ? (int)e - 1 : 0;
+        if (sig) big_add_shifted(&S, sig, te);
+    }
+    float g = big_ratio_to_f32(&S, -149, 2);
+    if (!(g >= OR_SCALE_FLOOR)) g = OR_SCALE_FLOOR;
+    *gamma_out = g;
+    return 0;
+}
+
+/*
  * Ternarization: W~ = Clip(Round(W / gamma), -1, +1).
  * [P1] "1. Absmean Weight Quantization" and the WeightQuantizerSTE listing
  * (division, torch.round, clamp); [P2] "1. Absmean Weight Quantization".

@@ -438,6 +438,63 @@ def pin_demo_shapes(O):
     assert np.array_equal(y_int, xq.astype(np.int64) @ Wt.astype(np.int64).T)
 
 
+# ------------------------------------------------------------ absmedian gamma
+# The median of |W| in place of the mean (second page: BitNet b1.58 Reloaded's
+# absmedian baseline); an even count takes the mean of the two middle values.
+
+def pin_absmedian_hand(O):
+    assert O.absmedian_gamma(np.array([[3, -1, 2]], np.float32)) == f32(2)
+    # even count: (2 + 3) / 2, where the mean of |W| would be 4
+    assert O.absmedian_gamma(np.array([[1, -2, 3, -10]], np.float32)) == f32(2.5)
+    assert O.absmedian_gamma(np.array([[-7.0]], np.float32)) == f32(7)
+    assert O.absmedian_gamma(np.zeros((3, 4), np.float32)) == f32(1e-5)   # clamp
+
+
+def pin_absmedian_library(O):
+    # numpy's median of the magnitudes in float64 is the mean of the two middle
+    # values rounded once in float64; rounding that to float32 is the correctly
+    # rounded mean (53 >= 2 * 24 + 2 bits), so it must equal the oracle's.
+    rng = np.random.default_rng(41)
+    for N, K in ((1, 1), (1, 2), (3, 5), (4, 6), (17, 33), (64, 64), (101, 7)):
+        W = (rng.standard_normal((N, K)) * np.exp2(rng.integers(-20, 20, (N, K)))).astype(np.float32)
+        W[rng.random((N, K)) < 0.2] = 0
+        want = np.float32(np.median(np.abs(W).astype(np.float64)))
+        want = max(want, f32(1e-5))
+        assert O.absmedian_gamma(W) == want, (N, K)
+
+
+def pin_absmedian_ties(O):
+    one = f32(1)
+    u = np.float32(2.0 ** -23)
+    # middle pair 1 and 1 + 2^-23: mean 1 + 2^-24, a tie, to the even 1
+    W = np.array([[0.5, 1, 1 + u, 3]], np.float32)
+    assert O.absmedian_gamma(W) == one
+    # middle pair 1 + 2^-23 and 1 + 2^-22: tie, to the even 1 + 2^-22
+    W = np.array([[0.5, -(1 + u), 1 + 2 * u, 3]], np.float32)
+    assert O.absmedian_gamma(W) == np.float32(1 + 2 * u)
+
+
+def pin_absmedian_invariants(O):
+    rng = np.random.default_rng(42)
+    W = rng.standard_normal((37, 53)).astype(np.float32)
+    g = O.absmedian_gamma(W)
+    P = rng.permutation(W.size)
+    assert O.absmedian_gamma(W.ravel()[P].reshape(53, 37)) == g
+    assert O.absmedian_gamma(-W) == g
+    assert O.absmedian_gamma(W * np.float32(2 ** 7)) == g * np.float32(2 ** 7)
+
+
+def pin_absmedian_statistics(O):
+    # |N(0, s^2)| has median s * Phi^-1(3/4) = 0.67449 s, and the ternarizer
+    # then zeroes |W| < gamma / 2: a fraction 2 Phi(0.33724) - 1 = 0.26406.
+    rng = np.random.default_rng(43)
+    W = (rng.standard_normal((700, 1000)) * 0.02).astype(np.float32)
+    Wt, g = O.quantize_weights_absmedian(W)
+    assert abs(float(g) / (0.02 * 0.6744897501960817) - 1) < 0.005
+    zero = float((Wt == 0).mean())
+    assert abs(zero - (erf(0.33724487509804085 / sqrt(2)))) < 0.003
+
+
 # ------------------------------------------------------------ base-3 packing
 # Five ternary weights per byte (second page: 1.58 bits per weight under
 # compact ternary packing; third page: log2(3) bits of information).  Reading

@@ -50,6 +50,15 @@ MUTANTS = {
                             "for (int64_t k = 0; k + 1 < j->K; ++k) {\n                if (wr[k]"),
     "contract_transposed_store": ("j->y[m * j->N + n] = (int32_t)acc;",
                                   "j->y[n * j->M + m] = (int32_t)acc;"),
+    # absmedian gamma
+    "absmedian_lower_median": ("const uint32_t lo = mag[(D - 1) / 2], hi = mag[D / 2];",
+                               "const uint32_t lo = mag[(D - 1) / 2], hi = mag[(D - 1) / 2];"),
+    "absmedian_upper_median": ("const uint32_t lo = mag[(D - 1) / 2], hi = mag[D / 2];",
+                               "const uint32_t lo = mag[D / 2], hi = mag[D / 2];"),
+    "absmedian_index_off_by_one": ("const uint32_t lo = mag[(D - 1) / 2], hi = mag[D / 2];",
+                                   "const uint32_t lo = mag[D / 2], hi = mag[D / 2 < D - 1 ? D / 2 + 1 : D / 2];"),
+    "absmedian_no_floor": ("    if (!(g >= OR_SCALE_FLOOR)) g = OR_SCALE_FLOOR;", ""),
+    "absmedian_sum_not_mean": ("float g = big_ratio_to_f32(&S, -149, 2);", "float g = big_ratio_to_f32(&S, -149, 1);"),
     # base-3 packing
     "pack3_digit_order_reversed": ("int v = 0, place = 1;\n            for (int j = 0; j < 5; ++j, place *= 3) {",
                                    "int v = 0, place = 81;\n            for (int j = 0; j < 5; ++j, place /= 3) {"),
