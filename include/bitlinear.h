@@ -139,6 +139,19 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed
                            float* gamma_host, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Absmedian variant of bitlinear_pack_weights: gamma is the median of |W| in
+ * place of the mean.  [P2] the paragraph after "Real-World Production
+ * Benchmarks" (BitNet b1.58 Reloaded's absmedian baseline).  For an even
+ * count N*K the median is the mean of the two middle magnitudes, rounded once
+ * to the nearest float32 (ties to even); it is clamped below at 1e-5 and the
+ * ternarization and 2-bit layout are those of bitlinear_pack_weights.  Same
+ * arguments; ws of bitlinear_workspace_bytes(0, N, K) bytes.
+ */
+int bitlinear_pack_weights_absmedian(const float* W, int64_t N, int64_t K, uint8_t* packed,
+                                     float* gamma, float* gamma_host, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+/*
  * Pack ternary weights that are already in {-1, 0, 1} (e.g. drawn directly,
  * with gamma supplied separately).
  *   Wt     [N][K] int8 (in)

@@ -64,6 +64,7 @@ _SIGS = {
     "bitlinear_quantize_act": ([_P, _I64, _I64, _P, _P, _P, _P], ctypes.c_int),
     "bitlinear_rmsnorm_quantize_act": ([_P, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "bitlinear_pack_weights": ([_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "bitlinear_pack_weights_absmedian": ([_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "bitlinear_pack_ternary": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "bitlinear_unpack_weights": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "bitlinear_forward": ([_P, _P, _P, _F, _I64, _I64, _I64, _P, _P, _P, _SZ, _P], ctypes.c_int),
@@ -202,6 +203,16 @@ BITLINEAR_FORMAT_BASE3 = 1
 
 def bitlinear_packed3_bytes(N: int, K: int) -> int:
     return _lib.bitlinear_packed3_bytes(N, K)
+
+
+def bitlinear_pack_weights_absmedian(W, N: int, K: int, packed, gamma=None, gamma_host=None,
+                                     ws=None, ws_bytes: int = 0, stream=None) -> None:
+    """gamma_host: a ctypes.c_float to receive gamma (the call then synchronizes), or None."""
+    if isinstance(gamma_host, ctypes.c_float):
+        gamma_host = ctypes.addressof(gamma_host)
+    _check(_lib.bitlinear_pack_weights_absmedian(_ptr(W), N, K, _ptr(packed), _ptr(gamma),
+                                                 gamma_host, _ptr(ws), ws_bytes, _stream(stream)),
+           "bitlinear_pack_weights_absmedian")
 
 
 def bitlinear_pack_weights3(W, N: int, K: int, packed3, gamma=None, gamma_host=None, ws=None,

@@ -11,6 +11,7 @@
 
 #include "kernels.hpp"
 #include "lut.hpp"
+#include "median.hpp"
 #include "pack.hpp"
 #include "rmsnorm.hpp"
 
@@ -174,7 +175,8 @@ size_t bitlinear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (check_sizes(M, N, K) != BITLINEAR_OK) return 0;
     const size_t f32 = align256((size_t)(M * K)) + align256((size_t)(4 * M)) +
                        align256(forward_ws_bytes(M, N, K));
-    const size_t pack = align256(gamma_ws_bytes());
+    size_t pack = align256(gamma_ws_bytes());
+    if (align256(median_ws_bytes()) > pack) pack = align256(median_ws_bytes());
     return f32 > pack ? f32 : pack;
 }
 
@@ -211,6 +213,26 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed
     if (rc) return rc;
     if (gamma_host) {
         const float* g = (const float*)((const char*)ws + kGammaBins * sizeof(unsigned long long));
+        BL_HIP_CHECK(hipMemcpyAsync(gamma_host, g, sizeof(float), hipMemcpyDeviceToHost, s));
+        BL_HIP_CHECK(hipStreamSynchronize(s));
+    }
+    return BITLINEAR_OK;
+}
+
+int bitlinear_pack_weights_absmedian(const float* W, int64_t N, int64_t K, uint8_t* packed,
+                                     float* gamma, float* gamma_host, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    int rc = check_sizes(0, N, K);
+    if (rc) return rc;
+    if (!W || !packed) return BITLINEAR_EINVAL;
+    if (!aligned(W, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
+    if (!ws || !aligned(ws, 256) || ws_bytes < median_ws_bytes()) return BITLINEAR_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    clear_hip_error();
+    const float* g = nullptr;
+    rc = launch_pack_weights_absmedian(W, N, K, packed, gamma, ws, &g, s);
+    if (rc) return rc;
+    if (gamma_host) {
         BL_HIP_CHECK(hipMemcpyAsync(gamma_host, g, sizeof(float), hipMemcpyDeviceToHost, s));
         BL_HIP_CHECK(hipStreamSynchronize(s));
     }

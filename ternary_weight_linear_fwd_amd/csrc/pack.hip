@@ -247,6 +247,15 @@ int launch_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed, f
     return BITLINEAR_OK;
 }
 
+int launch_ternarize_pack(const float* W, int64_t N, int64_t K, const float* gamma_dev,
+                          uint8_t* packed, hipStream_t stream) {
+    const int64_t nwords = layout_words(N, K);
+    hipLaunchKernelGGL(ternarize_pack_kernel, dim3((unsigned)ceil_div(nwords, 256)), dim3(256), 0,
+                       stream, W, N, K, ceil_div(K, 64), gamma_dev, (uint32_t*)packed, nwords);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
+
 __global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
 
 int launch_zero_i32(int32_t* p, hipStream_t stream) {

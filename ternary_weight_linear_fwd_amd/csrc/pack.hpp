@@ -10,6 +10,10 @@ namespace bl {
 int launch_gamma(const float* W, int64_t N, int64_t K, float* gamma_dev, void* ws,
                  hipStream_t stream);
 
+// Ternarize W with the scale at gamma_dev (device) and write the 2-bit layout.
+int launch_ternarize_pack(const float* W, int64_t N, int64_t K, const float* gamma_dev,
+                          uint8_t* packed, hipStream_t stream);
+
 // *p = 0, queued on the stream.
 int launch_zero_i32(int32_t* p, hipStream_t stream);
 

@@ -114,6 +114,9 @@ def test_validation_before_any_device_work():
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, FAKE + 8, 1 << 20, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_pack_weights_absmedian", FAKE, 64, 64, FAKE, None, None, FAKE, 4096, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_pack_weights_absmedian", None, 64, 64, FAKE, None, None, FAKE, 1 << 20, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_pack_weights_absmedian", FAKE, 64, 24, FAKE, None, None, FAKE, 1 << 20, None) == L.BITLINEAR_EUNSUPPORTED
     assert _rc("bitlinear_pack_ternary3", None, 64, 64, FAKE, None, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_pack_ternary3", FAKE, 64, 20, FAKE, None, None) == L.BITLINEAR_EUNSUPPORTED
     assert _rc("bitlinear_unpack_weights3", FAKE, 64, 64, None, None, None) == L.BITLINEAR_EINVAL
