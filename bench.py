@@ -175,6 +175,33 @@ def bench_lut(torch, L, reps: int):
     return out
 
 
+def bench_pack(torch, L, reps: int):
+    """Offline weight preparation of the largest 70B projection (28672 x 8192
+    latent float32): absmean and absmedian scales into the 2-bit layout, and
+    absmean into the base-3 layout; GB/s of latent weights."""
+    import ctypes
+    N, K = 28672, 8192
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    W = torch.randn((N, K), generator=gen, device="cuda") * 0.02
+    p2 = torch.empty(L.bitlinear_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+    p3 = torch.empty(L.bitlinear_packed3_bytes(N, K), dtype=torch.uint8, device="cuda")
+    ws_bytes = L.bitlinear_workspace_bytes(0, N, K)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    calls = {
+        "absmean_2bit": lambda: L.bitlinear_pack_weights(W, N, K, p2, None, None, ws, ws_bytes),
+        "absmedian_2bit": lambda: L.bitlinear_pack_weights_absmedian(W, N, K, p2, None, None, ws,
+                                                                     ws_bytes),
+        "absmean_base3": lambda: L.bitlinear_pack_weights3(W, N, K, p3, None, None, ws, ws_bytes),
+    }
+    out = {"matrix": f"{N}x{K} float32 latent"}
+    for name, fn in calls.items():
+        fn()
+        ms = time_events(torch, fn, reps)
+        out[name] = {"ms": round(ms, 3), "latent_gbs": round(4 * N * K / (ms * 1e-3) / 1e9, 1)}
+    del W, p2, p3, ws
+    return out
+
+
 def cpu_baseline(sw, S, budget_s: float = 12.0):
     """The oracle (unchanged) on a bounded sample of the sweep: layer 0's seven
     projections at M = 1 (quantize + contract + dequant), run repeatedly until
@@ -255,7 +282,8 @@ def summarize_profile(root: str) -> str:
         per = {}
         for r in rows:
             key = "copy" if "copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower() \
-                else ("contraction" if "gemv_dot4_kernel" in r["Kernel_Name"] else None)
+                else ("contraction" if ("gemv_dot4_kernel" in r["Kernel_Name"]
+                                        or "gemm_prefill_kernel" in r["Kernel_Name"]) else None)
             if key:
                 per.setdefault(key, []).append(float(r["Counter_Value"]))
         if "copy" in per and "contraction" in per:
@@ -304,6 +332,8 @@ def main() -> int:
     ap.add_argument("--profile-run", action="store_true",
                     help="short run for rocprofv3: the M=1 sweep, the contraction kernel alone and a "
                          "1 GiB copy whose counters calibrate FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--profile-prefill", action="store_true",
+                    help="short run for rocprofv3: the two 3B prefill GEMMs and a calibration copy")
     ap.add_argument("--summarize", metavar="DIR", help="summarize rocprofv3 output under DIR")
     args = ap.parse_args()
     if args.summarize:
@@ -323,6 +353,15 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"device {torch.cuda.get_device_name(0)}; building the sweep ({args.layers} layers)")
     Ms = (1,) if args.no_m16 else (1, 16)
+    if args.profile_prefill:
+        for r in bench_prefill(torch, L, S, max(1, args.steps)):
+            log(f"prefill {r['gemm']}: {r['us']} us")
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        return 0
     sw = DecodeSweep(layers=args.layers, Ms=Ms, progress=log)
     log(f"packed weights resident: {sw.weight_bytes() / 1e9:.3f} GB")
     if args.profile_run:
@@ -376,6 +415,11 @@ def main() -> int:
             log(f"decode {r['gemv']}: " + "; ".join(
                 f"{k} {v['us']} us {v['weight_gbs']} GB/s {v['gweights_per_s']} Gw/s"
                 for k, v in r.items() if k != "gemv"))
+
+    if not args.no_prefill:
+        extra["pack"] = bench_pack(torch, L, 3)
+        log("pack " + "; ".join(f"{k} {v['ms']} ms ({v['latent_gbs']} GB/s)"
+                                for k, v in extra["pack"].items() if k != "matrix"))
 
     cpu = None
     if not args.no_cpu_baseline:
