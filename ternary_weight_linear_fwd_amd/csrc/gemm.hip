@@ -101,31 +101,45 @@ struct PrefillCtx {
     static constexpr int Stage = AStage + 8192;   // + four wavefronts x two 1 KB B blocks
     static constexpr int NA = AStage / 4096;      // A DMA instructions per wave per step
     static constexpr int Ops = NA + 2;            // vector memory instructions per wave per step
-    const int8_t* asrc[NA];
-    int acol[NA];
-    const uint8_t* bsrc;   // this lane's 16 bytes of k-block 0 of the wavefront's row group
+    // DMA sources are a wave-uniform base (scalar registers) plus a 32-bit
+    // per-lane offset, so that the main loop spends no vector ALU work on
+    // addresses (row offsets stay below 2^32 since K <= 2^24).
+    const int8_t* abase;    // the tile's first activation row
+    uint32_t aoff[NA];      // (row in the tile, clamped below M) * K + byte column
+    uint32_t acol[NA];      // byte column inside the 128-k step
+    const uint8_t* bbase;   // k-block 0 of the wavefront's 64-row weight group
+    uint32_t boff;          // this lane's 16 bytes of a block: lane * 16
+    uint32_t afrag[4];      // LDS offset of this lane's A fragment of group d, row tile 0
+    uint32_t sxfrag;        // afrag[wave]: the word group this wavefront sums
     int64_t K, Kb, nsteps;
     int wave, lane, ln, lg;
 };
 
 // Queue step `step` into LDS stage `stage`: this wave's NA activation DMAs and
-// its two weight-block DMAs.
-template <int MT>
+// its two weight-block DMAs.  CHECKED: the step may reach past K (the last
+// step, or one queued past the end), so addresses are clamped in bounds;
+// otherwise all 128 k of the step lie inside K.
+template <int MT, bool CHECKED>
 __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT>& c, uint8_t* st, int64_t step) {
     using Ctx = PrefillCtx<MT>;
     const int64_t kbase = step * 128;
-    const bool full = kbase + 128 <= c.K;
 #pragma unroll
     for (int j = 0; j < Ctx::NA; ++j) {
-        const int8_t* src = c.asrc[j] + kbase;
-        if (!full && kbase + c.acol[j] >= c.K) src = c.asrc[j] + (c.K - 16 - c.acol[j]);
+        const int8_t* src;
+        if constexpr (CHECKED) {
+            const uint32_t o = kbase + c.acol[j] >= c.K ? c.aoff[j] - c.acol[j] + (uint32_t)(c.K - 16)
+                                                        : c.aoff[j] + (uint32_t)kbase;
+            src = c.abase + o;
+        } else {
+            src = (c.abase + kbase) + c.aoff[j];
+        }
         dma_16(src, st + (j * 4 + c.wave) * 1024);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         int64_t kb = step * 2 + h;
-        kb = kb < c.Kb ? kb : c.Kb - 1;   // a block past the end is replaced at use
-        dma_16(c.bsrc + kb * 1024, st + Ctx::AStage + (c.wave * 2 + h) * 1024);
+        if constexpr (CHECKED) kb = kb < c.Kb ? kb : c.Kb - 1;   // a block past the end is replaced at use
+        dma_16((c.bbase + kb * 1024) + c.boff, st + Ctx::AStage + (c.wave * 2 + h) * 1024);
     }
 }
 
@@ -151,13 +165,15 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, const u
             for (int t = 0; t < 2; ++t) bw[t] = v4i{0x55555555, 0x55555555, 0x55555555, 0x55555555};
         }
     }
+    // Row 32i + ln, chunk ((lg & 1) * 4 + d) ^ ((row >> 1) & 7): the swizzle
+    // term is the same for every row tile i, so the per-lane offsets are
+    // computed once and i enters as an immediate offset.
     auto a_frag = [&](int i, int d) {
-        const int r = i * 32 + (c.ln & 31);
-        return *reinterpret_cast<const v4i*>(A + r * 128 + ((((c.lg & 1) * 4 + (d & 3)) ^ ((r >> 1) & 7)) << 4));
+        return *reinterpret_cast<const v4i*>(A + i * 4096 + (c.afrag[d & 3] & 4095u));
     };
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-        const v4i f = a_frag(i, c.wave);
+        const v4i f = *reinterpret_cast<const v4i*>(A + i * 4096 + (c.sxfrag & 4095u));
         sx[i] = __builtin_amdgcn_sdot4(f.x, 0x01010101, sx[i], false);
         sx[i] = __builtin_amdgcn_sdot4(f.y, 0x01010101, sx[i], false);
         sx[i] = __builtin_amdgcn_sdot4(f.z, 0x01010101, sx[i], false);
@@ -207,7 +223,7 @@ __device__ __forceinline__ void prefill_step(const PrefillCtx<MT>& c, const uint
                                              int64_t step, v16i (&acc)[MT][2], int (&sx)[MT]) {
     wait_vmcnt<PrefillCtx<MT>::Ops>();
     __builtin_amdgcn_s_barrier();   // not __syncthreads(): that would drain the loads in flight
-    prefill_issue<MT>(c, refill, step + 2);
+    prefill_issue<MT, false>(c, refill, step + 2);   // step + 2 <= nsteps - 2: never the last
     prefill_compute<MT, false>(c, cur, step, acc, sx);
 }
 
@@ -219,7 +235,7 @@ __device__ __forceinline__ void prefill_step_tail(const PrefillCtx<MT>& c, const
     if (step + 1 < c.nsteps) wait_vmcnt<PrefillCtx<MT>::Ops>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (step + 2 < c.nsteps) prefill_issue<MT>(c, refill, step + 2);
+    if (step + 2 < c.nsteps) prefill_issue<MT, true>(c, refill, step + 2);
     prefill_compute<MT, true>(c, cur, step, acc, sx);
 }
 
@@ -262,15 +278,21 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
     c.lane = lane;
     c.ln = lane & 31;
     c.lg = lane >> 5;
+    c.abase = p.xq + m0 * K;
 #pragma unroll
     for (int j = 0; j < Ctx::NA; ++j) {
         const int P = (j * 4 + wave) * 64 + lane;       // physical 16-byte slot
         const int r = P >> 3;
-        c.acol[j] = ((P & 7) ^ ((r >> 1) & 7)) * 16;    // logical byte column
-        const int64_t m = m0 + r < M ? m0 + r : M - 1;
-        c.asrc[j] = p.xq + m * K + c.acol[j];
+        c.acol[j] = (uint32_t)(((P & 7) ^ ((r >> 1) & 7)) * 16);   // logical byte column
+        const int64_t rr = m0 + r < M ? r : M - 1 - m0;
+        c.aoff[j] = (uint32_t)(rr * K) + c.acol[j];
     }
-    c.bsrc = reinterpret_cast<const uint8_t*>(p.packed) + (group_ok ? group : 0) * Kb * 1024 + lane * 16;
+    c.bbase = reinterpret_cast<const uint8_t*>(p.packed) + (group_ok ? group : 0) * Kb * 1024;
+    c.boff = (uint32_t)lane * 16;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        c.afrag[d] = (uint32_t)((c.ln & 31) * 128 + ((((c.lg & 1) * 4 + d) ^ ((c.ln >> 1) & 7)) << 4));
+    c.sxfrag = (uint32_t)((c.ln & 31) * 128 + ((((c.lg & 1) * 4 + (wave & 3)) ^ ((c.ln >> 1) & 7)) << 4));
 
     v16i acc[MT][2];
     int sx[MT];
@@ -285,19 +307,21 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
 
     // Steps 0 and 1 are always queued (past the end they read clamped, in-bounds
     // addresses and are never used), so that no branch precedes the main loop.
-    prefill_issue<MT>(c, stage0, 0);
-    prefill_issue<MT>(c, stage1, 1);
+    prefill_issue<MT, true>(c, stage0, 0);
+    prefill_issue<MT, true>(c, stage1, 1);
+    // The main loop queues steps up to nsteps - 2, all of them whole.
     int64_t step = 0;
-    for (; step + 5 <= c.nsteps; step += 3) {
+    for (; step + 6 <= c.nsteps; step += 3) {
         prefill_step<MT>(c, stage0, stage2, step, acc, sx);
         prefill_step<MT>(c, stage1, stage0, step + 1, acc, sx);
         prefill_step<MT>(c, stage2, stage1, step + 2, acc, sx);
     }
-    // The last two to four steps.
+    // The last one to five steps.
     prefill_step_tail<MT>(c, stage0, stage2, step, acc, sx);
     prefill_step_tail<MT>(c, stage1, stage0, step + 1, acc, sx);
     prefill_step_tail<MT>(c, stage2, stage1, step + 2, acc, sx);
     prefill_step_tail<MT>(c, stage0, stage2, step + 3, acc, sx);
+    prefill_step_tail<MT>(c, stage1, stage0, step + 4, acc, sx);
 
     // Row sums: partials of (wave, lane group) -> one total per tile row.
 #pragma unroll

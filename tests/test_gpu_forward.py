@@ -5,7 +5,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import (assert_y_close, forward, forward_f32, pack_ternary, pack_weights, say)
+from gpu_helpers import (assert_y_close, bl, forward, forward_f32, pack_ternary, pack_weights, say, to_dev,
+                         torch_cuda)
 from ternary_weight_linear_fwd_amd import synthetic as S
 
 pytestmark = pytest.mark.gpu
@@ -101,3 +102,44 @@ def test_determinism():
                                    (1000, 200000, 32), (1537, 131136, 16)])
 def test_prefill_tall_tiles(M, N, K):
     run_case(M, N, K, seed=M + N + K, latent=False)
+
+
+
+# Prefill shapes of the batched-decode and 3B workloads and a few ragged ones,
+# each run twice (identical bits), checked row by row against the oracle (or
+# on sampled rows plus exact int64 checksums of every row when large).
+def test_prefill_workload_shapes():
+    torch = torch_cuda()
+    L = bl()
+    shapes = [(128, 11008, 4096), (128, 4096, 11008), (832, 8192, 2560), (96, 1000, 4160),
+              (130, 200, 208), (2048, 8640, 3200)]
+    for i, (M, N, K) in enumerate(shapes):
+        say(f"prefill shape M={M} N={N} K={K}")
+        x = S.random_x(700 + i, M, K, "t3")
+        Wt = S.random_ternary(800 + i, N, K)
+        packed, bad = pack_ternary(Wt)
+        assert bad == 0
+        xq, eta = oracle.quantize_act(x)
+        xq_d, eta_d = to_dev(xq), to_dev(eta)
+        ws_bytes = L.bitlinear_workspace_bytes(M, N, K)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        outs = []
+        for rep in range(2):
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            y_int = torch.empty((M, N), dtype=torch.int32, device="cuda")
+            L.bitlinear_forward(xq_d, eta_d, packed, 0.0173, M, N, K, y, y_int, ws, ws_bytes)
+            torch.cuda.synchronize()
+            outs.append((y.cpu().numpy(), y_int.cpu().numpy()))
+        (y, y_int), (y2, y_int2) = outs
+        assert np.array_equal(y_int, y_int2) and np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+        rows = np.arange(M) if M * N * K <= 6e9 else \
+            np.sort(np.random.default_rng(i).choice(M, 48, replace=False))
+        y_ref, y_int_ref = oracle.forward_q(xq[rows], eta[rows], Wt, np.float32(0.0173), threads=8)
+        assert np.array_equal(y_int[rows], y_int_ref), np.argwhere(y_int[rows] != y_int_ref)[:5]
+        assert_y_close(y[rows], y_ref)
+        assert np.array_equal(y[rows].view(np.uint32), y_ref.view(np.uint32))
+        # every row: exact int64 checksums
+        r = np.random.default_rng(i).integers(-3, 4, N).astype(np.int64)
+        x64 = xq.astype(np.int64)
+        assert np.array_equal(y_int.astype(np.int64).sum(axis=1), x64 @ Wt.astype(np.int64).sum(axis=0))
+        assert np.array_equal(y_int.astype(np.int64) @ r, x64 @ (Wt.astype(np.int64).T @ r))
