@@ -98,9 +98,8 @@ template <int MT>
 struct PrefillCtx {
     static constexpr int BM = 32 * MT;            // token rows per workgroup tile
     static constexpr int AStage = BM * 128;       // bytes of A per stage
-    static constexpr int Stage = AStage + 8192;   // + four wavefronts x two 1 KB B blocks
     static constexpr int NA = AStage / 4096;      // A DMA instructions per wave per step
-    static constexpr int Ops = NA + 2;            // vector memory instructions per wave per step
+    static constexpr int Ops = NA + 2;            // + two weight loads: vector memory instructions per step
     // DMA sources are a wave-uniform base (scalar registers) plus a 32-bit
     // per-lane offset, so that the main loop spends no vector ALU work on
     // addresses (row offsets stay below 2^32 since K <= 2^24).
@@ -108,19 +107,20 @@ struct PrefillCtx {
     uint32_t aoff[NA];      // (row in the tile, clamped below M) * K + byte column
     uint32_t acol[NA];      // byte column inside the 128-k step
     const uint8_t* bbase;   // k-block 0 of the wavefront's 64-row weight group
-    uint32_t boff;          // this lane's 16 bytes of a block: lane * 16
+    uint32_t boff;          // lane (ln, lg): row ln's 16 bytes of k-block lg of a step
     uint32_t afrag[4];      // LDS offset of this lane's A fragment of group d, row tile 0
     uint32_t sxfrag;        // afrag[wave]: the word group this wavefront sums
     int64_t K, Kb, nsteps;
     int wave, lane, ln, lg;
 };
 
-// Queue step `step` into LDS stage `stage`: this wave's NA activation DMAs and
-// its two weight-block DMAs.  CHECKED: the step may reach past K (the last
-// step, or one queued past the end), so addresses are clamped in bounds;
-// otherwise all 128 k of the step lie inside K.
+// Queue step `step`: this wave's NA activation DMAs into LDS stage `st` and
+// its two weight loads into registers bq (the weight chunks are private to
+// the wavefront, so they skip LDS).  CHECKED: the step may reach past K (the
+// last step, or one queued past the end), so addresses are clamped in
+// bounds; otherwise all 128 k of the step lie inside K.
 template <int MT, bool CHECKED>
-__device__ __forceinline__ void prefill_issue(const PrefillCtx<MT>& c, uint8_t* st, int64_t step) {
+__device__ __forceinline__ void prefill_issue(const PrefillCtx<MT>& c, uint8_t* st, int64_t step, v4i (&bq)[2]) {
     using Ctx = PrefillCtx<MT>;
     const int64_t kbase = step * 128;
 #pragma unroll
@@ -135,12 +135,16 @@ __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT>& c, uint8_t* 
         }
         dma_16(src, st + (j * 4 + c.wave) * 1024);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        int64_t kb = step * 2 + h;
-        if constexpr (CHECKED) kb = kb < c.Kb ? kb : c.Kb - 1;   // a block past the end is replaced at use
-        dma_16((c.bbase + kb * 1024) + c.boff, st + Ctx::AStage + (c.wave * 2 + h) * 1024);
+    // Lane (ln, lg) takes rows ln and ln + 32 of k-block 2 * step + lg.
+    const uint8_t* bsrc;
+    if constexpr (CHECKED) {
+        const int64_t kb = step * 2 + c.lg < c.Kb ? step * 2 + c.lg : c.Kb - 1;   // past the end: replaced at use
+        bsrc = c.bbase + (uint32_t)(kb * 1024 + (c.boff & 1023u));
+    } else {
+        bsrc = (c.bbase + step * 2048) + c.boff;
     }
+    bq[0] = *reinterpret_cast<const v4i*>(bsrc);
+    bq[1] = *reinterpret_cast<const v4i*>(bsrc + 512);
 }
 
 // One K-step of MFMAs from the LDS stage at A.  Wavefront w also adds word
@@ -149,16 +153,8 @@ __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT>& c, uint8_t* 
 // whose second k-block can lie past the end.
 template <int MT, bool TAIL>
 __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, const uint8_t* A, int64_t step,
-                                                v16i (&acc)[MT][2], int (&sx)[MT]) {
-    using Ctx = PrefillCtx<MT>;
-    // The masks bound every LDS offset visibly, so that the compiler can prove
-    // each read stays inside this stage's object and tell it apart from the
-    // loads in flight into the other stages.
-    const uint8_t* Bl = A + Ctx::AStage + ((c.wave & 3) * 2 + (c.lg & 1)) * 1024;
-    const v4i* Bv = reinterpret_cast<const v4i*>(Bl) + (c.ln & 31);
-    v4i bw[2];
-    bw[0] = Bv[0];
-    bw[1] = Bv[32];
+                                                const v4i (&bq)[2], v16i (&acc)[MT][2], int (&sx)[MT]) {
+    v4i bw[2] = {bq[0], bq[1]};
     if constexpr (TAIL) {
         if (step * 2 + 1 >= c.Kb && c.lg == 1) {   // k-block past the end: code 01
 #pragma unroll
@@ -167,7 +163,10 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, const u
     }
     // Row 32i + ln, chunk ((lg & 1) * 4 + d) ^ ((row >> 1) & 7): the swizzle
     // term is the same for every row tile i, so the per-lane offsets are
-    // computed once and i enters as an immediate offset.
+    // computed once and i enters as an immediate offset.  The masks bound
+    // every LDS offset visibly, so that the compiler can prove each read stays
+    // inside this stage's object and tell it apart from the loads in flight
+    // into the other stages.
     auto a_frag = [&](int i, int d) {
         return *reinterpret_cast<const v4i*>(A + i * 4096 + (c.afrag[d & 3] & 4095u));
     };
@@ -220,23 +219,25 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, const u
 // own.
 template <int MT>
 __device__ __forceinline__ void prefill_step(const PrefillCtx<MT>& c, const uint8_t* cur, uint8_t* refill,
-                                             int64_t step, v16i (&acc)[MT][2], int (&sx)[MT]) {
+                                             int64_t step, const v4i (&bq_cur)[2], v4i (&bq_refill)[2],
+                                             v16i (&acc)[MT][2], int (&sx)[MT]) {
     wait_vmcnt<PrefillCtx<MT>::Ops>();
     __builtin_amdgcn_s_barrier();   // not __syncthreads(): that would drain the loads in flight
-    prefill_issue<MT, false>(c, refill, step + 2);   // step + 2 <= nsteps - 2: never the last
-    prefill_compute<MT, false>(c, cur, step, acc, sx);
+    prefill_issue<MT, false>(c, refill, step + 2, bq_refill);   // step + 2 <= nsteps - 2: never the last
+    prefill_compute<MT, false>(c, cur, step, bq_cur, acc, sx);
 }
 
 // Any step, including the last ones (nothing left to refill, or past the end).
 template <int MT>
 __device__ __forceinline__ void prefill_step_tail(const PrefillCtx<MT>& c, const uint8_t* cur, uint8_t* refill,
-                                                  int64_t step, v16i (&acc)[MT][2], int (&sx)[MT]) {
+                                                  int64_t step, const v4i (&bq_cur)[2], v4i (&bq_refill)[2],
+                                                  v16i (&acc)[MT][2], int (&sx)[MT]) {
     if (step >= c.nsteps) return;
     if (step + 1 < c.nsteps) wait_vmcnt<PrefillCtx<MT>::Ops>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (step + 2 < c.nsteps) prefill_issue<MT, true>(c, refill, step + 2);
-    prefill_compute<MT, true>(c, cur, step, acc, sx);
+    if (step + 2 < c.nsteps) prefill_issue<MT, true>(c, refill, step + 2, bq_refill);
+    prefill_compute<MT, true>(c, cur, step, bq_cur, acc, sx);
 }
 
 template <int MT, bool GROUPED>
@@ -245,9 +246,9 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
     constexpr int BM = Ctx::BM;
     // Three stages, each its own LDS object, so that the compiler can tell a
     // read of one stage from the loads in flight into the others.
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[Ctx::Stage];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[Ctx::Stage];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage2[Ctx::Stage];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[Ctx::AStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[Ctx::AStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage2[Ctx::AStage];
     __shared__ int rowsum_part[8][BM];   // [wave * 2 + lane group][row]
     __shared__ int rowsum[BM];
 
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
         c.aoff[j] = (uint32_t)(rr * K) + c.acol[j];
     }
     c.bbase = reinterpret_cast<const uint8_t*>(p.packed) + (group_ok ? group : 0) * Kb * 1024;
-    c.boff = (uint32_t)lane * 16;
+    c.boff = (uint32_t)(c.lg * 1024 + c.ln * 16);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
         c.afrag[d] = (uint32_t)((c.ln & 31) * 128 + ((((c.lg & 1) * 4 + d) ^ ((c.ln >> 1) & 7)) << 4));
@@ -307,21 +308,23 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
 
     // Steps 0 and 1 are always queued (past the end they read clamped, in-bounds
     // addresses and are never used), so that no branch precedes the main loop.
-    prefill_issue<MT, true>(c, stage0, 0);
-    prefill_issue<MT, true>(c, stage1, 1);
+    // Weight words of the steps in flight, one register set per stage.
+    v4i bq0[2], bq1[2], bq2[2];
+    prefill_issue<MT, true>(c, stage0, 0, bq0);
+    prefill_issue<MT, true>(c, stage1, 1, bq1);
     // The main loop queues steps up to nsteps - 2, all of them whole.
     int64_t step = 0;
     for (; step + 6 <= c.nsteps; step += 3) {
-        prefill_step<MT>(c, stage0, stage2, step, acc, sx);
-        prefill_step<MT>(c, stage1, stage0, step + 1, acc, sx);
-        prefill_step<MT>(c, stage2, stage1, step + 2, acc, sx);
+        prefill_step<MT>(c, stage0, stage2, step, bq0, bq2, acc, sx);
+        prefill_step<MT>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+        prefill_step<MT>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
     }
     // The last one to five steps.
-    prefill_step_tail<MT>(c, stage0, stage2, step, acc, sx);
-    prefill_step_tail<MT>(c, stage1, stage0, step + 1, acc, sx);
-    prefill_step_tail<MT>(c, stage2, stage1, step + 2, acc, sx);
-    prefill_step_tail<MT>(c, stage0, stage2, step + 3, acc, sx);
-    prefill_step_tail<MT>(c, stage1, stage0, step + 4, acc, sx);
+    prefill_step_tail<MT>(c, stage0, stage2, step, bq0, bq2, acc, sx);
+    prefill_step_tail<MT>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+    prefill_step_tail<MT>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+    prefill_step_tail<MT>(c, stage0, stage2, step + 3, bq0, bq2, acc, sx);
+    prefill_step_tail<MT>(c, stage1, stage0, step + 4, bq1, bq0, acc, sx);
 
     // Row sums: partials of (wave, lane group) -> one total per tile row.
 #pragma unroll
