@@ -57,18 +57,19 @@ struct GemmArgs {
 // row index fastest inside a band, so the tiles an XCD runs at one time cover
 // a compact block (about 10 x 10 tiles of 64 x 256): its L2 then serves their
 // activation rows and weight columns to all of them.
-__device__ inline int64_t xcd_tile(int64_t b, int64_t T) {
-    constexpr int64_t X = 8;
-    const int64_t xcd = b % X, slot = b / X, q = T / X, r = T % X;
+// Tile counts stay below 2^26 (M * N < 2^40), so 32-bit arithmetic suffices.
+__device__ inline uint32_t xcd_tile(uint32_t b, uint32_t T) {
+    constexpr uint32_t X = 8;
+    const uint32_t xcd = b % X, slot = b / X, q = T / X, r = T % X;
     return xcd * q + (xcd < r ? xcd : r) + slot;
 }
 
-__device__ inline void tile_coords(int64_t b, int64_t ntm, int64_t ntn, int64_t band, int64_t& tm,
+__device__ inline void tile_coords(uint32_t b, uint32_t ntm, uint32_t ntn, uint32_t band, int64_t& tm,
                                    int64_t& tn) {
-    const int64_t t = xcd_tile(b, ntm * ntn);
-    const int64_t bi = t / (band * ntn);
-    const int64_t rows = ntm - bi * band < band ? ntm - bi * band : band;
-    const int64_t within = t - bi * band * ntn;
+    const uint32_t t = xcd_tile(b, ntm * ntn);
+    const uint32_t bi = t / (band * ntn);
+    const uint32_t rows = ntm - bi * band < band ? ntm - bi * band : band;
+    const uint32_t within = t - bi * band * ntn;
     tm = bi * band + within % rows;
     tn = within / rows;
 }
@@ -211,37 +212,41 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, const u
     }
 }
 
-// A step of the ring that is not among the last two: wait until its data has
-// landed (the next step's loads stay in flight), make that true for every
-// wave, refill the stage that step-1 read (every wave is past it) with
-// step+2, compute.  Straight-line code, so that the compiler can see which
-// stage each LDS read and each load in flight touch and adds no waits of its
-// own.
-template <int MT>
+// A step of a ring of NS stages that is not among the last ones: wait until
+// its data has landed (the next NS - 2 steps' loads stay in flight), make
+// that true for every wave, refill the stage that step - 1 read (every wave
+// is past it) with step + NS - 1, compute.  Straight-line code, so that the
+// compiler can see which stage each LDS read and each load in flight touch
+// and adds no waits of its own.
+template <int MT, int NS>
 __device__ __forceinline__ void prefill_step(const PrefillCtx<MT>& c, const uint8_t* cur, uint8_t* refill,
                                              int64_t step, const v4i (&bq_cur)[2], v4i (&bq_refill)[2],
                                              v16i (&acc)[MT][2], int (&sx)[MT]) {
-    wait_vmcnt<PrefillCtx<MT>::Ops>();
+    wait_vmcnt<(NS - 2) * PrefillCtx<MT>::Ops>();
     __builtin_amdgcn_s_barrier();   // not __syncthreads(): that would drain the loads in flight
-    prefill_issue<MT, false>(c, refill, step + 2, bq_refill);   // step + 2 <= nsteps - 2: never the last
+    prefill_issue<MT, false>(c, refill, step + NS - 1, bq_refill);   // <= nsteps - 2: never the last
     prefill_compute<MT, false>(c, cur, step, bq_cur, acc, sx);
 }
 
 // Any step, including the last ones (nothing left to refill, or past the end).
-template <int MT>
+template <int MT, int NS>
 __device__ __forceinline__ void prefill_step_tail(const PrefillCtx<MT>& c, const uint8_t* cur, uint8_t* refill,
                                                   int64_t step, const v4i (&bq_cur)[2], v4i (&bq_refill)[2],
                                                   v16i (&acc)[MT][2], int (&sx)[MT]) {
+    constexpr int Ops = PrefillCtx<MT>::Ops;
     if (step >= c.nsteps) return;
-    if (step + 1 < c.nsteps) wait_vmcnt<PrefillCtx<MT>::Ops>();
+    const int64_t later = c.nsteps - 1 - step;   // queued steps after this one
+    if (NS >= 4 && later >= 2) wait_vmcnt<(NS >= 4 ? 2 : 1) * Ops>();
+    else if (later >= 1) wait_vmcnt<Ops>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (step + 2 < c.nsteps) prefill_issue<MT, true>(c, refill, step + 2, bq_refill);
+    if (step + NS - 1 < c.nsteps) prefill_issue<MT, true>(c, refill, step + NS - 1, bq_refill);
     prefill_compute<MT, true>(c, cur, step, bq_cur, acc, sx);
 }
 
-template <int MT, bool GROUPED>
+template <int MT, bool GROUPED, int NS>
 __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefill_kernel(GemmArgs a) {
+    static_assert(NS == 3 || NS == 4, "ring of three or four stages");
     using Ctx = PrefillCtx<MT>;
     constexpr int BM = Ctx::BM;
     // Three stages, each its own LDS object, so that the compiler can tell a
@@ -249,8 +254,9 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[Ctx::AStage];
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[Ctx::AStage];
     __shared__ __attribute__((aligned(1024))) uint8_t stage2[Ctx::AStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage3[NS == 4 ? Ctx::AStage : 16];
     __shared__ int rowsum_part[8][BM];   // [wave * 2 + lane group][row]
-    __shared__ int rowsum[BM];
+    __shared__ float2 rowinfo[BM];   // (row sum as int bits, dequant scale)
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
         tile_m = blockIdx.y;
     } else {
         p = a.p;
-        tile_coords(blockIdx.x, a.ntiles_m, a.ntiles_n, 16 / MT, tile_m, tile_n);
+        tile_coords(blockIdx.x, (uint32_t)a.ntiles_m, (uint32_t)a.ntiles_n, 16 / MT, tile_m, tile_n);
     }
     const int64_t M = a.M, N = p.N, K = p.K, Kb = p.Kb;
     const int64_t m0 = tile_m * BM;
@@ -306,27 +312,48 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
             for (int e = 0; e < 16; ++e) acc[i][t][e] = 0;
     }
 
-    // Steps 0 and 1 are always queued (past the end they read clamped, in-bounds
-    // addresses and are never used), so that no branch precedes the main loop.
-    // Weight words of the steps in flight, one register set per stage.
-    v4i bq0[2], bq1[2], bq2[2];
+    // The first NS - 1 steps are always queued (past the end they read clamped,
+    // in-bounds addresses and are never used), so that no branch precedes the
+    // main loop.  Weight words of the steps in flight: one register set per
+    // stage.
+    v4i bq0[2], bq1[2], bq2[2], bq3[2];
     prefill_issue<MT, true>(c, stage0, 0, bq0);
     prefill_issue<MT, true>(c, stage1, 1, bq1);
-    // The main loop queues steps up to nsteps - 2, all of them whole.
+    if constexpr (NS == 4) prefill_issue<MT, true>(c, stage2, 2, bq2);
     int64_t step = 0;
-    for (; step + 6 <= c.nsteps; step += 3) {
-        prefill_step<MT>(c, stage0, stage2, step, bq0, bq2, acc, sx);
-        prefill_step<MT>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-        prefill_step<MT>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+    if constexpr (NS == 3) {
+        // The main loop queues steps up to nsteps - 2, all of them whole.
+        for (; step + 6 <= c.nsteps; step += 3) {
+            prefill_step<MT, 3>(c, stage0, stage2, step, bq0, bq2, acc, sx);
+            prefill_step<MT, 3>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+            prefill_step<MT, 3>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+        }
+        // The last one to five steps.
+        prefill_step_tail<MT, 3>(c, stage0, stage2, step, bq0, bq2, acc, sx);
+        prefill_step_tail<MT, 3>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, 3>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+        prefill_step_tail<MT, 3>(c, stage0, stage2, step + 3, bq0, bq2, acc, sx);
+        prefill_step_tail<MT, 3>(c, stage1, stage0, step + 4, bq1, bq0, acc, sx);
+    } else {
+        for (; step + 8 <= c.nsteps; step += 4) {
+            prefill_step<MT, 4>(c, stage0, stage3, step, bq0, bq3, acc, sx);
+            prefill_step<MT, 4>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+            prefill_step<MT, 4>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+            prefill_step<MT, 4>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
+        }
+        // The last one to seven steps.
+        prefill_step_tail<MT, 4>(c, stage0, stage3, step, bq0, bq3, acc, sx);
+        prefill_step_tail<MT, 4>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, 4>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+        prefill_step_tail<MT, 4>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
+        prefill_step_tail<MT, 4>(c, stage0, stage3, step + 4, bq0, bq3, acc, sx);
+        prefill_step_tail<MT, 4>(c, stage1, stage0, step + 5, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, 4>(c, stage2, stage1, step + 6, bq2, bq1, acc, sx);
     }
-    // The last one to five steps.
-    prefill_step_tail<MT>(c, stage0, stage2, step, bq0, bq2, acc, sx);
-    prefill_step_tail<MT>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-    prefill_step_tail<MT>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-    prefill_step_tail<MT>(c, stage0, stage2, step + 3, bq0, bq2, acc, sx);
-    prefill_step_tail<MT>(c, stage1, stage0, step + 4, bq1, bq0, acc, sx);
 
-    // Row sums: partials of (wave, lane group) -> one total per tile row.
+    // Row sums: partials of (wave, lane group) -> one total per tile row, and
+    // each row's dequant scale, computed once here rather than by every lane
+    // that stores a value of the row.
 #pragma unroll
     for (int i = 0; i < MT; ++i) rowsum_part[wave * 2 + c.lg][i * 32 + c.ln] = sx[i];
     __syncthreads();
@@ -334,13 +361,18 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
         int t = 0;
 #pragma unroll
         for (int w = 0; w < 8; ++w) t += rowsum_part[w][tid];
-        rowsum[tid] = t;
+        const int64_t m = m0 + tid;
+        rowinfo[tid] = make_float2(__int_as_float(t), m < M ? dequant_scale(p.eta[m], p.gamma) : 0.0f);
     }
     __syncthreads();
 
     // Epilogue: element 4j + q of tile (i, t) is row 32i + 8j + 4lg + q, column 32t + ln.
     if (!group_ok) return;
     const int ln = c.ln, lg = c.lg;
+    const int64_t n0 = group * 64 + ln;
+    const bool col0 = n0 < N, col1 = n0 + 32 < N;
+    float* ycol = p.y + m0 * N + n0;
+    int32_t* yicol = p.y_int ? p.y_int + m0 * N + n0 : nullptr;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -348,22 +380,26 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = i * 32 + j * 8 + lg * 4 + q;
-                const int64_t m = m0 + r;
-                if (m >= M) continue;
-                const float sc_m = dequant_scale(p.eta[m], p.gamma);
-                const int xs = rowsum[r];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int64_t n = group * 64 + t * 32 + ln;
-                    if (n >= N) continue;
-                    const int v = (int)((uint32_t)acc[i][t][j * 4 + q] - (uint32_t)xs);
-                    p.y[m * N + n] = dequant(v, sc_m);
-                    if (p.y_int) p.y_int[m * N + n] = v;
+                if (m0 + r >= M) continue;
+                const float2 ri = rowinfo[r];
+                const uint32_t xs = (uint32_t)__float_as_int(ri.x);
+                const int v0 = (int)((uint32_t)acc[i][0][j * 4 + q] - xs);
+                const int v1 = (int)((uint32_t)acc[i][1][j * 4 + q] - xs);
+                float* yr = ycol + (int64_t)r * N;
+                if (col0) yr[0] = dequant(v0, ri.y);
+                if (col1) yr[32] = dequant(v1, ri.y);
+                if (yicol) {
+                    int32_t* yir = yicol + (int64_t)r * N;
+                    if (col0) yir[0] = v0;
+                    if (col1) yir[32] = v1;
                 }
             }
         }
     }
 }
+
+// Stages of the LDS ring (steps in flight + 1).
+constexpr int kPrefillStages = 4;
 
 // Column tile width (output rows of W per workgroup) of the prefill kernel.
 static int gemm_bn(int64_t M) { (void)M; return kPreBN; }
@@ -380,17 +416,17 @@ static int prefill_mt(int64_t M, int64_t N) {
 static int dispatch(GemmArgs& a, int64_t ntn, bool grouped, hipStream_t stream) {
     const int64_t M = a.M;
     if (grouped) {   // grouped prefill keeps 128-row tiles (grid.y = row tiles)
-        hipLaunchKernelGGL((gemm_prefill_kernel<4, true>), dim3((unsigned)ntn, (unsigned)ceil_div(M, 128)),
+        hipLaunchKernelGGL((gemm_prefill_kernel<4, true, kPrefillStages>), dim3((unsigned)ntn, (unsigned)ceil_div(M, 128)),
                            dim3(256), 0, stream, a);
     } else {
         const int mt = prefill_mt(M, a.p.N);
         a.ntiles_n = ntn;
         a.ntiles_m = ceil_div(M, 32 * mt);
         if (mt == 2)
-            hipLaunchKernelGGL((gemm_prefill_kernel<2, false>), dim3((unsigned)(ntn * a.ntiles_m)),
+            hipLaunchKernelGGL((gemm_prefill_kernel<2, false, kPrefillStages>), dim3((unsigned)(ntn * a.ntiles_m)),
                                dim3(256), 0, stream, a);
         else
-            hipLaunchKernelGGL((gemm_prefill_kernel<4, false>), dim3((unsigned)(ntn * a.ntiles_m)),
+            hipLaunchKernelGGL((gemm_prefill_kernel<4, false, kPrefillStages>), dim3((unsigned)(ntn * a.ntiles_m)),
                                dim3(256), 0, stream, a);
     }
     BL_LAUNCH_CHECK();
