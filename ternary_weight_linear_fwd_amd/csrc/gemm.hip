@@ -385,13 +385,15 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
                 const uint32_t xs = (uint32_t)__float_as_int(ri.x);
                 const int v0 = (int)((uint32_t)acc[i][0][j * 4 + q] - xs);
                 const int v1 = (int)((uint32_t)acc[i][1][j * 4 + q] - xs);
+                // Non-temporal stores: y is not read again here, so it should
+                // not displace the operands from the caches.
                 float* yr = ycol + (int64_t)r * N;
-                if (col0) yr[0] = dequant(v0, ri.y);
-                if (col1) yr[32] = dequant(v1, ri.y);
+                if (col0) __builtin_nontemporal_store(dequant(v0, ri.y), yr);
+                if (col1) __builtin_nontemporal_store(dequant(v1, ri.y), yr + 32);
                 if (yicol) {
                     int32_t* yir = yicol + (int64_t)r * N;
-                    if (col0) yir[0] = v0;
-                    if (col1) yir[32] = v1;
+                    if (col0) __builtin_nontemporal_store(v0, yir);
+                    if (col1) __builtin_nontemporal_store(v1, yir + 32);
                 }
             }
         }
