@@ -93,7 +93,7 @@ def bench_prefill(torch, L, S, reps: int):
         L.bitlinear_quantize_act(xd, M, K, xq, eta)
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         fwd = lambda: L.bitlinear_forward(xq, eta, packed, g.value, M, N, K, y, None, ws, ws_bytes)
-        for _ in range(3):
+        for _ in range(30):   # a few ms of warm-up so that the clocks have settled
             fwd()
         ms = time_events(torch, fwd, reps)
         quant_ms = time_events(torch, lambda: L.bitlinear_quantize_act(xd, M, K, xq, eta), reps)
