@@ -35,6 +35,8 @@
 // than -1/0/+1 bytes, which lets the matrix cores hold a higher clock.  int32 arithmetic wraps, so the difference is exact whenever the
 // result fits (|y_int| <= 127 K < 2^31).
 // Epilogue: y = float(y_int) * ((eta[m] * gamma) / 127), fused.
+#include <atomic>
+
 #include "kernels.hpp"
 
 namespace bl {
@@ -95,20 +97,20 @@ __device__ __forceinline__ void dma_16(const void* src, void* lds_dst) {
                                  (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
-template <int MT>
+template <int MT, int NT>
 struct PrefillCtx {
     static constexpr int BM = 32 * MT;            // token rows per workgroup tile
     static constexpr int AStage = BM * 128;       // bytes of A per stage
     static constexpr int NA = AStage / 4096;      // A DMA instructions per wave per step
-    static constexpr int Ops = NA + 2;            // + two weight loads: vector memory instructions per step
+    static constexpr int Ops = NA + NT;           // + NT weight loads: vector memory instructions per step
     // DMA sources are a wave-uniform base (scalar registers) plus a 32-bit
     // per-lane offset, so that the main loop spends no vector ALU work on
     // addresses (row offsets stay below 2^32 since K <= 2^24).
     const int8_t* abase;    // the tile's first activation row
     uint32_t aoff[NA];      // (row in the tile, clamped below M) * K + byte column
     uint32_t acol[NA];      // byte column inside the 128-k step
-    const uint8_t* bbase;   // k-block 0 of the wavefront's 64-row weight group
-    uint32_t boff;          // lane (ln, lg): row ln's 16 bytes of k-block lg of a step
+    const uint8_t* bbase[NT];   // k-block 0 of the 32 weight rows of the wavefront's column tile t
+    uint32_t boff;              // lane (ln, lg): row ln's 16 bytes of k-block lg of a step
     uint32_t afrag[4];      // LDS offset of this lane's A fragment of group d, row tile 0
     uint32_t sxfrag;        // afrag[wave]: the word group this wavefront sums
     int64_t K, Kb, nsteps;
@@ -120,9 +122,10 @@ struct PrefillCtx {
 // the wavefront, so they skip LDS).  CHECKED: the step may reach past K (the
 // last step, or one queued past the end), so addresses are clamped in
 // bounds; otherwise all 128 k of the step lie inside K.
-template <int MT, bool CHECKED>
-__device__ __forceinline__ void prefill_issue(const PrefillCtx<MT>& c, uint8_t* st, int64_t step, v4i (&bq)[2]) {
-    using Ctx = PrefillCtx<MT>;
+template <int MT, int NT, bool CHECKED>
+__device__ __forceinline__ void prefill_issue(const PrefillCtx<MT, NT>& c, uint8_t* st, int64_t step, v4i (&bq)[NT]) {
+    using Ctx = PrefillCtx<MT, NT>;
+    if constexpr (MT * NT > 4) __builtin_amdgcn_sched_barrier(0);
     const int64_t kbase = step * 128;
 #pragma unroll
     for (int j = 0; j < Ctx::NA; ++j) {
@@ -136,30 +139,41 @@ __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT>& c, uint8_t* 
         }
         dma_16(src, st + (j * 4 + c.wave) * 1024);
     }
-    // Lane (ln, lg) takes rows ln and ln + 32 of k-block 2 * step + lg.
-    const uint8_t* bsrc;
-    if constexpr (CHECKED) {
-        const int64_t kb = step * 2 + c.lg < c.Kb ? step * 2 + c.lg : c.Kb - 1;   // past the end: replaced at use
-        bsrc = c.bbase + (uint32_t)(kb * 1024 + (c.boff & 1023u));
-    } else {
-        bsrc = (c.bbase + step * 2048) + c.boff;
+    // Lane (ln, lg) takes row ln of each column tile's 32 rows in k-block
+    // 2 * step + lg.
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const uint8_t* bsrc;
+        if constexpr (CHECKED) {
+            const int64_t kb = step * 2 + c.lg < c.Kb ? step * 2 + c.lg : c.Kb - 1;   // past the end: replaced at use
+            bsrc = c.bbase[t] + (uint32_t)(kb * 1024 + (c.boff & 1023u));
+        } else {
+            bsrc = (c.bbase[t] + step * 2048) + c.boff;
+        }
+        bq[t] = *reinterpret_cast<const v4i*>(bsrc);
     }
-    bq[0] = *reinterpret_cast<const v4i*>(bsrc);
-    bq[1] = *reinterpret_cast<const v4i*>(bsrc + 512);
+    // The explicit vmcnt waits count on each step's loads being issued as one
+    // group, in step order.  Under the register pressure of the wide tile the
+    // scheduler otherwise interleaves the groups (and then waits for
+    // everything); the smaller tile keeps them in order by itself and runs
+    // faster without the fence.
+    if constexpr (MT * NT > 4) __builtin_amdgcn_sched_barrier(0);
 }
 
 // One K-step of MFMAs from the LDS stage at A.  Wavefront w also adds word
 // group w of the step's A rows into the row sums `sx` (one extra fragment
 // read per row tile, four v_dot4 each).  TAIL: the step may be the last one,
 // whose second k-block can lie past the end.
-template <int MT, bool TAIL>
-__device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, const uint8_t* A, int64_t step,
-                                                const v4i (&bq)[2], v16i (&acc)[MT][2], int (&sx)[MT]) {
-    v4i bw[2] = {bq[0], bq[1]};
+template <int MT, int NT, bool TAIL>
+__device__ __forceinline__ void prefill_compute(const PrefillCtx<MT, NT>& c, const uint8_t* A, int64_t step,
+                                                const v4i (&bq)[NT], v16i (&acc)[MT][NT], int (&sx)[MT]) {
+    v4i bw[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) bw[t] = bq[t];
     if constexpr (TAIL) {
         if (step * 2 + 1 >= c.Kb && c.lg == 1) {   // k-block past the end: code 01
 #pragma unroll
-            for (int t = 0; t < 2; ++t) bw[t] = v4i{0x55555555, 0x55555555, 0x55555555, 0x55555555};
+            for (int t = 0; t < NT; ++t) bw[t] = v4i{0x55555555, 0x55555555, 0x55555555, 0x55555555};
         }
     }
     // Row 32i + ln, chunk ((lg & 1) * 4 + d) ^ ((row >> 1) & 7): the swizzle
@@ -181,14 +195,14 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, const u
     }
     // Two register sets for the A fragments and the B codes: group d+1's LDS
     // reads and field extraction run while group d's MFMAs execute.
-    v4i af[2][MT], bf[2][2];
+    v4i af[2][MT], bf[2][NT];
     auto load_a = [&](v4i (&dst)[MT], int d) {
 #pragma unroll
         for (int i = 0; i < MT; ++i) dst[i] = a_frag(i, d);
     };
-    auto fields = [&](v4i (&dst)[2], int d) {
+    auto fields = [&](v4i (&dst)[NT], int d) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NT; ++t) {
             const uint32_t w = (uint32_t)bw[t][d];
             dst[t].x = (int)(w & 0x03030303u);
             dst[t].y = (int)((w >> 2) & 0x03030303u);
@@ -197,18 +211,32 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, const u
         }
     };
     load_a(af[0], 0);
-    fields(bf[0], 0);
+    if constexpr (MT * NT <= 4) fields(bf[0], 0);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const int cur = d & 1;
         if (d < 3) load_a(af[cur ^ 1], d + 1);
         __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of this group's MFMAs
+        if constexpr (MT * NT <= 4) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int i = 0; i < MT; ++i)
-                acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][t], acc[i][t], 0, 0, 0);
-        if (d < 3) fields(bf[cur ^ 1], d + 1);
+                for (int i = 0; i < MT; ++i)
+                    acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][t], acc[i][t], 0, 0, 0);
+            if (d < 3) fields(bf[cur ^ 1], d + 1);
+        } else {
+            // Wide tiles: one set of expanded codes (register budget); each
+            // weight word's fields are taken just before their MT MFMAs.
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const uint32_t w = (uint32_t)bw[t][d];
+                const v4i f = v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u),
+                                  (int)((w >> 4) & 0x03030303u), (int)((w >> 6) & 0x03030303u)};
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+                    acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], f, acc[i][t], 0, 0, 0);
+            }
+        }
     }
 }
 
@@ -218,36 +246,39 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT>& c, const u
 // is past it) with step + NS - 1, compute.  Straight-line code, so that the
 // compiler can see which stage each LDS read and each load in flight touch
 // and adds no waits of its own.
-template <int MT, int NS>
-__device__ __forceinline__ void prefill_step(const PrefillCtx<MT>& c, const uint8_t* cur, uint8_t* refill,
-                                             int64_t step, const v4i (&bq_cur)[2], v4i (&bq_refill)[2],
-                                             v16i (&acc)[MT][2], int (&sx)[MT]) {
-    wait_vmcnt<(NS - 2) * PrefillCtx<MT>::Ops>();
+template <int MT, int NT, int NS>
+__device__ __forceinline__ void prefill_step(const PrefillCtx<MT, NT>& c, const uint8_t* cur, uint8_t* refill,
+                                             int64_t step, const v4i (&bq_cur)[NT], v4i (&bq_refill)[NT],
+                                             v16i (&acc)[MT][NT], int (&sx)[MT]) {
+    wait_vmcnt<(NS - 2) * PrefillCtx<MT, NT>::Ops>();
     __builtin_amdgcn_s_barrier();   // not __syncthreads(): that would drain the loads in flight
-    prefill_issue<MT, false>(c, refill, step + NS - 1, bq_refill);   // <= nsteps - 2: never the last
-    prefill_compute<MT, false>(c, cur, step, bq_cur, acc, sx);
+    prefill_issue<MT, NT, false>(c, refill, step + NS - 1, bq_refill);   // <= nsteps - 2: never the last
+    prefill_compute<MT, NT, false>(c, cur, step, bq_cur, acc, sx);
 }
 
 // Any step, including the last ones (nothing left to refill, or past the end).
-template <int MT, int NS>
-__device__ __forceinline__ void prefill_step_tail(const PrefillCtx<MT>& c, const uint8_t* cur, uint8_t* refill,
-                                                  int64_t step, const v4i (&bq_cur)[2], v4i (&bq_refill)[2],
-                                                  v16i (&acc)[MT][2], int (&sx)[MT]) {
-    constexpr int Ops = PrefillCtx<MT>::Ops;
+template <int MT, int NT, int NS>
+__device__ __forceinline__ void prefill_step_tail(const PrefillCtx<MT, NT>& c, const uint8_t* cur, uint8_t* refill,
+                                                  int64_t step, const v4i (&bq_cur)[NT], v4i (&bq_refill)[NT],
+                                                  v16i (&acc)[MT][NT], int (&sx)[MT]) {
+    constexpr int Ops = PrefillCtx<MT, NT>::Ops;
     if (step >= c.nsteps) return;
     const int64_t later = c.nsteps - 1 - step;   // queued steps after this one
     if (NS >= 4 && later >= 2) wait_vmcnt<(NS >= 4 ? 2 : 1) * Ops>();
     else if (later >= 1) wait_vmcnt<Ops>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (step + NS - 1 < c.nsteps) prefill_issue<MT, true>(c, refill, step + NS - 1, bq_refill);
-    prefill_compute<MT, true>(c, cur, step, bq_cur, acc, sx);
+    if (step + NS - 1 < c.nsteps) prefill_issue<MT, NT, true>(c, refill, step + NS - 1, bq_refill);
+    prefill_compute<MT, NT, true>(c, cur, step, bq_cur, acc, sx);
 }
 
-template <int MT, bool GROUPED, int NS>
-__global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefill_kernel(GemmArgs a) {
+// Resident workgroups per CU for an MT x NT wave tile (register budget).
+constexpr int prefill_occupancy(int mt, int nt) { return mt * nt <= 2 ? 4 : mt * nt <= 4 ? 3 : 2; }
+
+template <int MT, int NT, bool GROUPED, int NS>
+__global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_kernel(GemmArgs a) {
     static_assert(NS == 3 || NS == 4, "ring of three or four stages");
-    using Ctx = PrefillCtx<MT>;
+    using Ctx = PrefillCtx<MT, NT>;
     constexpr int BM = Ctx::BM;
     // Three stages, each its own LDS object, so that the compiler can tell a
     // read of one stage from the loads in flight into the others.
@@ -274,8 +305,10 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
     }
     const int64_t M = a.M, N = p.N, K = p.K, Kb = p.Kb;
     const int64_t m0 = tile_m * BM;
-    const int64_t group = tile_n * 4 + wave;
-    const bool group_ok = group < ceil_div(N, 64);
+    // Column tile t of this wavefront: 32-column block cb0 + t, the rows
+    // 32 * (cb & 1) .. + 31 of 64-row weight group cb / 2.
+    const int64_t cb0 = tile_n * (4 * NT) + (int64_t)wave * NT;
+    const bool group_ok = cb0 * 32 < N;   // any of the wavefront's columns inside N
 
     Ctx c;
     c.K = K;
@@ -294,20 +327,25 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
         const int64_t rr = m0 + r < M ? r : M - 1 - m0;
         c.aoff[j] = (uint32_t)(rr * K) + c.acol[j];
     }
-    c.bbase = reinterpret_cast<const uint8_t*>(p.packed) + (group_ok ? group : 0) * Kb * 1024;
+    const int64_t ngroups = ceil_div(N, 64);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int64_t cb = cb0 + t, g = cb >> 1;
+        c.bbase[t] = reinterpret_cast<const uint8_t*>(p.packed) + (g < ngroups ? g : 0) * Kb * 1024 + (cb & 1) * 512;
+    }
     c.boff = (uint32_t)(c.lg * 1024 + c.ln * 16);
 #pragma unroll
     for (int d = 0; d < 4; ++d)
         c.afrag[d] = (uint32_t)((c.ln & 31) * 128 + ((((c.lg & 1) * 4 + d) ^ ((c.ln >> 1) & 7)) << 4));
     c.sxfrag = (uint32_t)((c.ln & 31) * 128 + ((((c.lg & 1) * 4 + (wave & 3)) ^ ((c.ln >> 1) & 7)) << 4));
 
-    v16i acc[MT][2];
+    v16i acc[MT][NT];
     int sx[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
         sx[i] = 0;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][t][e] = 0;
     }
@@ -316,39 +354,39 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
     // in-bounds addresses and are never used), so that no branch precedes the
     // main loop.  Weight words of the steps in flight: one register set per
     // stage.
-    v4i bq0[2], bq1[2], bq2[2], bq3[2];
-    prefill_issue<MT, true>(c, stage0, 0, bq0);
-    prefill_issue<MT, true>(c, stage1, 1, bq1);
-    if constexpr (NS == 4) prefill_issue<MT, true>(c, stage2, 2, bq2);
+    v4i bq0[NT], bq1[NT], bq2[NT], bq3[NT];
+    prefill_issue<MT, NT, true>(c, stage0, 0, bq0);
+    prefill_issue<MT, NT, true>(c, stage1, 1, bq1);
+    if constexpr (NS == 4) prefill_issue<MT, NT, true>(c, stage2, 2, bq2);
     int64_t step = 0;
     if constexpr (NS == 3) {
         // The main loop queues steps up to nsteps - 2, all of them whole.
         for (; step + 6 <= c.nsteps; step += 3) {
-            prefill_step<MT, 3>(c, stage0, stage2, step, bq0, bq2, acc, sx);
-            prefill_step<MT, 3>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-            prefill_step<MT, 3>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+            prefill_step<MT, NT, 3>(c, stage0, stage2, step, bq0, bq2, acc, sx);
+            prefill_step<MT, NT, 3>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+            prefill_step<MT, NT, 3>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
         }
         // The last one to five steps.
-        prefill_step_tail<MT, 3>(c, stage0, stage2, step, bq0, bq2, acc, sx);
-        prefill_step_tail<MT, 3>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-        prefill_step_tail<MT, 3>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-        prefill_step_tail<MT, 3>(c, stage0, stage2, step + 3, bq0, bq2, acc, sx);
-        prefill_step_tail<MT, 3>(c, stage1, stage0, step + 4, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 3>(c, stage0, stage2, step, bq0, bq2, acc, sx);
+        prefill_step_tail<MT, NT, 3>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 3>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+        prefill_step_tail<MT, NT, 3>(c, stage0, stage2, step + 3, bq0, bq2, acc, sx);
+        prefill_step_tail<MT, NT, 3>(c, stage1, stage0, step + 4, bq1, bq0, acc, sx);
     } else {
         for (; step + 8 <= c.nsteps; step += 4) {
-            prefill_step<MT, 4>(c, stage0, stage3, step, bq0, bq3, acc, sx);
-            prefill_step<MT, 4>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-            prefill_step<MT, 4>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-            prefill_step<MT, 4>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
+            prefill_step<MT, NT, 4>(c, stage0, stage3, step, bq0, bq3, acc, sx);
+            prefill_step<MT, NT, 4>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+            prefill_step<MT, NT, 4>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+            prefill_step<MT, NT, 4>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
         }
         // The last one to seven steps.
-        prefill_step_tail<MT, 4>(c, stage0, stage3, step, bq0, bq3, acc, sx);
-        prefill_step_tail<MT, 4>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-        prefill_step_tail<MT, 4>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-        prefill_step_tail<MT, 4>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
-        prefill_step_tail<MT, 4>(c, stage0, stage3, step + 4, bq0, bq3, acc, sx);
-        prefill_step_tail<MT, 4>(c, stage1, stage0, step + 5, bq1, bq0, acc, sx);
-        prefill_step_tail<MT, 4>(c, stage2, stage1, step + 6, bq2, bq1, acc, sx);
+        prefill_step_tail<MT, NT, 4>(c, stage0, stage3, step, bq0, bq3, acc, sx);
+        prefill_step_tail<MT, NT, 4>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 4>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+        prefill_step_tail<MT, NT, 4>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
+        prefill_step_tail<MT, NT, 4>(c, stage0, stage3, step + 4, bq0, bq3, acc, sx);
+        prefill_step_tail<MT, NT, 4>(c, stage1, stage0, step + 5, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 4>(c, stage2, stage1, step + 6, bq2, bq1, acc, sx);
     }
 
     // Row sums: partials of (wave, lane group) -> one total per tile row, and
@@ -369,10 +407,13 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
     // Epilogue: element 4j + q of tile (i, t) is row 32i + 8j + 4lg + q, column 32t + ln.
     if (!group_ok) return;
     const int ln = c.ln, lg = c.lg;
-    const int64_t n0 = group * 64 + ln;
-    const bool col0 = n0 < N, col1 = n0 + 32 < N;
+    const int64_t n0 = cb0 * 32 + ln;
+    bool col[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) col[t] = n0 + 32 * t < N;
+    // Non-temporal stores: y is not read again here, so it should not
+    // displace the operands from the caches.
     float* ycol = p.y + m0 * N + n0;
-    int32_t* yicol = p.y_int ? p.y_int + m0 * N + n0 : nullptr;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -383,75 +424,119 @@ __global__ __launch_bounds__(256, MT == 1 ? 4 : MT == 2 ? 3 : 2) void gemm_prefi
                 if (m0 + r >= M) continue;
                 const float2 ri = rowinfo[r];
                 const uint32_t xs = (uint32_t)__float_as_int(ri.x);
-                const int v0 = (int)((uint32_t)acc[i][0][j * 4 + q] - xs);
-                const int v1 = (int)((uint32_t)acc[i][1][j * 4 + q] - xs);
-                // Non-temporal stores: y is not read again here, so it should
-                // not displace the operands from the caches.
                 float* yr = ycol + (int64_t)r * N;
-                if (col0) __builtin_nontemporal_store(dequant(v0, ri.y), yr);
-                if (col1) __builtin_nontemporal_store(dequant(v1, ri.y), yr + 32);
-                if (yicol) {
-                    int32_t* yir = yicol + (int64_t)r * N;
-                    if (col0) __builtin_nontemporal_store(v0, yir);
-                    if (col1) __builtin_nontemporal_store(v1, yir + 32);
-                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    if (col[t])
+                        __builtin_nontemporal_store(dequant((int)((uint32_t)acc[i][t][j * 4 + q] - xs), ri.y),
+                                                    yr + 32 * t);
+            }
+        }
+    }
+    if (!p.y_int) return;
+    int32_t* yicol = p.y_int + m0 * N + n0;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = i * 32 + j * 8 + lg * 4 + q;
+                if (m0 + r >= M) continue;
+                const uint32_t xs = (uint32_t)__float_as_int(rowinfo[r].x);
+                int32_t* yir = yicol + (int64_t)r * N;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    if (col[t]) __builtin_nontemporal_store((int)((uint32_t)acc[i][t][j * 4 + q] - xs), yir + 32 * t);
             }
         }
     }
 }
 
-// Stages of the LDS ring (steps in flight + 1).
-constexpr int kPrefillStages = 4;
+// Stages of the LDS ring (steps in flight + 1); the 3 x 3 wave tile keeps
+// three, so that its weight-word ring fits the register budget.
+constexpr int prefill_stages(int mt, int nt) { return mt * nt > 4 ? 3 : 4; }
 
-// Column tile width (output rows of W per workgroup) of the prefill kernel.
+// Column tile of the grouped prefill launch (output rows of W per workgroup).
 static int gemm_bn(int64_t M) { (void)M; return kPreBN; }
 
-// Prefill tile height.  64-row tiles (158 VGPRs, 32 KB LDS: three workgroups
-// per CU, 768 slots on 256 CUs) balance far better at prefill sizes such as
-// M = 2048; 128-row tiles (two per CU) reuse each expanded weight word twice
-// as often and only pay off once the grid is many rounds deep.
-static int prefill_mt(int64_t M, int64_t N) {
-    const int64_t t64 = ceil_div(M, 64) * ceil_div(N, kPreBN);
-    return t64 <= 4 * 768 ? 2 : 4;
+// Wave tile of a single prefill launch.  Each SIMD runs one wavefront of
+// every tile its CU holds, so the time goes as the most tiles any CU gets
+// times the MFMA work of one wavefront's tile: ceil(T / CUs) * MT * NT.  Ties
+// go to the smaller tile (more resident wavefronts to hide latency), except
+// on grids four or more rounds deep, where 128 x 256 tiles (each weight word
+// expanded for twice the rows) measure faster.  E.g. on 256 CUs: M = 2048,
+// N = 8640 takes 96 x 384 tiles (506 in one round) over 64 x 256 ones (1088:
+// up to five per CU); M = 2048, N = 3200 keeps 64 x 256.
+struct TileCfg {
+    int mt, nt;
+};
+
+static TileCfg prefill_tile(int64_t M, int64_t N, int cus) {
+    auto rounds = [&](TileCfg t) { return ceil_div(ceil_div(M, 32 * t.mt) * ceil_div(N, 128 * t.nt), cus); };
+    const TileCfg small{2, 2}, wide{3, 3}, tall{4, 2};
+    TileCfg best = small;
+    int64_t best_cost = rounds(small) * 4;
+    if (rounds(wide) * 9 < best_cost) {
+        best = wide;
+        best_cost = rounds(wide) * 9;
+    }
+    const int64_t rt = rounds(tall);
+    if (rt * 8 < best_cost || (rt * 8 == best_cost && rt >= 4)) best = tall;
+    return best;
 }
 
-static int dispatch(GemmArgs& a, int64_t ntn, bool grouped, hipStream_t stream) {
-    const int64_t M = a.M;
-    if (grouped) {   // grouped prefill keeps 128-row tiles (grid.y = row tiles)
-        hipLaunchKernelGGL((gemm_prefill_kernel<4, true, kPrefillStages>), dim3((unsigned)ntn, (unsigned)ceil_div(M, 128)),
-                           dim3(256), 0, stream, a);
-    } else {
-        const int mt = prefill_mt(M, a.p.N);
-        a.ntiles_n = ntn;
-        a.ntiles_m = ceil_div(M, 32 * mt);
-        if (mt == 2)
-            hipLaunchKernelGGL((gemm_prefill_kernel<2, false, kPrefillStages>), dim3((unsigned)(ntn * a.ntiles_m)),
-                               dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL((gemm_prefill_kernel<4, false, kPrefillStages>), dim3((unsigned)(ntn * a.ntiles_m)),
-                               dim3(256), 0, stream, a);
+// CUs of the current device, asked of the runtime once per device (the
+// query costs more host time than a short prefill launch can hide).
+static int device_cus() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
     }
-    BL_LAUNCH_CHECK();
-    return BITLINEAR_OK;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+template <int MT, int NT>
+static void launch_single(GemmArgs& a, hipStream_t stream) {
+    a.ntiles_m = ceil_div(a.M, 32 * MT);
+    a.ntiles_n = ceil_div(a.p.N, 128 * NT);
+    hipLaunchKernelGGL((gemm_prefill_kernel<MT, NT, false, prefill_stages(MT, NT)>), dim3((unsigned)(a.ntiles_m * a.ntiles_n)),
+                       dim3(256), 0, stream, a);
 }
 
 int launch_gemm(const Problem& p, int64_t M, hipStream_t stream) {
     GemmArgs a{};
     a.p = p;
     a.M = M;
-    const int64_t ntn = ceil_div(p.N, gemm_bn(M));
-    return dispatch(a, ntn, false, stream);
+    const TileCfg t = prefill_tile(M, p.N, device_cus());
+    if (t.mt == 3) launch_single<3, 3>(a, stream);
+    else if (t.mt == 4) launch_single<4, 2>(a, stream);
+    else launch_single<2, 2>(a, stream);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
 }
 
 int gemm_tile_n(int64_t M) { return gemm_bn(M); }
 
 int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
                         hipStream_t stream) {
+    // Grouped prefill keeps 128 x 256 tiles (grid.y = row tiles).
     GemmArgs a{};
     a.problems = problems;
     a.units = units;
     a.M = M;
-    return dispatch(a, nunits, true, stream);
+    hipLaunchKernelGGL((gemm_prefill_kernel<4, 2, true, prefill_stages(4, 2)>), dim3((unsigned)nunits, (unsigned)ceil_div(M, 128)),
+                       dim3(256), 0, stream, a);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
 }
 
 }  // namespace bl

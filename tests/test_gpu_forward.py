@@ -96,12 +96,20 @@ def test_determinism():
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
 
 
-# Shapes with more than 3072 tiles of 64 x 256 select the 128-row prefill
-# variant (smaller ones take 64-row tiles); both with ragged M, N and K.
+# Prefill grids many rounds deep (thousands of tiles), with ragged M, N and K;
+# on a 256-CU chip (1000, 32700) takes 128 x 256 tiles, the others 64 x 256.
 @pytest.mark.parametrize("M,N,K", [(130, 33000, 80), (257, 32832, 208), (200, 65600, 48),
-                                   (1000, 200000, 32), (1537, 131136, 16)])
+                                   (1000, 200000, 32), (1537, 131136, 16), (1000, 32700, 208)])
 def test_prefill_tall_tiles(M, N, K):
     run_case(M, N, K, seed=M + N + K, latent=False)
+
+
+# Shapes for which the prefill launch picks 96 x 384 tiles (3 x 3 MFMA tiles
+# per wavefront) on a 256-CU chip: M not a multiple of 96, N not a multiple of
+# 384 or of 32, K with partial and odd last blocks.
+@pytest.mark.parametrize("M,N,K", [(772, 10000, 1040), (1927, 4100, 208), (2949, 2600, 80)])
+def test_prefill_wide_tiles(M, N, K):
+    run_case(M, N, K, seed=M * 3 + N + K, latent=False)
 
 
 
