@@ -125,7 +125,7 @@ struct PrefillCtx {
 template <int MT, int NT, bool CHECKED>
 __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT, NT>& c, uint8_t* st, int64_t step, v4i (&bq)[NT]) {
     using Ctx = PrefillCtx<MT, NT>;
-    if constexpr (MT * NT > 4) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NT == 3) __builtin_amdgcn_sched_barrier(0);
     const int64_t kbase = step * 128;
 #pragma unroll
     for (int j = 0; j < Ctx::NA; ++j) {
@@ -153,11 +153,11 @@ __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT, NT>& c, uint8
         bq[t] = *reinterpret_cast<const v4i*>(bsrc);
     }
     // The explicit vmcnt waits count on each step's loads being issued as one
-    // group, in step order.  Under the register pressure of the wide tile the
-    // scheduler otherwise interleaves the groups (and then waits for
-    // everything); the smaller tile keeps them in order by itself and runs
+    // group, in step order.  Under the register pressure of the 96 x 384 tile
+    // the scheduler otherwise interleaves the groups (and then waits for
+    // everything); the other tiles keep them in order by themselves and run
     // faster without the fence.
-    if constexpr (MT * NT > 4) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NT == 3) __builtin_amdgcn_sched_barrier(0);
 }
 
 // One K-step of MFMAs from the LDS stage at A.  Wavefront w also adds word
@@ -453,9 +453,10 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     }
 }
 
-// Stages of the LDS ring (steps in flight + 1); the 3 x 3 wave tile keeps
-// three, so that its weight-word ring fits the register budget.
-constexpr int prefill_stages(int mt, int nt) { return mt * nt > 4 ? 3 : 4; }
+// Stages of the LDS ring (steps in flight + 1), as measured fastest: three,
+// and four for 128 x 256 tiles, whose longer steps give fewer wavefronts per
+// SIMD more to hide.
+constexpr int prefill_stages(int mt, int nt) { return mt == 4 ? 4 : 3; }
 
 // Column tile of the grouped prefill launch (output rows of W per workgroup).
 static int gemm_bn(int64_t M) { (void)M; return kPreBN; }
