@@ -15,8 +15,10 @@ Also reported:
                 quantize stage precomputed), timed with HIP events on the
                 stream it runs on, against 8 TB/s HBM3E.
   prefill       the 3B-shaped prefill GEMMs (M = 2048: 3200->8640 and
-                8640->3200) on pre-quantized activations, int8 TOP/s against
-                the 5.0 POP/s dense int8 MFMA peak.
+                8640->3200) on pre-quantized activations with the row sums
+                the quantizer writes (as the fused forward runs them), int8
+                TOP/s against the 5.0 POP/s dense int8 MFMA peak; also the
+                same contraction summing the rows itself and the quantizer.
   decode_m16    the same sweep at M = 16 tokens.
   cpu_baseline  the CPU oracle (plain C, all host threads) on a bounded
                 sample of the same sweep (the first layers at M = 1).
@@ -90,14 +92,19 @@ def bench_prefill(torch, L, S, reps: int):
         L.bitlinear_pack_weights(Wd, N, K, packed, None, g, ws, ws_bytes)
         xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
         eta = torch.empty(M, dtype=torch.float32, device="cuda")
-        L.bitlinear_quantize_act(xd, M, K, xq, eta)
+        xsum = torch.empty(M, dtype=torch.int32, device="cuda")
+        L.bitlinear_quantize_act(xd, M, K, xq, eta, xsum)
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         # Device addresses and the stream resolved once, outside the timed
         # loop, so that host-side argument handling does not open gaps
-        # between launches of a ~60 us kernel.
+        # between launches of a ~50 us kernel.
         st = torch.cuda.current_stream().cuda_stream
-        a = [t.data_ptr() for t in (xq, eta, packed, y, ws, xd)]
-        fwd = lambda: L.bitlinear_forward(a[0], a[1], a[2], g.value, M, N, K, a[3], None, a[4], ws_bytes, st)
+        a = [t.data_ptr() for t in (xq, eta, packed, y, ws, xd, xsum)]
+        # The contraction as the fused forward runs it: row sums from the
+        # quantizer (timed with them below).
+        fwd = lambda: L.bitlinear_forward_xsum(a[0], a[1], a[6], a[2], g.value, M, N, K, a[3], None, a[4],
+                                               ws_bytes, st)
+        fwd_own = lambda: L.bitlinear_forward(a[0], a[1], a[2], g.value, M, N, K, a[3], None, a[4], ws_bytes, st)
         # Warm-up by time: the first few hundred launches of a process run at
         # lower clocks than the steady state.
         t_end = time.perf_counter() + 0.2
@@ -106,13 +113,15 @@ def bench_prefill(torch, L, S, reps: int):
                 fwd()
             torch.cuda.synchronize()
         ms = time_events(torch, fwd, reps)
-        quant_ms = time_events(torch, lambda: L.bitlinear_quantize_act(a[5], M, K, a[0], a[1], None, st), reps)
+        own_ms = time_events(torch, fwd_own, reps)
+        quant_ms = time_events(torch, lambda: L.bitlinear_quantize_act(a[5], M, K, a[0], a[1], a[6], st), reps)
         ops = 2 * M * N * K
         tops = ops / (ms * 1e-3) / 1e12
         out.append({"gemm": f"M={M} K={K} N={N}", "us": round(ms * 1e3, 2),
                     "tops": round(tops, 1), "frac": round(tops / INT8_PEAK_TOPS, 4),
-                    "quantize_us": round(quant_ms * 1e3, 2)})
-        del Wd, xd, packed, ws, xq, eta, y
+                    "quantize_us": round(quant_ms * 1e3, 2),
+                    "us_own_row_sums": round(own_ms * 1e3, 2)})
+        del Wd, xd, packed, ws, xq, eta, y, xsum
     return out
 
 
@@ -383,7 +392,8 @@ def main() -> int:
     if not args.no_prefill and not args.profile_run:
         prefill = bench_prefill(torch, L, S, max(10, args.steps))
         for r in prefill:
-            log(f"prefill {r['gemm']}: {r['us']} us, {r['tops']} TOP/s ({r['frac']:.1%})")
+            log(f"prefill {r['gemm']}: {r['us']} us, {r['tops']} TOP/s ({r['frac']:.1%}); "
+                f"own row sums {r['us_own_row_sums']} us; quantize {r['quantize_us']} us")
     sw = DecodeSweep(layers=args.layers, Ms=Ms, progress=log)
     log(f"packed weights resident: {sw.weight_bytes() / 1e9:.3f} GB")
     if args.profile_run:

@@ -192,8 +192,27 @@ int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed,
                       size_t ws_bytes, void* stream);
 
 /*
- * Fused forward from float32 activations: quantize (into the workspace),
- * contract, dequantize.  Same arguments as above; ws is required.
+ * bitlinear_forward with the activation row sums supplied: the same result,
+ * bit for bit, when xsum is right.  The prefill contraction (M > 64) of
+ * [P2] "3. Additive Integer Accumulation" runs on the stored weight codes
+ * c = w + 1 in {0, 1, 2}: sum_k xq w = sum_k xq c - sum_k xq, so it needs
+ * each row's sum; the quantizer produces those sums in the same pass that
+ * writes xq, and passing them on spares the contraction summing its
+ * activation tiles again.
+ *   xsum [M] int32 (in): xsum[m] = sum over k < K of xq[m][k], exactly as
+ *        bitlinear_quantize_act or bitlinear_rmsnorm_quantize_act write it.
+ *        Not checked: a wrong row sum shifts that row's y_int by the error.
+ *        The decode kernels (M <= 64) do not read it.
+ *   other arguments, workspace and errors as bitlinear_forward.
+ */
+int bitlinear_forward_xsum(const int8_t* xq, const float* eta, const int32_t* xsum,
+                           const uint8_t* packed, float gamma, int64_t M, int64_t N, int64_t K,
+                           float* y, int32_t* y_int, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fused forward from float32 activations: quantize (into the workspace, with
+ * the row sums for bitlinear_forward_xsum), contract, dequantize.  Same
+ * arguments as above; ws is required.
  * [P1] BitLinear158.forward steps 2, 4 and 5.
  */
 int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, int64_t M,

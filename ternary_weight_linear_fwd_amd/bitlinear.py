@@ -68,6 +68,8 @@ _SIGS = {
     "bitlinear_pack_ternary": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "bitlinear_unpack_weights": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "bitlinear_forward": ([_P, _P, _P, _F, _I64, _I64, _I64, _P, _P, _P, _SZ, _P], ctypes.c_int),
+    "bitlinear_forward_xsum": ([_P, _P, _P, _P, _F, _I64, _I64, _I64, _P, _P, _P, _SZ, _P],
+                               ctypes.c_int),
     "bitlinear_forward_f32": ([_P, _P, _F, _I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
     "bitlinear_forward_rmsnorm_f32": ([_P, _P, _F, _I64, _I64, _I64, _P, _P, _SZ, _P],
                                       ctypes.c_int),
@@ -174,6 +176,14 @@ def bitlinear_forward(xq, eta, packed, gamma: float, M: int, N: int, K: int, y, 
     _check(_lib.bitlinear_forward(_ptr(xq), _ptr(eta), _ptr(packed), float(gamma), M, N, K,
                                   _ptr(y), _ptr(y_int), _ptr(ws), ws_bytes, _stream(stream)),
            "bitlinear_forward")
+
+
+def bitlinear_forward_xsum(xq, eta, xsum, packed, gamma: float, M: int, N: int, K: int, y,
+                           y_int=None, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check(_lib.bitlinear_forward_xsum(_ptr(xq), _ptr(eta), _ptr(xsum), _ptr(packed),
+                                       float(gamma), M, N, K, _ptr(y), _ptr(y_int), _ptr(ws),
+                                       ws_bytes, _stream(stream)),
+           "bitlinear_forward_xsum")
 
 
 def bitlinear_forward_f32(x, packed, gamma: float, M: int, N: int, K: int, y, ws,

@@ -9,6 +9,7 @@
 #include <map>
 #include <vector>
 
+#include "gemm.hpp"
 #include "kernels.hpp"
 #include "lut.hpp"
 #include "median.hpp"
@@ -67,13 +68,31 @@ Problem make_problem(const int8_t* xq, const float* eta, const uint8_t* packed, 
     return p;
 }
 
-int run_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma, int64_t M,
-                int64_t N, int64_t K, float* y, int32_t* y_int, void* ws, hipStream_t stream) {
+// xsum (may be null): the activation row sums, read by the prefill kernel
+// in place of its own; the decode kernels sum their slices themselves.
+int run_forward(const int8_t* xq, const float* eta, const int32_t* xsum, const uint8_t* packed,
+                float gamma, int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,
+                hipStream_t stream) {
     if (M == 0) return BITLINEAR_OK;
     const Problem p = make_problem(xq, eta, packed, gamma, N, K, y, y_int);
     if (M <= kGemvMaxM) return launch_gemv(p, M, ws, stream);
     if (M <= kSkinnyMaxM) return launch_skinny(p, M, ws, stream);
-    return launch_gemm(p, M, stream);
+    return launch_gemm_xsum(p, M, xsum, stream);
+}
+
+// Workspace of the fused float32 forward: xq, eta, the row sums (prefill
+// sizes only), then the contraction's own workspace.
+struct F32Ws {
+    size_t xq, eta, xsum, bytes;
+};
+
+F32Ws f32_ws(int64_t M, int64_t N, int64_t K) {
+    F32Ws w;
+    w.xq = align256((size_t)(M * K));
+    w.eta = align256((size_t)(4 * M));
+    w.xsum = M > kSkinnyMaxM ? align256((size_t)(4 * M)) : 0;
+    w.bytes = w.xq + w.eta + w.xsum + align256(forward_ws_bytes(M, N, K));
+    return w;
 }
 
 struct TableLayout {
@@ -162,7 +181,7 @@ const char* bitlinear_status_string(int status) {
     }
 }
 
-int bitlinear_abi_version(void) { return 10100; }
+int bitlinear_abi_version(void) { return 10200; }
 
 const char* bitlinear_last_error(void) { return g_last_error; }
 
@@ -173,8 +192,7 @@ size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
 
 size_t bitlinear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (check_sizes(M, N, K) != BITLINEAR_OK) return 0;
-    const size_t f32 = align256((size_t)(M * K)) + align256((size_t)(4 * M)) +
-                       align256(forward_ws_bytes(M, N, K));
+    const size_t f32 = f32_ws(M, N, K).bytes;
     size_t pack = align256(gamma_ws_bytes());
     if (align256(median_ws_bytes()) > pack) pack = align256(median_ws_bytes());
     return f32 > pack ? f32 : pack;
@@ -339,7 +357,20 @@ int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed,
     const size_t need = forward_ws_bytes(M, N, K);
     if (need && (!ws || !aligned(ws, 256) || ws_bytes < need)) return BITLINEAR_EWORKSPACE;
     clear_hip_error();
-    return run_forward(xq, eta, packed, gamma, M, N, K, y, y_int, ws, (hipStream_t)stream);
+    return run_forward(xq, eta, nullptr, packed, gamma, M, N, K, y, y_int, ws, (hipStream_t)stream);
+}
+
+int bitlinear_forward_xsum(const int8_t* xq, const float* eta, const int32_t* xsum,
+                           const uint8_t* packed, float gamma, int64_t M, int64_t N, int64_t K,
+                           float* y, int32_t* y_int, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sizes(M, N, K);
+    if (rc) return rc;
+    if (!xq || !eta || !xsum || !packed || !y) return BITLINEAR_EINVAL;
+    if (!aligned(xq, 16) || !aligned(packed, 16) || !aligned(xsum, 4)) return BITLINEAR_EINVAL;
+    const size_t need = forward_ws_bytes(M, N, K);
+    if (need && (!ws || !aligned(ws, 256) || ws_bytes < need)) return BITLINEAR_EWORKSPACE;
+    clear_hip_error();
+    return run_forward(xq, eta, xsum, packed, gamma, M, N, K, y, y_int, ws, (hipStream_t)stream);
 }
 
 static int forward_f32_common(const float* x, const uint8_t* packed, float gamma, int64_t M,
@@ -349,19 +380,21 @@ static int forward_f32_common(const float* x, const uint8_t* packed, float gamma
     if (rc) return rc;
     if (!x || !packed || !y) return BITLINEAR_EINVAL;
     if (!aligned(x, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
-    const size_t xq_bytes = align256((size_t)(M * K)), eta_bytes = align256((size_t)(4 * M));
-    const size_t need = xq_bytes + eta_bytes + align256(forward_ws_bytes(M, N, K));
-    if (!ws || !aligned(ws, 256) || ws_bytes < need) return BITLINEAR_EWORKSPACE;
+    const F32Ws w = f32_ws(M, N, K);
+    if (!ws || !aligned(ws, 256) || ws_bytes < w.bytes) return BITLINEAR_EWORKSPACE;
     if (M == 0) return BITLINEAR_OK;
     int8_t* xq = (int8_t*)ws;
-    float* eta = (float*)((char*)ws + xq_bytes);
-    void* rest = (char*)ws + xq_bytes + eta_bytes;
+    float* eta = (float*)((char*)ws + w.xq);
+    int32_t* xsum = w.xsum ? (int32_t*)((char*)ws + w.xq + w.eta) : nullptr;
+    void* rest = (char*)ws + w.xq + w.eta + w.xsum;
     hipStream_t s = (hipStream_t)stream;
     clear_hip_error();
-    rc = rmsnorm ? launch_rmsnorm_quantize(x, M, K, xq, eta, nullptr, nullptr, s)
-                 : launch_quantize(x, M, K, xq, eta, nullptr, s);
+    // The quantizer writes the row sums alongside xq, so the contraction
+    // need not sum the activation tiles again.
+    rc = rmsnorm ? launch_rmsnorm_quantize(x, M, K, xq, eta, xsum, nullptr, s)
+                 : launch_quantize(x, M, K, xq, eta, xsum, s);
     if (rc) return rc;
-    return run_forward(xq, eta, packed, gamma, M, N, K, y, nullptr, rest, s);
+    return run_forward(xq, eta, xsum, packed, gamma, M, N, K, y, nullptr, rest, s);
 }
 
 int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, int64_t M, int64_t N,

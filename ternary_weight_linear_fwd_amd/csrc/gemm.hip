@@ -37,6 +37,7 @@
 // Epilogue: y = float(y_int) * ((eta[m] * gamma) / 127), fused.
 #include <atomic>
 
+#include "gemm.hpp"
 #include "kernels.hpp"
 
 namespace bl {
@@ -51,6 +52,7 @@ struct GemmArgs {
     int64_t M;
     int64_t ntiles_n;         // single: column tiles
     int64_t ntiles_m;         // single: row tiles
+    const int32_t* xsum;      // single: the row sums sum_k xq[m][k], or null
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
@@ -160,18 +162,30 @@ __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT, NT>& c, uint8
     if constexpr (NT == 3) __builtin_amdgcn_sched_barrier(0);
 }
 
-// One K-step of MFMAs from the LDS stage at A.  Wavefront w also adds word
-// group w of the step's A rows into the row sums `sx` (one extra fragment
-// read per row tile, four v_dot4 each).  TAIL: the step may be the last one,
-// whose second k-block can lie past the end.
-template <int MT, int NT, bool TAIL>
+// One K-step of MFMAs from the LDS stage at A.  Without given row sums (RS
+// false) wavefront w also adds word group w of the step's A rows into the row
+// sums `sx` (one extra fragment read per row tile, four v_dot4 each).  TAIL:
+// the step may be the last one, whose second k-block can lie past the end.
+template <int MT, int NT, bool TAIL, bool RS>
 __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT, NT>& c, const uint8_t* A, int64_t step,
                                                 const v4i (&bq)[NT], v16i (&acc)[MT][NT], int (&sx)[MT]) {
     v4i bw[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) bw[t] = bq[t];
     if constexpr (TAIL) {
-        if (step * 2 + 1 >= c.Kb && c.lg == 1) {   // k-block past the end: code 01
+        if constexpr (RS) {
+            // The given row sums cover k < K only, so every k at or past K
+            // gets code 00 (c = 0): it adds nothing whatever A holds there.
+            // Word d of the lane's chunk is k = 64 kb + 16 d .. + 15, and K
+            // is a multiple of 16, so a word is wholly inside or outside.
+            const int64_t k0 = (step * 2 + c.lg) * 64;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                if (k0 + 16 * d >= c.K) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) bw[t][d] = 0;
+                }
+        } else if (step * 2 + 1 >= c.Kb && c.lg == 1) {   // k-block past the end: code 01
 #pragma unroll
             for (int t = 0; t < NT; ++t) bw[t] = v4i{0x55555555, 0x55555555, 0x55555555, 0x55555555};
         }
@@ -185,13 +199,15 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT, NT>& c, con
     auto a_frag = [&](int i, int d) {
         return *reinterpret_cast<const v4i*>(A + i * 4096 + (c.afrag[d & 3] & 4095u));
     };
+    if constexpr (!RS) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const v4i f = *reinterpret_cast<const v4i*>(A + i * 4096 + (c.sxfrag & 4095u));
-        sx[i] = __builtin_amdgcn_sdot4(f.x, 0x01010101, sx[i], false);
-        sx[i] = __builtin_amdgcn_sdot4(f.y, 0x01010101, sx[i], false);
-        sx[i] = __builtin_amdgcn_sdot4(f.z, 0x01010101, sx[i], false);
-        sx[i] = __builtin_amdgcn_sdot4(f.w, 0x01010101, sx[i], false);
+        for (int i = 0; i < MT; ++i) {
+            const v4i f = *reinterpret_cast<const v4i*>(A + i * 4096 + (c.sxfrag & 4095u));
+            sx[i] = __builtin_amdgcn_sdot4(f.x, 0x01010101, sx[i], false);
+            sx[i] = __builtin_amdgcn_sdot4(f.y, 0x01010101, sx[i], false);
+            sx[i] = __builtin_amdgcn_sdot4(f.z, 0x01010101, sx[i], false);
+            sx[i] = __builtin_amdgcn_sdot4(f.w, 0x01010101, sx[i], false);
+        }
     }
     // Two register sets for the A fragments and the B codes: group d+1's LDS
     // reads and field extraction run while group d's MFMAs execute.
@@ -246,18 +262,18 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT, NT>& c, con
 // is past it) with step + NS - 1, compute.  Straight-line code, so that the
 // compiler can see which stage each LDS read and each load in flight touch
 // and adds no waits of its own.
-template <int MT, int NT, int NS>
+template <int MT, int NT, int NS, bool RS>
 __device__ __forceinline__ void prefill_step(const PrefillCtx<MT, NT>& c, const uint8_t* cur, uint8_t* refill,
                                              int64_t step, const v4i (&bq_cur)[NT], v4i (&bq_refill)[NT],
                                              v16i (&acc)[MT][NT], int (&sx)[MT]) {
     wait_vmcnt<(NS - 2) * PrefillCtx<MT, NT>::Ops>();
     __builtin_amdgcn_s_barrier();   // not __syncthreads(): that would drain the loads in flight
     prefill_issue<MT, NT, false>(c, refill, step + NS - 1, bq_refill);   // <= nsteps - 2: never the last
-    prefill_compute<MT, NT, false>(c, cur, step, bq_cur, acc, sx);
+    prefill_compute<MT, NT, false, RS>(c, cur, step, bq_cur, acc, sx);
 }
 
 // Any step, including the last ones (nothing left to refill, or past the end).
-template <int MT, int NT, int NS>
+template <int MT, int NT, int NS, bool RS>
 __device__ __forceinline__ void prefill_step_tail(const PrefillCtx<MT, NT>& c, const uint8_t* cur, uint8_t* refill,
                                                   int64_t step, const v4i (&bq_cur)[NT], v4i (&bq_refill)[NT],
                                                   v16i (&acc)[MT][NT], int (&sx)[MT]) {
@@ -269,13 +285,15 @@ __device__ __forceinline__ void prefill_step_tail(const PrefillCtx<MT, NT>& c, c
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (step + NS - 1 < c.nsteps) prefill_issue<MT, NT, true>(c, refill, step + NS - 1, bq_refill);
-    prefill_compute<MT, NT, true>(c, cur, step, bq_cur, acc, sx);
+    prefill_compute<MT, NT, true, RS>(c, cur, step, bq_cur, acc, sx);
 }
 
 // Resident workgroups per CU for an MT x NT wave tile (register budget).
 constexpr int prefill_occupancy(int mt, int nt) { return mt * nt <= 2 ? 4 : mt * nt <= 4 ? 3 : 2; }
 
-template <int MT, int NT, bool GROUPED, int NS>
+// RS: the row sums come from a.xsum (single mode) instead of being summed
+// from the activation tiles on the way.
+template <int MT, int NT, bool GROUPED, int NS, bool RS>
 __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_kernel(GemmArgs a) {
     static_assert(NS == 3 || NS == 4, "ring of three or four stages");
     using Ctx = PrefillCtx<MT, NT>;
@@ -286,7 +304,7 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[Ctx::AStage];
     __shared__ __attribute__((aligned(1024))) uint8_t stage2[Ctx::AStage];
     __shared__ __attribute__((aligned(1024))) uint8_t stage3[NS == 4 ? Ctx::AStage : 16];
-    __shared__ int rowsum_part[8][BM];   // [wave * 2 + lane group][row]
+    __shared__ int rowsum_part[RS ? 1 : 8][BM];   // [wave * 2 + lane group][row]
     __shared__ float2 rowinfo[BM];   // (row sum as int bits, dequant scale)
 
     const int tid = threadIdx.x;
@@ -362,44 +380,50 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     if constexpr (NS == 3) {
         // The main loop queues steps up to nsteps - 2, all of them whole.
         for (; step + 6 <= c.nsteps; step += 3) {
-            prefill_step<MT, NT, 3>(c, stage0, stage2, step, bq0, bq2, acc, sx);
-            prefill_step<MT, NT, 3>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-            prefill_step<MT, NT, 3>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+            prefill_step<MT, NT, 3, RS>(c, stage0, stage2, step, bq0, bq2, acc, sx);
+            prefill_step<MT, NT, 3, RS>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+            prefill_step<MT, NT, 3, RS>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
         }
         // The last one to five steps.
-        prefill_step_tail<MT, NT, 3>(c, stage0, stage2, step, bq0, bq2, acc, sx);
-        prefill_step_tail<MT, NT, 3>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-        prefill_step_tail<MT, NT, 3>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-        prefill_step_tail<MT, NT, 3>(c, stage0, stage2, step + 3, bq0, bq2, acc, sx);
-        prefill_step_tail<MT, NT, 3>(c, stage1, stage0, step + 4, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 3, RS>(c, stage0, stage2, step, bq0, bq2, acc, sx);
+        prefill_step_tail<MT, NT, 3, RS>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 3, RS>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+        prefill_step_tail<MT, NT, 3, RS>(c, stage0, stage2, step + 3, bq0, bq2, acc, sx);
+        prefill_step_tail<MT, NT, 3, RS>(c, stage1, stage0, step + 4, bq1, bq0, acc, sx);
     } else {
         for (; step + 8 <= c.nsteps; step += 4) {
-            prefill_step<MT, NT, 4>(c, stage0, stage3, step, bq0, bq3, acc, sx);
-            prefill_step<MT, NT, 4>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-            prefill_step<MT, NT, 4>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-            prefill_step<MT, NT, 4>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
+            prefill_step<MT, NT, 4, RS>(c, stage0, stage3, step, bq0, bq3, acc, sx);
+            prefill_step<MT, NT, 4, RS>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+            prefill_step<MT, NT, 4, RS>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+            prefill_step<MT, NT, 4, RS>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
         }
         // The last one to seven steps.
-        prefill_step_tail<MT, NT, 4>(c, stage0, stage3, step, bq0, bq3, acc, sx);
-        prefill_step_tail<MT, NT, 4>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-        prefill_step_tail<MT, NT, 4>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-        prefill_step_tail<MT, NT, 4>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
-        prefill_step_tail<MT, NT, 4>(c, stage0, stage3, step + 4, bq0, bq3, acc, sx);
-        prefill_step_tail<MT, NT, 4>(c, stage1, stage0, step + 5, bq1, bq0, acc, sx);
-        prefill_step_tail<MT, NT, 4>(c, stage2, stage1, step + 6, bq2, bq1, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS>(c, stage0, stage3, step, bq0, bq3, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS>(c, stage0, stage3, step + 4, bq0, bq3, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS>(c, stage1, stage0, step + 5, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS>(c, stage2, stage1, step + 6, bq2, bq1, acc, sx);
     }
 
     // Row sums: partials of (wave, lane group) -> one total per tile row, and
     // each row's dequant scale, computed once here rather than by every lane
     // that stores a value of the row.
+    if constexpr (!RS) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) rowsum_part[wave * 2 + c.lg][i * 32 + c.ln] = sx[i];
-    __syncthreads();
+        for (int i = 0; i < MT; ++i) rowsum_part[wave * 2 + c.lg][i * 32 + c.ln] = sx[i];
+        __syncthreads();
+    }
     if (tid < BM) {
-        int t = 0;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) t += rowsum_part[w][tid];
         const int64_t m = m0 + tid;
+        int t = 0;
+        if constexpr (RS) {
+            t = m < M ? a.xsum[m] : 0;
+        } else {
+#pragma unroll
+            for (int w = 0; w < 8; ++w) t += rowsum_part[w][tid];
+        }
         rowinfo[tid] = make_float2(__int_as_float(t), m < M ? dequant_scale(p.eta[m], p.gamma) : 0.0f);
     }
     __syncthreads();
@@ -509,14 +533,20 @@ template <int MT, int NT>
 static void launch_single(GemmArgs& a, hipStream_t stream) {
     a.ntiles_m = ceil_div(a.M, 32 * MT);
     a.ntiles_n = ceil_div(a.p.N, 128 * NT);
-    hipLaunchKernelGGL((gemm_prefill_kernel<MT, NT, false, prefill_stages(MT, NT)>), dim3((unsigned)(a.ntiles_m * a.ntiles_n)),
-                       dim3(256), 0, stream, a);
+    const dim3 grid((unsigned)(a.ntiles_m * a.ntiles_n));
+    if (a.xsum)
+        hipLaunchKernelGGL((gemm_prefill_kernel<MT, NT, false, prefill_stages(MT, NT), true>), grid, dim3(256), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((gemm_prefill_kernel<MT, NT, false, prefill_stages(MT, NT), false>), grid, dim3(256), 0,
+                           stream, a);
 }
 
-int launch_gemm(const Problem& p, int64_t M, hipStream_t stream) {
+int launch_gemm_xsum(const Problem& p, int64_t M, const int32_t* xsum, hipStream_t stream) {
     GemmArgs a{};
     a.p = p;
     a.M = M;
+    a.xsum = xsum;
     const TileCfg t = prefill_tile(M, p.N, device_cus());
     if (t.mt == 3) launch_single<3, 3>(a, stream);
     else if (t.mt == 4) launch_single<4, 2>(a, stream);
@@ -524,6 +554,8 @@ int launch_gemm(const Problem& p, int64_t M, hipStream_t stream) {
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
 }
+
+int launch_gemm(const Problem& p, int64_t M, hipStream_t stream) { return launch_gemm_xsum(p, M, nullptr, stream); }
 
 int gemm_tile_n(int64_t M) { return gemm_bn(M); }
 
@@ -534,7 +566,7 @@ int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nuni
     a.problems = problems;
     a.units = units;
     a.M = M;
-    hipLaunchKernelGGL((gemm_prefill_kernel<4, 2, true, prefill_stages(4, 2)>), dim3((unsigned)nunits, (unsigned)ceil_div(M, 128)),
+    hipLaunchKernelGGL((gemm_prefill_kernel<4, 2, true, prefill_stages(4, 2), false>), dim3((unsigned)nunits, (unsigned)ceil_div(M, 128)),
                        dim3(256), 0, stream, a);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;

@@ -101,6 +101,22 @@ def forward(xq: np.ndarray, eta: np.ndarray, packed, gamma, N: int, with_int=Tru
     return y.cpu().numpy(), (y_int.cpu().numpy() if with_int else None)
 
 
+def forward_xsum(xq: np.ndarray, eta: np.ndarray, xsum: np.ndarray, packed, gamma, N: int):
+    """bitlinear_forward_xsum with the given row sums (an input, like xq)."""
+    torch = torch_cuda()
+    L = bl()
+    M, K = xq.shape
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    y_int = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    ws_bytes = L.bitlinear_workspace_bytes(M, N, K)
+    ws = empty(ws_bytes)
+    L.bitlinear_forward_xsum(to_dev(xq.astype(np.int8)), to_dev(eta.astype(np.float32)),
+                             to_dev(xsum.astype(np.int32)), packed, float(gamma), M, N, K, y, y_int,
+                             ws, ws_bytes)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), y_int.cpu().numpy()
+
+
 def forward_f32(x: np.ndarray, packed, gamma, N: int):
     torch = torch_cuda()
     L = bl()

@@ -55,7 +55,7 @@ def test_status_strings():
     for code in (-1, -2, -3, -4, -5):
         assert bl.bitlinear_status_string(code).startswith("BITLINEAR_E")
     assert bl.bitlinear_status_string(7) == "BITLINEAR_UNKNOWN"
-    assert bl.bitlinear_abi_version() == 10100
+    assert bl.bitlinear_abi_version() == 10200
 
 
 def test_packed3_and_lut_workspace_bytes():
@@ -83,6 +83,8 @@ def test_workspace_bytes():
     for M, N, K in ((1, 2048, 2048), (8, 3200, 8640), (2048, 8640, 3200), (0, 64, 64)):
         ws = bl.bitlinear_workspace_bytes(M, N, K)
         assert ws >= M * K + 4 * M and ws % 256 == 0 and ws >= 2048
+    # prefill sizes: xq, eta and the row sums, each 256-byte aligned
+    assert bl.bitlinear_workspace_bytes(2048, 8640, 3200) >= 2048 * 3200 + 2 * 4 * 2048
     assert bl.bitlinear_workspace_bytes(-1, 64, 64) == 0
 
 
@@ -112,6 +114,11 @@ def test_validation_before_any_device_work():
     need = L.bitlinear_workspace_bytes(1, 8192, 8192)
     assert need > 0
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    # forward with row sums: the sums are required; otherwise as bitlinear_forward
+    assert _rc("bitlinear_forward_xsum", FAKE, FAKE, None, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward_xsum", FAKE, FAKE, FAKE + 2, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward_xsum", FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), 128, 64, 40, FAKE, None, None, 0, None) == L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_forward_xsum", FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, FAKE + 8, 1 << 20, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_pack_weights_absmedian", FAKE, 64, 64, FAKE, None, None, FAKE, 4096, None) == L.BITLINEAR_EWORKSPACE

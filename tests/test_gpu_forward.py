@@ -5,8 +5,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import (assert_y_close, bl, forward, forward_f32, pack_ternary, pack_weights, say, to_dev,
-                         torch_cuda)
+from gpu_helpers import (assert_y_close, bl, forward, forward_f32, forward_xsum, pack_ternary, pack_weights,
+                         say, to_dev, torch_cuda)
 from ternary_weight_linear_fwd_amd import synthetic as S
 
 pytestmark = pytest.mark.gpu
@@ -31,6 +31,11 @@ def run_case(M, N, K, seed, dist="normal", latent=True):
     assert np.array_equal(y_int, y_int_ref), np.argwhere(y_int != y_int_ref)[:5]
     assert_y_close(y, y_ref)
     assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+    # row sums supplied (the definition, sum over k of xq): the same bits
+    xsum = xq.astype(np.int64).sum(axis=1)
+    y3, y_int3 = forward_xsum(xq, eta, xsum, packed, g, N)
+    assert np.array_equal(y_int3, y_int_ref), np.argwhere(y_int3 != y_int_ref)[:5]
+    assert np.array_equal(y3.view(np.uint32), y_ref.view(np.uint32))
     # fused path from float32 activations
     yf = forward_f32(x, packed, g, N)
     assert_y_close(yf, y_ref)
@@ -140,6 +145,8 @@ def test_prefill_workload_shapes():
             outs.append((y.cpu().numpy(), y_int.cpu().numpy()))
         (y, y_int), (y2, y_int2) = outs
         assert np.array_equal(y_int, y_int2) and np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+        y3, y_int3 = forward_xsum(xq, eta, xq.astype(np.int64).sum(axis=1), packed, 0.0173, N)
+        assert np.array_equal(y_int, y_int3) and np.array_equal(y.view(np.uint32), y3.view(np.uint32))
         rows = np.arange(M) if M * N * K <= 6e9 else \
             np.sort(np.random.default_rng(i).choice(M, 48, replace=False))
         y_ref, y_int_ref = oracle.forward_q(xq[rows], eta[rows], Wt, np.float32(0.0173), threads=8)
@@ -151,3 +158,25 @@ def test_prefill_workload_shapes():
         x64 = xq.astype(np.int64)
         assert np.array_equal(y_int.astype(np.int64).sum(axis=1), x64 @ Wt.astype(np.int64).sum(axis=0))
         assert np.array_equal(y_int.astype(np.int64) @ r, x64 @ (Wt.astype(np.int64).T @ r))
+
+
+# The prefill kernel reads the given row sums (and sums nothing itself): an
+# offset d[m] in xsum[m] moves row m of y_int by exactly -d[m] (int32
+# wrap-around arithmetic).  Decode sizes (M <= 64) ignore the argument.
+@pytest.mark.parametrize("M,N,K", [(65, 300, 208), (200, 1000, 1040), (2048, 640, 80)])
+def test_forward_xsum_is_read(M, N, K):
+    say(f"forward_xsum offsets M={M} N={N} K={K}")
+    x = S.random_x(M + N, M, K)
+    Wt = S.random_ternary(M + K, N, K)
+    packed, bad = pack_ternary(Wt)
+    assert bad == 0
+    xq, eta = oracle.quantize_act(x)
+    y_ref, y_int_ref = oracle.forward_q(xq, eta, Wt, np.float32(0.02), threads=8)
+    d = np.random.default_rng(M).integers(-1000, 1001, M).astype(np.int64)
+    xsum = xq.astype(np.int64).sum(axis=1)
+    _, y_int = forward_xsum(xq, eta, xsum + d, packed, 0.02, N)
+    assert np.array_equal(y_int.astype(np.int64), y_int_ref.astype(np.int64) - d[:, None])
+    # decode sizes: the argument is not read
+    yq, y_intq = forward_xsum(xq[:16], eta[:16], xsum[:16] + d[:16], packed, 0.02, N)
+    assert np.array_equal(y_intq, y_int_ref[:16])
+    assert np.array_equal(yq.view(np.uint32), y_ref[:16].view(np.uint32))
