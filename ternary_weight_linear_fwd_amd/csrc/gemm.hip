@@ -104,7 +104,9 @@ struct PrefillCtx {
     static constexpr int BM = 32 * MT;            // token rows per workgroup tile
     static constexpr int AStage = BM * 128;       // bytes of A per stage
     static constexpr int NA = AStage / 4096;      // A DMA instructions per wave per step
-    static constexpr int Ops = NA + NT;           // + NT weight loads: vector memory instructions per step
+    // Vector memory instructions per step: NA activation DMAs, plus NT weight
+    // loads for a wavefront with columns inside N.
+    static constexpr int ops(bool act) { return NA + (act ? NT : 0); }
     // DMA sources are a wave-uniform base (scalar registers) plus a 32-bit
     // per-lane offset, so that the main loop spends no vector ALU work on
     // addresses (row offsets stay below 2^32 since K <= 2^24).
@@ -120,11 +122,12 @@ struct PrefillCtx {
 };
 
 // Queue step `step`: this wave's NA activation DMAs into LDS stage `st` and
-// its two weight loads into registers bq (the weight chunks are private to
+// its NT weight loads into registers bq (the weight chunks are private to
 // the wavefront, so they skip LDS).  CHECKED: the step may reach past K (the
 // last step, or one queued past the end), so addresses are clamped in
-// bounds; otherwise all 128 k of the step lie inside K.
-template <int MT, int NT, bool CHECKED>
+// bounds; otherwise all 128 k of the step lie inside K.  ACT false: the
+// wavefront has no columns inside N and loads only its share of A.
+template <int MT, int NT, bool CHECKED, bool ACT>
 __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT, NT>& c, uint8_t* st, int64_t step, v4i (&bq)[NT]) {
     using Ctx = PrefillCtx<MT, NT>;
     if constexpr (NT == 3) __builtin_amdgcn_sched_barrier(0);
@@ -144,7 +147,7 @@ __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT, NT>& c, uint8
     // Lane (ln, lg) takes row ln of each column tile's 32 rows in k-block
     // 2 * step + lg.
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < (ACT ? NT : 0); ++t) {
         const uint8_t* bsrc;
         if constexpr (CHECKED) {
             const int64_t kb = step * 2 + c.lg < c.Kb ? step * 2 + c.lg : c.Kb - 1;   // past the end: replaced at use
@@ -166,7 +169,8 @@ __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT, NT>& c, uint8
 // false) wavefront w also adds word group w of the step's A rows into the row
 // sums `sx` (one extra fragment read per row tile, four v_dot4 each).  TAIL:
 // the step may be the last one, whose second k-block can lie past the end.
-template <int MT, int NT, bool TAIL, bool RS>
+// ACT false: no columns inside N, so only the row sums (if any).
+template <int MT, int NT, bool TAIL, bool RS, bool ACT>
 __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT, NT>& c, const uint8_t* A, int64_t step,
                                                 const v4i (&bq)[NT], v16i (&acc)[MT][NT], int (&sx)[MT]) {
     v4i bw[NT];
@@ -209,6 +213,7 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT, NT>& c, con
             sx[i] = __builtin_amdgcn_sdot4(f.w, 0x01010101, sx[i], false);
         }
     }
+    if constexpr (!ACT) return;
     // Two register sets for the A fragments and the B codes: group d+1's LDS
     // reads and field extraction run while group d's MFMAs execute.
     v4i af[2][MT], bf[2][NT];
@@ -262,30 +267,78 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT, NT>& c, con
 // is past it) with step + NS - 1, compute.  Straight-line code, so that the
 // compiler can see which stage each LDS read and each load in flight touch
 // and adds no waits of its own.
-template <int MT, int NT, int NS, bool RS>
+template <int MT, int NT, int NS, bool RS, bool ACT>
 __device__ __forceinline__ void prefill_step(const PrefillCtx<MT, NT>& c, const uint8_t* cur, uint8_t* refill,
                                              int64_t step, const v4i (&bq_cur)[NT], v4i (&bq_refill)[NT],
                                              v16i (&acc)[MT][NT], int (&sx)[MT]) {
-    wait_vmcnt<(NS - 2) * PrefillCtx<MT, NT>::Ops>();
+    wait_vmcnt<(NS - 2) * PrefillCtx<MT, NT>::ops(ACT)>();
     __builtin_amdgcn_s_barrier();   // not __syncthreads(): that would drain the loads in flight
-    prefill_issue<MT, NT, false>(c, refill, step + NS - 1, bq_refill);   // <= nsteps - 2: never the last
-    prefill_compute<MT, NT, false, RS>(c, cur, step, bq_cur, acc, sx);
+    prefill_issue<MT, NT, false, ACT>(c, refill, step + NS - 1, bq_refill);   // <= nsteps - 2: never the last
+    prefill_compute<MT, NT, false, RS, ACT>(c, cur, step, bq_cur, acc, sx);
 }
 
 // Any step, including the last ones (nothing left to refill, or past the end).
-template <int MT, int NT, int NS, bool RS>
+template <int MT, int NT, int NS, bool RS, bool ACT>
 __device__ __forceinline__ void prefill_step_tail(const PrefillCtx<MT, NT>& c, const uint8_t* cur, uint8_t* refill,
                                                   int64_t step, const v4i (&bq_cur)[NT], v4i (&bq_refill)[NT],
                                                   v16i (&acc)[MT][NT], int (&sx)[MT]) {
-    constexpr int Ops = PrefillCtx<MT, NT>::Ops;
+    constexpr int Ops = PrefillCtx<MT, NT>::ops(ACT);
     if (step >= c.nsteps) return;
     const int64_t later = c.nsteps - 1 - step;   // queued steps after this one
     if (NS >= 4 && later >= 2) wait_vmcnt<(NS >= 4 ? 2 : 1) * Ops>();
     else if (later >= 1) wait_vmcnt<Ops>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (step + NS - 1 < c.nsteps) prefill_issue<MT, NT, true>(c, refill, step + NS - 1, bq_refill);
-    prefill_compute<MT, NT, true, RS>(c, cur, step, bq_cur, acc, sx);
+    if (step + NS - 1 < c.nsteps) prefill_issue<MT, NT, true, ACT>(c, refill, step + NS - 1, bq_refill);
+    prefill_compute<MT, NT, true, RS, ACT>(c, cur, step, bq_cur, acc, sx);
+}
+
+// The K loop over a ring of NS LDS stages (each its own LDS object, so that
+// the compiler can tell a read of one stage from the loads in flight into
+// the others).
+template <int MT, int NT, int NS, bool RS, bool ACT>
+__device__ __forceinline__ void prefill_pipeline(const PrefillCtx<MT, NT>& c, uint8_t* stage0, uint8_t* stage1,
+                                                 uint8_t* stage2, uint8_t* stage3, v16i (&acc)[MT][NT],
+                                                 int (&sx)[MT]) {
+    // The first NS - 1 steps are always queued (past the end they read clamped,
+    // in-bounds addresses and are never used), so that no branch precedes the
+    // main loop.  Weight words of the steps in flight: one register set per
+    // stage.
+    v4i bq0[NT], bq1[NT], bq2[NT], bq3[NT];
+    prefill_issue<MT, NT, true, ACT>(c, stage0, 0, bq0);
+    prefill_issue<MT, NT, true, ACT>(c, stage1, 1, bq1);
+    if constexpr (NS == 4) prefill_issue<MT, NT, true, ACT>(c, stage2, 2, bq2);
+    int64_t step = 0;
+    if constexpr (NS == 3) {
+        // The main loop queues steps up to nsteps - 2, all of them whole.
+        for (; step + 6 <= c.nsteps; step += 3) {
+            prefill_step<MT, NT, 3, RS, ACT>(c, stage0, stage2, step, bq0, bq2, acc, sx);
+            prefill_step<MT, NT, 3, RS, ACT>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+            prefill_step<MT, NT, 3, RS, ACT>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+        }
+        // The last one to five steps.
+        prefill_step_tail<MT, NT, 3, RS, ACT>(c, stage0, stage2, step, bq0, bq2, acc, sx);
+        prefill_step_tail<MT, NT, 3, RS, ACT>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 3, RS, ACT>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+        prefill_step_tail<MT, NT, 3, RS, ACT>(c, stage0, stage2, step + 3, bq0, bq2, acc, sx);
+        prefill_step_tail<MT, NT, 3, RS, ACT>(c, stage1, stage0, step + 4, bq1, bq0, acc, sx);
+    } else {
+        for (; step + 8 <= c.nsteps; step += 4) {
+            prefill_step<MT, NT, 4, RS, ACT>(c, stage0, stage3, step, bq0, bq3, acc, sx);
+            prefill_step<MT, NT, 4, RS, ACT>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+            prefill_step<MT, NT, 4, RS, ACT>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+            prefill_step<MT, NT, 4, RS, ACT>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
+        }
+        // The last one to seven steps.
+        prefill_step_tail<MT, NT, 4, RS, ACT>(c, stage0, stage3, step, bq0, bq3, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS, ACT>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS, ACT>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS, ACT>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS, ACT>(c, stage0, stage3, step + 4, bq0, bq3, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS, ACT>(c, stage1, stage0, step + 5, bq1, bq0, acc, sx);
+        prefill_step_tail<MT, NT, 4, RS, ACT>(c, stage2, stage1, step + 6, bq2, bq1, acc, sx);
+    }
+
 }
 
 // Resident workgroups per CU for an MT x NT wave tile (register budget).
@@ -368,44 +421,10 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
             for (int e = 0; e < 16; ++e) acc[i][t][e] = 0;
     }
 
-    // The first NS - 1 steps are always queued (past the end they read clamped,
-    // in-bounds addresses and are never used), so that no branch precedes the
-    // main loop.  Weight words of the steps in flight: one register set per
-    // stage.
-    v4i bq0[NT], bq1[NT], bq2[NT], bq3[NT];
-    prefill_issue<MT, NT, true>(c, stage0, 0, bq0);
-    prefill_issue<MT, NT, true>(c, stage1, 1, bq1);
-    if constexpr (NS == 4) prefill_issue<MT, NT, true>(c, stage2, 2, bq2);
-    int64_t step = 0;
-    if constexpr (NS == 3) {
-        // The main loop queues steps up to nsteps - 2, all of them whole.
-        for (; step + 6 <= c.nsteps; step += 3) {
-            prefill_step<MT, NT, 3, RS>(c, stage0, stage2, step, bq0, bq2, acc, sx);
-            prefill_step<MT, NT, 3, RS>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-            prefill_step<MT, NT, 3, RS>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-        }
-        // The last one to five steps.
-        prefill_step_tail<MT, NT, 3, RS>(c, stage0, stage2, step, bq0, bq2, acc, sx);
-        prefill_step_tail<MT, NT, 3, RS>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-        prefill_step_tail<MT, NT, 3, RS>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-        prefill_step_tail<MT, NT, 3, RS>(c, stage0, stage2, step + 3, bq0, bq2, acc, sx);
-        prefill_step_tail<MT, NT, 3, RS>(c, stage1, stage0, step + 4, bq1, bq0, acc, sx);
-    } else {
-        for (; step + 8 <= c.nsteps; step += 4) {
-            prefill_step<MT, NT, 4, RS>(c, stage0, stage3, step, bq0, bq3, acc, sx);
-            prefill_step<MT, NT, 4, RS>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-            prefill_step<MT, NT, 4, RS>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-            prefill_step<MT, NT, 4, RS>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
-        }
-        // The last one to seven steps.
-        prefill_step_tail<MT, NT, 4, RS>(c, stage0, stage3, step, bq0, bq3, acc, sx);
-        prefill_step_tail<MT, NT, 4, RS>(c, stage1, stage0, step + 1, bq1, bq0, acc, sx);
-        prefill_step_tail<MT, NT, 4, RS>(c, stage2, stage1, step + 2, bq2, bq1, acc, sx);
-        prefill_step_tail<MT, NT, 4, RS>(c, stage3, stage2, step + 3, bq3, bq2, acc, sx);
-        prefill_step_tail<MT, NT, 4, RS>(c, stage0, stage3, step + 4, bq0, bq3, acc, sx);
-        prefill_step_tail<MT, NT, 4, RS>(c, stage1, stage0, step + 5, bq1, bq0, acc, sx);
-        prefill_step_tail<MT, NT, 4, RS>(c, stage2, stage1, step + 6, bq2, bq1, acc, sx);
-    }
+    // Wavefronts with no columns inside N (the last column tile of a ragged
+    // N) only keep the shared activation ring moving.
+    if (group_ok) prefill_pipeline<MT, NT, NS, RS, true>(c, stage0, stage1, stage2, stage3, acc, sx);
+    else prefill_pipeline<MT, NT, NS, RS, false>(c, stage0, stage1, stage2, stage3, acc, sx);
 
     // Row sums: partials of (wave, lane group) -> one total per tile row, and
     // each row's dequant scale, computed once here rather than by every lane
