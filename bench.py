@@ -379,7 +379,8 @@ def main() -> int:
     Ms = (1,) if args.no_m16 else (1, 16)
     if args.profile_prefill:
         for r in bench_prefill(torch, L, S, max(1, args.steps)):
-            log(f"prefill {r['gemm']}: {r['us']} us")
+            log(f"prefill {r['gemm']}: {r['us']} us; own row sums {r['us_own_row_sums']} us; "
+                f"quantize {r['quantize_us']} us")
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):

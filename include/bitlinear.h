@@ -184,8 +184,9 @@ int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t
  *   gamma  the matrix's scale (by value)
  *   y      [M][N] float32 (out)
  *   y_int  [M][N] int32   (out, may be NULL): the exact integer sums
- *   ws     workspace of bitlinear_workspace_bytes(M, N, K) bytes (may be NULL
- *          with ws_bytes 0 when that size is 0)
+ *   ws     workspace of bitlinear_workspace_bytes(M, N, K) bytes, 256-byte
+ *          aligned: split-K partial sums at decode sizes, room for the
+ *          activation row sums at prefill sizes (M > 64)
  */
 int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
                       int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,

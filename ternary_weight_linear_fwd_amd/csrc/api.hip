@@ -50,7 +50,7 @@ int check_sizes(int64_t M, int64_t N, int64_t K) {
 size_t forward_ws_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= kGemvMaxM) return gemv_ws_bytes(M, N, K);
     if (M <= kSkinnyMaxM) return skinny_ws_bytes(M, N, K);
-    return 0;
+    return gemm_ws_bytes(M);
 }
 
 Problem make_problem(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
@@ -68,8 +68,9 @@ Problem make_problem(const int8_t* xq, const float* eta, const uint8_t* packed, 
     return p;
 }
 
-// xsum (may be null): the activation row sums, read by the prefill kernel
-// in place of its own; the decode kernels sum their slices themselves.
+// xsum (may be null): the activation row sums for the prefill kernel, which
+// otherwise sums them itself (or into the workspace first).  The decode
+// kernels sum their slices themselves.
 int run_forward(const int8_t* xq, const float* eta, const int32_t* xsum, const uint8_t* packed,
                 float gamma, int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,
                 hipStream_t stream) {
@@ -77,21 +78,20 @@ int run_forward(const int8_t* xq, const float* eta, const int32_t* xsum, const u
     const Problem p = make_problem(xq, eta, packed, gamma, N, K, y, y_int);
     if (M <= kGemvMaxM) return launch_gemv(p, M, ws, stream);
     if (M <= kSkinnyMaxM) return launch_skinny(p, M, ws, stream);
-    return launch_gemm_xsum(p, M, xsum, stream);
+    return xsum ? launch_gemm_xsum(p, M, xsum, stream) : launch_gemm(p, M, ws, stream);
 }
 
-// Workspace of the fused float32 forward: xq, eta, the row sums (prefill
-// sizes only), then the contraction's own workspace.
+// Workspace of the fused float32 forward: xq, eta, then the contraction's
+// own workspace (at prefill sizes the row sums, which the quantizer fills).
 struct F32Ws {
-    size_t xq, eta, xsum, bytes;
+    size_t xq, eta, bytes;
 };
 
 F32Ws f32_ws(int64_t M, int64_t N, int64_t K) {
     F32Ws w;
     w.xq = align256((size_t)(M * K));
     w.eta = align256((size_t)(4 * M));
-    w.xsum = M > kSkinnyMaxM ? align256((size_t)(4 * M)) : 0;
-    w.bytes = w.xq + w.eta + w.xsum + align256(forward_ws_bytes(M, N, K));
+    w.bytes = w.xq + w.eta + align256(forward_ws_bytes(M, N, K));
     return w;
 }
 
@@ -385,8 +385,8 @@ static int forward_f32_common(const float* x, const uint8_t* packed, float gamma
     if (M == 0) return BITLINEAR_OK;
     int8_t* xq = (int8_t*)ws;
     float* eta = (float*)((char*)ws + w.xq);
-    int32_t* xsum = w.xsum ? (int32_t*)((char*)ws + w.xq + w.eta) : nullptr;
-    void* rest = (char*)ws + w.xq + w.eta + w.xsum;
+    void* rest = (char*)ws + w.xq + w.eta;
+    int32_t* xsum = M > kSkinnyMaxM ? (int32_t*)rest : nullptr;
     hipStream_t s = (hipStream_t)stream;
     clear_hip_error();
     // The quantizer writes the row sums alongside xq, so the contraction

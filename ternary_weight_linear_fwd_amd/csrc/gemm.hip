@@ -548,33 +548,82 @@ static int device_cus() {
     return cus;
 }
 
-template <int MT, int NT>
+template <int MT, int NT, bool RS>
 static void launch_single(GemmArgs& a, hipStream_t stream) {
     a.ntiles_m = ceil_div(a.M, 32 * MT);
     a.ntiles_n = ceil_div(a.p.N, 128 * NT);
-    const dim3 grid((unsigned)(a.ntiles_m * a.ntiles_n));
-    if (a.xsum)
-        hipLaunchKernelGGL((gemm_prefill_kernel<MT, NT, false, prefill_stages(MT, NT), true>), grid, dim3(256), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((gemm_prefill_kernel<MT, NT, false, prefill_stages(MT, NT), false>), grid, dim3(256), 0,
-                           stream, a);
+    hipLaunchKernelGGL((gemm_prefill_kernel<MT, NT, false, prefill_stages(MT, NT), RS>),
+                       dim3((unsigned)(a.ntiles_m * a.ntiles_n)), dim3(256), 0, stream, a);
+}
+
+// Row sums of the int8 activations, xsum[m] = sum_k xq[m][k] in int32
+// (wrapping, like the contraction): one wavefront per row, 16 bytes per lane
+// per pass (K is a multiple of 16, so no chunk straddles a row end).  Plain
+// loads: the contraction reads the same rows next.
+__global__ __launch_bounds__(256) void rowsum_kernel(const int8_t* __restrict__ xq, int64_t M, int64_t K,
+                                                     int32_t* __restrict__ xsum) {
+    const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const int lane = threadIdx.x & 63;
+    const int8_t* row = xq + m * K;
+    int s = 0;
+    for (int64_t k = (int64_t)lane * 16; k < K; k += 1024) {
+        const v4i v = *reinterpret_cast<const v4i*>(row + k);
+        s = __builtin_amdgcn_sdot4(v.x, 0x01010101, s, false);
+        s = __builtin_amdgcn_sdot4(v.y, 0x01010101, s, false);
+        s = __builtin_amdgcn_sdot4(v.z, 0x01010101, s, false);
+        s = __builtin_amdgcn_sdot4(v.w, 0x01010101, s, false);
+    }
+    uint32_t u = (uint32_t)s;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) u += (uint32_t)__shfl_xor((int)u, off);
+    if (lane == 0) xsum[m] = (int32_t)u;
+}
+
+size_t gemm_ws_bytes(int64_t M) { return (size_t)M * sizeof(int32_t); }
+
+int launch_rowsum(const int8_t* xq, int64_t M, int64_t K, int32_t* xsum, hipStream_t stream) {
+    if (M == 0) return BITLINEAR_OK;
+    hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)ceil_div(M, 4)), dim3(256), 0, stream, xq, M, K, xsum);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
 }
 
 int launch_gemm_xsum(const Problem& p, int64_t M, const int32_t* xsum, hipStream_t stream) {
+    if (!xsum) return BITLINEAR_EINVAL;
     GemmArgs a{};
     a.p = p;
     a.M = M;
     a.xsum = xsum;
     const TileCfg t = prefill_tile(M, p.N, device_cus());
-    if (t.mt == 3) launch_single<3, 3>(a, stream);
-    else if (t.mt == 4) launch_single<4, 2>(a, stream);
-    else launch_single<2, 2>(a, stream);
+    if (t.mt == 3) launch_single<3, 3, true>(a, stream);
+    else if (t.mt == 4) launch_single<4, 2, true>(a, stream);
+    else launch_single<2, 2, true>(a, stream);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
 }
 
-int launch_gemm(const Problem& p, int64_t M, hipStream_t stream) { return launch_gemm_xsum(p, M, nullptr, stream); }
+// Without given row sums: the 64 x 256 and 128 x 256 tiles sum the rows
+// from their activation tiles on the way (a few percent of their time);
+// the 96 x 384 tile has no registers to spare for that, so a pre-pass sums
+// them into the workspace (about M * K bytes read, the operand's first
+// pass through the caches).
+int launch_gemm(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
+    const TileCfg t = prefill_tile(M, p.N, device_cus());
+    if (t.mt == 3) {
+        int32_t* xsum = static_cast<int32_t*>(ws);
+        const int rc = launch_rowsum(p.xq, M, p.K, xsum, stream);
+        if (rc) return rc;
+        return launch_gemm_xsum(p, M, xsum, stream);
+    }
+    GemmArgs a{};
+    a.p = p;
+    a.M = M;
+    if (t.mt == 4) launch_single<4, 2, false>(a, stream);
+    else launch_single<2, 2, false>(a, stream);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
 
 int gemm_tile_n(int64_t M) { return gemm_bn(M); }
 

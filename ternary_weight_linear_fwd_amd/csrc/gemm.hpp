@@ -1,13 +1,22 @@
-// gemm.hpp -- the prefill contraction (gemm.hip) with row sums supplied by
-// the caller.
+// gemm.hpp -- the single-problem prefill contraction (gemm.hip) and the
+// activation row sums it takes.
 #pragma once
 #include "kernels.hpp"
 
 namespace bl {
 
-// As launch_gemm, with xsum[m] = sum_k xq[m][k] (exact, as the activation
-// quantizer writes it) read instead of summed from the activation tiles.
-// xsum null: launch_gemm.
+// Workspace of a prefill contraction whose caller has no row sums: xsum [M].
+size_t gemm_ws_bytes(int64_t M);
+
+// xsum[m] = sum_k xq[m][k] (int32, wrapping), queued on the stream.
+int launch_rowsum(const int8_t* xq, int64_t M, int64_t K, int32_t* xsum, hipStream_t stream);
+
+// Prefill contraction (M > 64) with the fused dequant epilogue, given the
+// exact row sums xsum[m] = sum_k xq[m][k] (from launch_rowsum or the
+// activation quantizer).
 int launch_gemm_xsum(const Problem& p, int64_t M, const int32_t* xsum, hipStream_t stream);
+
+// The same without row sums; ws holds gemm_ws_bytes(M) bytes.
+int launch_gemm(const Problem& p, int64_t M, void* ws, hipStream_t stream);
 
 }  // namespace bl

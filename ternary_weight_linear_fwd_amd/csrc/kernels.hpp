@@ -80,8 +80,8 @@ int launch_skinny(const Problem& p, int64_t M, void* ws, hipStream_t stream);
 int launch_skinny_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
                           hipStream_t stream);
 
-// ---- prefill contraction on int8 MFMA for M > 64 (gemm.hip)
-int launch_gemm(const Problem& p, int64_t M, hipStream_t stream);
+// ---- prefill contraction on int8 MFMA for M > 64 (gemm.hip; the single
+// launch is declared in gemm.hpp)
 int gemm_tile_n(int64_t M);  // output rows per workgroup (column tile) for M
 int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
                         hipStream_t stream);

@@ -114,6 +114,9 @@ def test_validation_before_any_device_work():
     need = L.bitlinear_workspace_bytes(1, 8192, 8192)
     assert need > 0
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    # prefill sizes: the row sums need the workspace
+    assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, FAKE, 256, None) == L.BITLINEAR_EWORKSPACE
     # forward with row sums: the sums are required; otherwise as bitlinear_forward
     assert _rc("bitlinear_forward_xsum", FAKE, FAKE, None, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_forward_xsum", FAKE, FAKE, FAKE + 2, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
