@@ -39,6 +39,7 @@
 
 #include "gemm.hpp"
 #include "kernels.hpp"
+#include "xcd.hpp"
 
 namespace bl {
 
@@ -55,22 +56,15 @@ struct GemmArgs {
     const int32_t* xsum;      // single: the row sums sum_k xq[m][k], or null
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
-// XCD b % 8), each with its own 4 MB L2.  Each XCD takes a contiguous run of
-// the tile order, and the order walks the grid in bands of `band` row tiles,
-// row index fastest inside a band, so the tiles an XCD runs at one time cover
-// a compact block (about 10 x 10 tiles of 64 x 256): its L2 then serves their
-// activation rows and weight columns to all of them.
+// Tile order: each XCD takes a contiguous run of the tile order
+// (xcd_contiguous), and the order walks the grid in bands of `band` row
+// tiles, row index fastest inside a band, so the tiles an XCD runs at one time
+// cover a compact block (about 10 x 10 tiles of 64 x 256): its L2 then serves
+// their activation rows and weight columns to all of them.
 // Tile counts stay below 2^26 (M * N < 2^40), so 32-bit arithmetic suffices.
-__device__ inline uint32_t xcd_tile(uint32_t b, uint32_t T) {
-    constexpr uint32_t X = 8;
-    const uint32_t xcd = b % X, slot = b / X, q = T / X, r = T % X;
-    return xcd * q + (xcd < r ? xcd : r) + slot;
-}
-
 __device__ inline void tile_coords(uint32_t b, uint32_t ntm, uint32_t ntn, uint32_t band, int64_t& tm,
                                    int64_t& tn) {
-    const uint32_t t = xcd_tile(b, ntm * ntn);
+    const uint32_t t = xcd_contiguous(b, ntm * ntn);
     const uint32_t bi = t / (band * ntn);
     const uint32_t rows = ntm - bi * band < band ? ntm - bi * band : band;
     const uint32_t within = t - bi * band * ntn;

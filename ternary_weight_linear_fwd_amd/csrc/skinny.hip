@@ -25,6 +25,7 @@
 //    the packed layout -- one step ahead of their use.
 // One barrier per step.
 #include "kernels.hpp"
+#include "xcd.hpp"
 
 namespace bl {
 
@@ -78,8 +79,11 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
     const int lane = threadIdx.x & 63;
     Problem p;
     int64_t blk, kb0, kb1, slice = 0;
+    // Each XCD streams a contiguous run of the units (adjacent weight rows,
+    // adjacent output columns).
+    const uint32_t u = xcd_contiguous(blockIdx.x, (uint32_t)a.nunits);
     if constexpr (GROUPED) {
-        const Unit un = a.units[blockIdx.x];
+        const Unit un = a.units[u];
         p = a.problems[un.problem];
         blk = un.group;
         kb0 = 0;
@@ -87,8 +91,8 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
     } else {
         p = a.p;
         const int S = a.sk.S;
-        blk = blockIdx.x / S;
-        slice = blockIdx.x - blk * S;
+        blk = u / S;
+        slice = u - blk * S;
         kb0 = slice * a.sk.kb_per_slice;
         kb1 = kb0 + a.sk.kb_per_slice;
         if (kb1 > p.Kb) kb1 = p.Kb;
