@@ -22,6 +22,10 @@ Also reported:
   decode_m16    the same sweep at M = 16 tokens.
   cpu_baseline  the CPU oracle (plain C, all host threads) on a bounded
                 sample of the same sweep (the first layers at M = 1).
+  ceilings      what this part sustains, measured by the library's probes:
+                a 4 GiB streaming read and an int8 MFMA loop on the prefill
+                operands; roofline and prefill lines also give their
+                fraction of these (frac_of_measured).
 """
 from __future__ import annotations
 
@@ -114,6 +118,8 @@ def bench_prefill(torch, L, S, reps: int):
             torch.cuda.synchronize()
         ms = time_events(torch, fwd, reps)
         own_ms = time_events(torch, fwd_own, reps)
+        if which == 0:
+            mfma_ceiling = bench_mfma_ceiling(torch, L, xq, packed)
         quant_ms = time_events(torch, lambda: L.bitlinear_quantize_act(a[5], M, K, a[0], a[1], a[6], st), reps)
         ops = 2 * M * N * K
         tops = ops / (ms * 1e-3) / 1e12
@@ -122,7 +128,42 @@ def bench_prefill(torch, L, S, reps: int):
                     "quantize_us": round(quant_ms * 1e3, 2),
                     "us_own_row_sums": round(own_ms * 1e3, 2)})
         del Wd, xd, packed, ws, xq, eta, y, xsum
-    return out
+    for r in out:
+        r["frac_of_measured"] = round(r["tops"] / mfma_ceiling["tops"], 4)
+    return out, mfma_ceiling
+
+
+def bench_mfma_ceiling(torch, L, xq, packed) -> dict:
+    """The int8 matrix-core loop (bitlinear_measure_mfma_i8) fed with the first
+    8 KB of these activations and 2 KB of these packed weights: what the
+    MFMAs alone sustain on this part, on this data, with every CU busy."""
+    sink = torch.empty(L.bitlinear_measure_sink_bytes(), dtype=torch.uint8, device="cuda")
+    iters = 40000
+    run = lambda: L.bitlinear_measure_mfma_i8(xq, packed, iters, sink)
+    t_end = time.perf_counter() + 0.2
+    while time.perf_counter() < t_end:
+        run()
+        torch.cuda.synchronize()
+    ms = time_events(torch, run, 5)
+    tops = L.bitlinear_measure_mfma_ops(iters) / (ms * 1e-3) / 1e12
+    return {"tops": round(tops, 1), "frac_of_peak": round(tops / INT8_PEAK_TOPS, 4),
+            "kernel": "mfma_loop_kernel: 2 workgroups per CU, 8 independent v_mfma_i32_32x32x32_i8 "
+                      "per round, operands from the M=2048 K=3200 activations and packed weights"}
+
+
+def bench_stream_ceiling(torch, L) -> dict:
+    """The streaming-read probe (bitlinear_measure_stream_read) over 4 GiB."""
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(L.bitlinear_measure_sink_bytes(), dtype=torch.uint8, device="cuda")
+    run = lambda: L.bitlinear_measure_stream_read(buf, nbytes, sink)
+    for _ in range(3):
+        run()
+    ms = time_events(torch, run, 10)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del buf
+    return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "kernel": "stream_read_kernel: 4 GiB read once, 16-byte non-temporal loads, 4 in flight per lane"}
 
 
 def bench_rmsnorm(torch, L, S, reps: int):
@@ -378,7 +419,7 @@ def main() -> int:
     log(f"device {torch.cuda.get_device_name(0)}; building the sweep ({args.layers} layers)")
     Ms = (1,) if args.no_m16 else (1, 16)
     if args.profile_prefill:
-        for r in bench_prefill(torch, L, S, max(1, args.steps)):
+        for r in bench_prefill(torch, L, S, max(1, args.steps))[0]:
             log(f"prefill {r['gemm']}: {r['us']} us; own row sums {r['us_own_row_sums']} us; "
                 f"quantize {r['quantize_us']} us")
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -389,9 +430,9 @@ def main() -> int:
         return 0
     # The prefill GEMMs are timed first, on a GPU that has not just spent
     # seconds streaming the 17 GB sweep (their own warm-up settles the clocks).
-    prefill = None
+    prefill = mfma_ceiling = None
     if not args.no_prefill and not args.profile_run:
-        prefill = bench_prefill(torch, L, S, max(10, args.steps))
+        prefill, mfma_ceiling = bench_prefill(torch, L, S, max(10, args.steps))
         for r in prefill:
             log(f"prefill {r['gemm']}: {r['us']} us, {r['tops']} TOP/s ({r['frac']:.1%}); "
                 f"own row sums {r['us_own_row_sums']} us; quantize {r['quantize_us']} us")
@@ -420,7 +461,12 @@ def main() -> int:
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     log(f"contraction kernel: {kern_ms:.3f} ms, {achieved:.1f} GB/s ({achieved / HBM_PEAK_GBS:.1%})")
 
-    extra = {}
+    stream_ceiling = bench_stream_ceiling(torch, L)
+    log(f"measured ceilings: stream read {stream_ceiling['gbs']} GB/s"
+        + (f", int8 MFMA loop {mfma_ceiling['tops']} TOP/s" if mfma_ceiling else ""))
+    extra = {"ceilings": {"stream_read": stream_ceiling}}
+    if mfma_ceiling:
+        extra["ceilings"]["mfma_i8"] = mfma_ceiling
     if not args.no_m16:
         for _ in range(2):
             sw.step(16)
@@ -480,7 +526,8 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
                      "kernel": "gemv_dot4_kernel<1, grouped> (contraction + fused dequant)",
-                     "kernel_ms": round(kern_ms, 4), "algorithmic_bytes": kern_bytes},
+                     "kernel_ms": round(kern_ms, 4), "algorithmic_bytes": kern_bytes,
+                     "frac_of_measured": round(achieved / stream_ceiling["gbs"], 4)},
         "cpu_baseline": cpu,
     }
     line.update(extra)

@@ -84,6 +84,11 @@ _SIGS = {
     "bitlinear_grouped_plan_init": ([ctypes.POINTER(BitLinearProblem), _I32, _I64, _P, _SZ,
                                      ctypes.POINTER(BitLinearGroupedPlan), _P], ctypes.c_int),
     "bitlinear_forward_grouped": ([ctypes.POINTER(BitLinearGroupedPlan), _P], ctypes.c_int),
+    # measurement probes (include/bitlinear_measure.h)
+    "bitlinear_measure_sink_bytes": ([], _SZ),
+    "bitlinear_measure_stream_read": ([_P, _SZ, _P, _P], ctypes.c_int),
+    "bitlinear_measure_mfma_i8": ([_P, _P, _I32, _P, _P], ctypes.c_int),
+    "bitlinear_measure_mfma_ops": ([_I32], ctypes.c_double),
 }
 
 for _name, (_args, _res) in _SIGS.items():
@@ -289,3 +294,22 @@ def bitlinear_grouped_plan_init(problems, count: int, M: int, table, table_bytes
 def bitlinear_forward_grouped(plan: BitLinearGroupedPlan, stream=None) -> None:
     _check(_lib.bitlinear_forward_grouped(ctypes.byref(plan), _stream(stream)),
            "bitlinear_forward_grouped")
+
+
+# ------------------------------------------------- measurement probes (ceilings)
+def bitlinear_measure_sink_bytes() -> int:
+    return _lib.bitlinear_measure_sink_bytes()
+
+
+def bitlinear_measure_stream_read(buf, nbytes: int, sink, stream=None) -> None:
+    _check(_lib.bitlinear_measure_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)),
+           "bitlinear_measure_stream_read")
+
+
+def bitlinear_measure_mfma_i8(xq, packed, iters: int, sink, stream=None) -> None:
+    _check(_lib.bitlinear_measure_mfma_i8(_ptr(xq), _ptr(packed), iters, _ptr(sink), _stream(stream)),
+           "bitlinear_measure_mfma_i8")
+
+
+def bitlinear_measure_mfma_ops(iters: int) -> float:
+    return _lib.bitlinear_measure_mfma_ops(iters)

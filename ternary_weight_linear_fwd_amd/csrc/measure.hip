@@ -1,0 +1,133 @@
+// measure.hip -- the ceiling probes declared in include/bitlinear_measure.h:
+// an HBM streaming-read kernel and an int8 matrix-core loop, each doing only
+// that one thing, so that the forward kernels can be reported as a fraction
+// of what this part actually sustains as well as of its published peaks.
+#include "bitlinear_measure.h"
+#include "kernels.hpp"
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kSinkWords = 16384;       // 64 KB: one word per workgroup
+constexpr int kStreamBlocks = 4096;     // 16 workgroups per CU on 256 CUs
+
+__device__ inline uint32_t wave_xor(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v ^= (uint32_t)__shfl_xor((int)v, off, 64);
+    return v;
+}
+
+// Grid-stride read of n16 16-byte chunks: consecutive lanes take consecutive
+// chunks (one contiguous 1 KB wave load), four loads in flight per pass.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, uint64_t n16,
+                                                          uint32_t* __restrict__ sink) {
+    const uint64_t stride = (uint64_t)gridDim.x * 256;
+    uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t x = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = ldnt_u4(p + i), b = ldnt_u4(p + i + stride);
+        const uint4 c = ldnt_u4(p + i + 2 * stride), d = ldnt_u4(p + i + 3 * stride);
+        x ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = ldnt_u4(p + i);
+        x ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    __shared__ uint32_t part[4];
+    x = wave_xor(x);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+// Eight A fragments and eight expanded weight words per lane, loaded once;
+// each round issues the eight independent MFMAs (four accumulators) and
+// nothing else.
+__global__ __launch_bounds__(256, 2) void mfma_loop_kernel(const int8_t* __restrict__ xq,
+                                                           const uint8_t* __restrict__ packed, int iters,
+                                                           int32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    v4i a[8], b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = *reinterpret_cast<const v4i*>(xq + (j * 64 + lane) * 16);
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(packed + (j * 64 + lane) * 4);
+        b[j] = v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+                   (int)((w >> 6) & 0x03030303u)};
+    }
+    v16i acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][e] = 0;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[j], b[j], acc[j & 3], 0, 0, 0);
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += (uint32_t)acc[t][e];
+    __shared__ uint32_t part[4];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += (uint32_t)__shfl_xor((int)s, off, 64);
+    if (lane == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = (int32_t)(part[0] + part[1] + part[2] + part[3]);
+}
+
+static int current_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+static int mfma_blocks() {
+    const int b = 2 * current_cus();
+    return b < kSinkWords ? b : kSinkWords;
+}
+
+}  // namespace bl
+
+using namespace bl;
+
+extern "C" {
+
+size_t bitlinear_measure_sink_bytes(void) { return (size_t)kSinkWords * sizeof(uint32_t); }
+
+int bitlinear_measure_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink || bytes == 0 || bytes % 16 != 0) return BITLINEAR_EINVAL;
+    if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+        return BITLINEAR_EINVAL;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamBlocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const uint4*>(buf), (uint64_t)(bytes / 16), sink);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
+
+int bitlinear_measure_mfma_i8(const int8_t* xq, const uint8_t* packed, int32_t iters, int32_t* sink,
+                              void* stream) {
+    if (!xq || !packed || !sink || iters < 1 || iters > (1 << 24)) return BITLINEAR_EINVAL;
+    if (reinterpret_cast<uintptr_t>(xq) % 16 != 0 || reinterpret_cast<uintptr_t>(packed) % 4 != 0 ||
+        reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+        return BITLINEAR_EINVAL;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3(mfma_blocks()), dim3(256), 0, (hipStream_t)stream, xq, packed,
+                       (int)iters, sink);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
+
+double bitlinear_measure_mfma_ops(int32_t iters) {
+    if (iters < 1 || iters > (1 << 24)) return 0.0;
+    // workgroups x 4 wavefronts x iters x 8 MFMAs x (32 * 32 * 32 multiply-adds = 65536 ops)
+    return (double)mfma_blocks() * 4.0 * (double)iters * 8.0 * 65536.0;
+}
+
+}  // extern "C"

@@ -11,6 +11,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 CSRC = os.path.join(ROOT, "ternary_weight_linear_fwd_amd", "csrc")
 
 bl = pytest.importorskip("ternary_weight_linear_fwd_amd.bitlinear",
@@ -18,9 +20,11 @@ bl = pytest.importorskip("ternary_weight_linear_fwd_amd.bitlinear",
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_function_is_exported():
@@ -38,7 +42,8 @@ def test_every_declared_function_is_exported():
 @pytest.mark.parametrize("lang,compiler", [("c", "gcc"), ("c++", "g++")])
 def test_header_compiles(lang, compiler, tmp_path):
     src = tmp_path / ("t." + ("c" if lang == "c" else "cpp"))
-    src.write_text('#include "bitlinear.h"\nint main(void){ bitlinear_problem p; (void)p; '
+    src.write_text('#include "bitlinear.h"\n#include "bitlinear_measure.h"\n'
+                   'int main(void){ bitlinear_problem p; (void)p; '
                    'return (int)sizeof(bitlinear_grouped_plan) > 0 ? 0 : 1; }\n')
     subprocess.check_call([compiler, "-std=c99" if lang == "c" else "-std=c++11", "-Wall",
                            "-Werror", "-pedantic", "-I", os.path.dirname(HEADER), "-fsyntax-only",
@@ -117,6 +122,14 @@ def test_validation_before_any_device_work():
     # prefill sizes: the row sums need the workspace
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, FAKE, 256, None) == L.BITLINEAR_EWORKSPACE
+    # measurement probes
+    assert L.bitlinear_measure_sink_bytes() >= 4 * 2048
+    assert _rc("bitlinear_measure_stream_read", None, 1024, FAKE, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_measure_stream_read", FAKE, 1000, FAKE, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_measure_stream_read", FAKE + 8, 1024, FAKE, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_measure_mfma_i8", FAKE, FAKE, 0, FAKE, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_measure_mfma_i8", FAKE, None, 10, FAKE, None) == L.BITLINEAR_EINVAL
+    assert L.bitlinear_measure_mfma_ops(0) == 0.0
     # forward with row sums: the sums are required; otherwise as bitlinear_forward
     assert _rc("bitlinear_forward_xsum", FAKE, FAKE, None, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_forward_xsum", FAKE, FAKE, FAKE + 2, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
