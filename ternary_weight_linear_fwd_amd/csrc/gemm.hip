@@ -4,21 +4,22 @@
 // contraction of [P2] "3. Additive Integer Accumulation" is a dense integer
 // product; it runs on v_mfma_i32_32x32x32_i8 with int32 accumulation.
 //
-// Workgroup tile: BM = 32*MT token rows x 256 weight rows (output columns).
-// Four wavefronts sit side by side in N; each owns all BM rows x 64 columns
-// as MT x 2 MFMA tiles of 32 x 32, so every packed weight word is expanded
+// Workgroup tile: BM = 32*MT token rows x 128*NT weight rows (output
+// columns), MT x NT in {2 x 2, 3 x 3, 4 x 2}, chosen per shape.  Four
+// wavefronts sit side by side in N; each owns all BM rows x 32*NT columns as
+// MT x NT MFMA tiles of 32 x 32, so every packed weight word is expanded
 // once per workgroup.  The K loop advances 128 (two 64-k blocks) per step
-// through a ring of three LDS stages, keeping two steps in flight ahead of
-// the one being computed.  Both operands arrive by direct global->LDS
-// loads (global_load_lds_dwordx4, 1 KB per wave instruction) whose completion
-// the kernel tracks itself: an explicit vmcnt wait and one barrier per step,
-// with no register destinations for the compiler to wait on.
-//  * A (int8 activations): BM rows x 128 bytes per stage.  Chunk c (16 bytes)
-//    of row r is stored at chunk c ^ ((r >> 1) & 7): the 16 rows one
-//    ds_read_b128 phase serves land on distinct banks, and each wave's 1 KB
-//    DMA stays contiguous.
-//  * B (packed codes): each wavefront copies its own two 1 KB blocks (64 rows
-//    x 64 k) exactly as they lie in the packed layout.
+// through a ring of three stages (four for 128-row tiles), keeping the next
+// steps in flight while one is computed.  The kernel tracks the completion
+// of its own loads: an explicit vmcnt wait and one barrier per step.
+//  * A (int8 activations) arrives by direct global->LDS loads
+//    (global_load_lds_dwordx4, 1 KB per wave instruction): BM rows x 128
+//    bytes per stage.  Chunk c (16 bytes) of row r is stored at chunk
+//    c ^ ((r >> 1) & 7): the 16 rows one ds_read_b128 phase serves land on
+//    distinct banks, and each wave's 1 KB DMA stays contiguous.
+//  * B (packed codes) is private to each wavefront, so it goes straight to
+//    registers (one 16-byte load per lane and column tile per step, a ring
+//    of register sets matching the LDS stages) and is expanded there.
 // Lane (n, g) reads row n's 16-byte chunk of k-block 2*step + g; word d of it
 // feeds MFMA group d, whose 32 k are the two lane groups' 16-k runs, and A is
 // read in the same (g, d) order (the order of k inside a reduction is free;
@@ -27,13 +28,16 @@
 // The codes go to the MFMA as they are: with c = w + 1 in {0, 1, 2} (field j
 // of a word is (w >> 2j) & 0x03030303),
 //     sum_k x_k w_k = sum_k x_k c_k - sum_k x_k .
-// The row sums sum_k x_k are taken from the same LDS fragments (v_dot4
-// against ones; wavefront w sums word group w of every step), so every k
-// whose code is 01 -- pads inside the last block, blocks past the end (forced
-// to 01), and k past K read from clamped addresses -- contributes equally to
-// both terms and cancels.  Raw codes also toggle far fewer multiplier bits
-// than -1/0/+1 bytes, which lets the matrix cores hold a higher clock.  int32 arithmetic wraps, so the difference is exact whenever the
-// result fits (|y_int| <= 127 K < 2^31).
+// The row sums sum_k x_k are either given (the activation quantizer writes
+// them; every k at or past K then gets code 00, so it adds nothing) or taken
+// from the same LDS fragments (v_dot4 against ones; wavefront w sums word
+// group w of every step), in which case every k whose code is 01 -- pads
+// inside the last block, blocks past the end (forced to 01), and k past K
+// read from clamped addresses -- contributes equally to both terms and
+// cancels.  Raw codes also toggle far fewer multiplier bits than -1/0/+1
+// bytes, which lets the matrix cores hold a higher clock.  int32 arithmetic
+// wraps, so the difference is exact whenever the result fits
+// (|y_int| <= 127 K < 2^31).
 // Epilogue: y = float(y_int) * ((eta[m] * gamma) / 127), fused.
 #include <atomic>
 
@@ -345,8 +349,8 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     static_assert(NS == 3 || NS == 4, "ring of three or four stages");
     using Ctx = PrefillCtx<MT, NT>;
     constexpr int BM = Ctx::BM;
-    // Three stages, each its own LDS object, so that the compiler can tell a
-    // read of one stage from the loads in flight into the others.
+    // Up to four stages, each its own LDS object, so that the compiler can
+    // tell a read of one stage from the loads in flight into the others.
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[Ctx::AStage];
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[Ctx::AStage];
     __shared__ __attribute__((aligned(1024))) uint8_t stage2[Ctx::AStage];
