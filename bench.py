@@ -302,9 +302,10 @@ COPY_BYTES = 1 << 30
 
 def profile_run(torch, L, sw, args) -> int:
     """Kernels for rocprofv3: full steps, contraction-only launches, a calibration copy."""
+    M = args.profile_m
     for _ in range(max(1, args.steps)):
-        sw.step(1)
-    plan_c, _table = contraction_only_plan(sw, 1)
+        sw.step(M)
+    plan_c, _table = contraction_only_plan(sw, M)
     for _ in range(max(1, args.steps)):
         L.bitlinear_forward_grouped(plan_c)
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -312,7 +313,7 @@ def profile_run(torch, L, sw, args) -> int:
     for _ in range(3):
         dst.copy_(src)   # reads and writes exactly COPY_BYTES each
     torch.cuda.synchronize()
-    log(f"profile run done: contraction bytes per launch {sw.contraction_bytes(1)}")
+    log(f"profile run done: M={M}, contraction bytes per launch {sw.contraction_bytes(M)}")
     return 0
 
 
@@ -347,8 +348,9 @@ def summarize_profile(root: str) -> str:
         per = {}
         for r in rows:
             key = "copy" if "copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower() \
-                else ("contraction" if ("gemv_dot4_kernel" in r["Kernel_Name"]
-                                        or "gemm_prefill_kernel" in r["Kernel_Name"]) else None)
+                else ("contraction" if any(k in r["Kernel_Name"] for k in
+                                           ("gemv_dot4_kernel", "skinny_mfma_kernel", "gemm_prefill_kernel"))
+                      else None)
             if key:
                 per.setdefault(key, []).append(float(r["Counter_Value"]))
         if "copy" in per and "contraction" in per:
@@ -394,6 +396,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-m16", action="store_true")
+    ap.add_argument("--profile-m", type=int, default=1, choices=(1, 16),
+                    help="token count of the --profile-run sweep")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run for rocprofv3: the M=1 sweep, the contraction kernel alone and a "
                          "1 GiB copy whose counters calibrate FETCH_SIZE/WRITE_SIZE")
@@ -418,6 +422,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"device {torch.cuda.get_device_name(0)}; building the sweep ({args.layers} layers)")
     Ms = (1,) if args.no_m16 else (1, 16)
+    if args.profile_run:
+        Ms = (args.profile_m,)
     if args.profile_prefill:
         for r in bench_prefill(torch, L, S, max(1, args.steps))[0]:
             log(f"prefill {r['gemm']}: {r['us']} us; own row sums {r['us_own_row_sums']} us; "

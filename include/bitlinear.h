@@ -300,7 +300,7 @@ typedef struct bitlinear_grouped_plan {
     int32_t count;         /* number of problems */
     int32_t M;             /* tokens per problem */
     int32_t kernel;        /* contraction kernel variant chosen by the planner */
-    int32_t max_K;
+    int32_t max_K;         /* longest K among the problems */
 } bitlinear_grouped_plan;
 
 /* Device bytes the work table for these problems needs (host only). */
