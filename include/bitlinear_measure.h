@@ -25,10 +25,11 @@ extern "C" {
 size_t bitlinear_measure_sink_bytes(void);
 
 /*
- * HBM streaming-read ceiling: read `bytes` bytes of `buf` exactly once with
- * 16-byte non-temporal loads spread over every CU (each wavefront keeps four
- * loads in flight), fold them with XOR and write one word per workgroup to
- * `sink`.  Achieved bandwidth = bytes / kernel time.
+ * HBM streaming-read ceiling: read `bytes` bytes of `buf` exactly once (four
+ * wavefronts per SIMD, each streaming one contiguous run with 16-byte
+ * non-temporal loads, sixteen in flight per lane), fold them with XOR and
+ * write one word per workgroup to `sink`.  Achieved bandwidth = bytes /
+ * kernel time.
  *   buf    16-byte aligned device buffer (in); bytes a multiple of 16, > 0
  *   sink   bitlinear_measure_sink_bytes() bytes (out)
  * BITLINEAR_EINVAL for a null or misaligned pointer or a bad size.

@@ -17,6 +17,7 @@
 // accumulator), so one packed word costs 5 VALU ops + 4 dot4 per token.  The
 // activation bytes are wave-uniform and come from scalar loads.
 #include "kernels.hpp"
+#include "xcd.hpp"
 
 namespace bl {
 
@@ -78,7 +79,8 @@ template <int M, bool GROUPED, int U>
 __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int64_t u = (int64_t)blockIdx.x * kGemvWaves + wave;
+    // Each XCD streams a contiguous run of the units (adjacent weight rows).
+    const int64_t u = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * kGemvWaves + wave;
     if (u >= a.nunits) return;
 
     Problem p;
@@ -232,7 +234,9 @@ int launch_gemv(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
 
 template <int M>
 static void launch_grouped(const GemvArgs& a, int64_t blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((gemv_dot4_kernel<M, true, 4>), dim3((unsigned)blocks), dim3(256), 0,
+    // Eight k-blocks per batch (8 KB per wavefront in flight): the grouped
+    // launch is one long stream, where the deeper queue pays.
+    hipLaunchKernelGGL((gemv_dot4_kernel<M, true, 8>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, a);
 }
 

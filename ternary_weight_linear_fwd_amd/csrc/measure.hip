@@ -11,7 +11,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kSinkWords = 16384;       // 64 KB: one word per workgroup
-constexpr int kStreamBlocks = 4096;     // 16 workgroups per CU on 256 CUs
+constexpr int kStreamWavesPerSimd = 4;  // resident wavefronts of the read probe
+constexpr int kStreamDepth = 16;        // 16-byte loads in flight per lane
 
 __device__ inline uint32_t wave_xor(uint32_t v) {
 #pragma unroll
@@ -19,25 +20,34 @@ __device__ inline uint32_t wave_xor(uint32_t v) {
     return v;
 }
 
-// Grid-stride read of n16 16-byte chunks: consecutive lanes take consecutive
-// chunks (one contiguous 1 KB wave load), four loads in flight per pass.
+// Each wavefront streams one contiguous run of the buffer (1 KB wave loads,
+// kStreamDepth of them in flight per lane, non-temporal), the way the decode
+// kernels stream their weight rows; of the patterns tried on this part this
+// one reads fastest.  Runs are whole 1 KB rows of chunks except the last.
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, uint64_t n16,
                                                           uint32_t* __restrict__ sink) {
-    const uint64_t stride = (uint64_t)gridDim.x * 256;
-    uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    const uint64_t waves = (uint64_t)gridDim.x * 4;
+    const uint64_t w = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const uint64_t lane = threadIdx.x & 63;
+    const uint64_t per = ((n16 + waves - 1) / waves + 63) & ~uint64_t(63);   // chunks per wavefront
+    const uint64_t begin = w * per;
+    const uint64_t end = begin + per < n16 ? begin + per : n16;
     uint32_t x = 0;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = ldnt_u4(p + i), b = ldnt_u4(p + i + stride);
-        const uint4 c = ldnt_u4(p + i + 2 * stride), d = ldnt_u4(p + i + 3 * stride);
-        x ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+    uint64_t j = begin;
+    for (; j + 64 * kStreamDepth <= end; j += 64 * kStreamDepth) {
+        uint4 v[kStreamDepth];
+#pragma unroll
+        for (int u = 0; u < kStreamDepth; ++u) v[u] = ldnt_u4(p + j + u * 64 + lane);
+#pragma unroll
+        for (int u = 0; u < kStreamDepth; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
-    for (; i < n16; i += stride) {
-        const uint4 a = ldnt_u4(p + i);
+    for (j += lane; j < end; j += 64) {
+        const uint4 a = ldnt_u4(p + j);
         x ^= a.x ^ a.y ^ a.z ^ a.w;
     }
     __shared__ uint32_t part[4];
     x = wave_xor(x);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    if (lane == 0) part[threadIdx.x >> 6] = x;
     __syncthreads();
     if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
@@ -87,6 +97,11 @@ static int current_cus() {
     return cus;
 }
 
+static int stream_blocks() {
+    const int b = current_cus() * kStreamWavesPerSimd;   // 4 SIMDs per CU, 4 waves per workgroup
+    return b < kSinkWords ? b : kSinkWords;
+}
+
 static int mfma_blocks() {
     const int b = 2 * current_cus();
     return b < kSinkWords ? b : kSinkWords;
@@ -105,7 +120,7 @@ int bitlinear_measure_stream_read(const void* buf, size_t bytes, uint32_t* sink,
     if (reinterpret_cast<uintptr_t>(buf) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
         return BITLINEAR_EINVAL;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamBlocks), dim3(256), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL(stream_read_kernel, dim3(stream_blocks()), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const uint4*>(buf), (uint64_t)(bytes / 16), sink);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
