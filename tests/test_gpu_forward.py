@@ -180,3 +180,41 @@ def test_forward_xsum_is_read(M, N, K):
     yq, y_intq = forward_xsum(xq[:16], eta[:16], xsum[:16] + d[:16], packed, 0.02, N)
     assert np.array_equal(y_intq, y_int_ref[:16])
     assert np.array_equal(yq.view(np.uint32), y_ref[:16].view(np.uint32))
+
+
+# Every call only queues work on the stream it is given: the fused forward on
+# two non-default streams at once (decode split-K, streaming MFMA and prefill
+# sizes, each with its own workspace), while a third stream is kept busy,
+# gives the same bits as the default stream.
+def test_non_default_streams():
+    torch = torch_cuda()
+    L = bl()
+    N, K = 4096, 4160
+    Wt = S.random_ternary(31, N, K)
+    packed, bad = pack_ternary(Wt)
+    assert bad == 0
+    cases = [(2, S.random_x(32, 2, K)), (48, S.random_x(33, 48, K)), (300, S.random_x(34, 300, K))]
+    ref = []
+    for M, x in cases:
+        ref.append(forward_f32(x, packed, 0.02, N))
+    busy = torch.cuda.Stream()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    big = torch.randn(4096, 4096, device="cuda")
+    outs = []
+    torch.cuda.synchronize()
+    with torch.cuda.stream(busy):
+        for _ in range(4):
+            big = big @ big.T * 1e-3
+    for i, (M, x) in enumerate(cases):
+        st = streams[i % 2]
+        with torch.cuda.stream(st):
+            xd = to_dev(x)
+            ws_bytes = L.bitlinear_workspace_bytes(M, N, K)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            L.bitlinear_forward_f32(xd, packed, 0.02, M, N, K, y, ws, ws_bytes, stream=st)
+            outs.append((y, xd, ws))
+    torch.cuda.synchronize()
+    for (M, _), r, (y, _, _) in zip(cases, ref, outs):
+        say(f"stream case M={M}")
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), r.view(np.uint32))
