@@ -179,8 +179,14 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
                 if (!GROUPED && a.sk.S > 1) {
                     a.sk.partial[(slice * M + m) * N + n] = v;
                 } else {
-                    p.y[m * N + n] = dequant(v, s);
-                    if (p.y_int) p.y_int[m * N + n] = v;
+                    // Device-scope stores write through the XCD's L2: the
+                    // outputs then leave at once instead of as dirty lines
+                    // evicted later into the weight stream (measured faster
+                    // at 16 tokens; relaxed, so values and order are those
+                    // of plain stores).
+                    __hip_atomic_store(p.y + m * N + n, dequant(v, s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (p.y_int)
+                        __hip_atomic_store(p.y_int + m * N + n, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
