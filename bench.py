@@ -48,6 +48,23 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+def system_info(torch) -> dict:
+    """The part, its runtime and the host CPU the numbers were taken on."""
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),
+            "cus": props.multi_processor_count, "hip": torch.version.hip, "torch": torch.__version__,
+            "cpu": cpu, "host_threads": len(os.sched_getaffinity(0))}
+
+
 def time_events(torch, fn, reps: int) -> float:
     """Mean milliseconds per call of fn() over reps calls, HIP events on the current stream."""
     stream = torch.cuda.current_stream()
@@ -536,6 +553,7 @@ def main() -> int:
                      "kernel_ms": round(kern_ms, 4), "algorithmic_bytes": kern_bytes,
                      "frac_of_measured": round(achieved / stream_ceiling["gbs"], 4)},
         "cpu_baseline": cpu,
+        "system": system_info(torch),
     }
     line.update(extra)
     print(json.dumps(line), flush=True)
