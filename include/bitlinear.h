@@ -96,7 +96,8 @@ size_t bitlinear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   x    [M][K] float32 (in)
  *   xq   [M][K] int8    (out)
  *   eta  [M]    float32 (out)
- *   xsum [M]    int32   (out, may be NULL): sum over k of xq[m][k]
+ *   xsum [M]    int32   (out, may be NULL): sum over k of xq[m][k] (int32,
+ *        wrapping), the row sums bitlinear_forward_xsum takes
  */
 int bitlinear_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta,
                            int32_t* xsum, void* stream);
