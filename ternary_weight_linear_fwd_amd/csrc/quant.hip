@@ -8,15 +8,16 @@
 // butterflies (DPP/permute) and one LDS exchange across the workgroup's
 // waves; pass 2 quantizes with one IEEE multiply, one correctly rounded
 // division and round-half-even per element and stores four int8 per dword.
-// Rows whose float4 chunks fit the register budget (R per thread) are read
-// from HBM once; longer rows are read a second time (from L2/MALL).
+// The first R float4 chunks per thread stay in registers between the
+// passes (read once from HBM); chunks beyond are read a second time (from
+// L2/MALL).  NT: non-temporal loads for the cached chunks.
 #include "kernels.hpp"
 #include "quant_row.hpp"
 
 namespace bl {
 
 // Quantize one row of K floats (K % 4 == 0, 16-byte aligned).
-template <int THREADS, int R>
+template <int THREADS, int R, bool NT = true>
 __device__ inline void quant_row(const float* __restrict__ x, int K, int8_t* __restrict__ xq,
                                  float* __restrict__ eta_out, int32_t* __restrict__ xsum_out) {
     __shared__ float redf[THREADS / 64];
@@ -32,15 +33,14 @@ __device__ inline void quant_row(const float* __restrict__ x, int K, int8_t* __r
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int i = t + r * THREADS;
-            cache[r] = i < n4 ? ldnt_f4(&x4[i]) : make_float4(0, 0, 0, 0);
+            cache[r] = i < n4 ? (NT ? ldnt_f4(&x4[i]) : x4[i]) : make_float4(0, 0, 0, 0);
             amax = fmaxf(amax, fmaxf(fmaxf(fabsf(cache[r].x), fabsf(cache[r].y)),
                                      fmaxf(fabsf(cache[r].z), fabsf(cache[r].w))));
         }
-    } else {
-        for (int i = t; i < n4; i += THREADS) {
-            float4 v = x4[i];
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        }
+    }
+    for (int i = t + R * THREADS; i < n4; i += THREADS) {
+        float4 v = x4[i];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
     amax = block_max<THREADS>(amax, redf);
     const float eta = amax < kScaleFloor ? kScaleFloor : amax;
@@ -52,9 +52,8 @@ __device__ inline void quant_row(const float* __restrict__ x, int K, int8_t* __r
             const int i = t + r * THREADS;
             if (i < n4) q4[i] = quant4(cache[r], eta, sum);
         }
-    } else {
-        for (int i = t; i < n4; i += THREADS) q4[i] = quant4(x4[i], eta, sum);
     }
+    for (int i = t + R * THREADS; i < n4; i += THREADS) q4[i] = quant4(x4[i], eta, sum);
     if (t == 0) eta_out[0] = eta;
     if (xsum_out) {
         sum = block_sum<THREADS>(sum, redi);
@@ -71,10 +70,13 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(const float* __rest
     quant_row<THREADS, R>(x + m * K, K, xq + m * K, eta + m, xsum ? xsum + m : nullptr);
 }
 
-// Grouped: one workgroup per row descriptor.
-__global__ __launch_bounds__(256) void quant_rows_grouped_kernel(const QuantRow* __restrict__ rows) {
+// Grouped: one workgroup per row descriptor; rows of up to 32768 floats stay
+// in registers (512 threads x 16 chunks), longer ones are read twice.  Plain
+// loads measured faster than non-temporal ones over the decode step.
+constexpr int kGroupedQuantThreads = 512;
+__global__ __launch_bounds__(kGroupedQuantThreads) void quant_rows_grouped_kernel(const QuantRow* __restrict__ rows) {
     const QuantRow r = rows[blockIdx.x];
-    quant_row<256, 0>(r.x, r.K, r.xq, r.eta, nullptr);
+    quant_row<kGroupedQuantThreads, 16, false>(r.x, r.K, r.xq, r.eta, nullptr);
 }
 
 int launch_quantize(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta, int32_t* xsum,
@@ -97,7 +99,8 @@ int launch_quantize(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta
 
 int launch_quantize_grouped(const QuantRow* rows, int64_t nrows, hipStream_t stream) {
     if (nrows == 0) return BITLINEAR_OK;
-    hipLaunchKernelGGL(quant_rows_grouped_kernel, dim3((unsigned)nrows), dim3(256), 0, stream, rows);
+    hipLaunchKernelGGL(quant_rows_grouped_kernel, dim3((unsigned)nrows), dim3(kGroupedQuantThreads), 0, stream,
+                       rows);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
 }

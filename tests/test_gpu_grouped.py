@@ -82,3 +82,39 @@ def test_c4_sweep_full_size_sampled():
             y = sw.y[key].cpu().numpy()
             assert_y_close(y, y_ref)
             assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+
+
+# Rows of very different lengths in one plan: K past the quantizer's register
+# budget (32768 floats: read twice), tiny K, and ordinary K; x̃ and eta from the
+# grouped quantizer and the integer sums bit-exact.
+@pytest.mark.parametrize("M", [2, 20])
+def test_grouped_mixed_row_lengths(M):
+    torch = torch_cuda()
+    L = bl()
+    shapes = [(128, 33792), (200, 64), (70, 16), (96, 4160)]
+    specs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        x_np = S.random_x(900 + 10 * M + i, M, K, "t3")
+        Wt = S.random_ternary(950 + i, N, K)
+        packed = torch.empty(L.bitlinear_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+        L.bitlinear_pack_ternary(torch.from_numpy(Wt).cuda(), N, K, packed)
+        xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        eta = torch.empty(M, dtype=torch.float32, device="cuda")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        y_int = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        specs.append(dict(x=torch.from_numpy(x_np).cuda(), xq=xq, eta=eta, packed=packed, y=y, y_int=y_int,
+                          gamma=np.float32(0.03), N=N, K=K))
+        refs.append((x_np, Wt))
+    probs = L.make_problems(specs)
+    tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
+    table = torch.empty(tb, dtype=torch.uint8, device="cuda")
+    plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
+    L.bitlinear_forward_grouped(plan)
+    torch.cuda.synchronize()
+    for s, (x_np, Wt) in zip(specs, refs):
+        say(f"mixed rows M={M} N={s['N']} K={s['K']}")
+        y_ref, xq_ref, eta_ref, y_int_ref = oracle.forward(x_np, Wt, np.float32(0.03), threads=THREADS)
+        assert np.array_equal(s["xq"].cpu().numpy(), xq_ref)
+        assert np.array_equal(s["eta"].cpu().numpy().view(np.uint32), eta_ref.view(np.uint32))
+        assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref)
+        assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
