@@ -509,14 +509,19 @@ static int gemm_bn(int64_t M) { (void)M; return kPreBN; }
 // on grids four or more rounds deep, where 128 x 256 tiles (each weight word
 // expanded for twice the rows) measure faster.  E.g. on 256 CUs: M = 2048,
 // N = 8640 takes 96 x 384 tiles (506 in one round) over 64 x 256 ones (1088:
-// up to five per CU); M = 2048, N = 3200 keeps 64 x 256.
+// up to five per CU); M = 2048, N = 3200 keeps 64 x 256.  Grids that would
+// leave CUs idle even with 64 x 256 tiles (batched decode, M = 65 .. a few
+// hundred) take 32 x 128 tiles: four times the workgroups, each with a
+// quarter of the K loop's MFMAs per step (M = 128, N = 4096, K = 11008:
+// 32.7 -> 20.2 us).
 struct TileCfg {
     int mt, nt;
 };
 
 static TileCfg prefill_tile(int64_t M, int64_t N, int cus) {
     auto rounds = [&](TileCfg t) { return ceil_div(ceil_div(M, 32 * t.mt) * ceil_div(N, 128 * t.nt), cus); };
-    const TileCfg small{2, 2}, wide{3, 3}, tall{4, 2};
+    const TileCfg small{2, 2}, wide{3, 3}, tall{4, 2}, tiny{1, 1};
+    if (ceil_div(M, 64) * ceil_div(N, 256) < cus) return tiny;
     TileCfg best = small;
     int64_t best_cost = rounds(small) * 4;
     if (rounds(wide) * 9 < best_cost) {
@@ -596,12 +601,13 @@ int launch_gemm_xsum(const Problem& p, int64_t M, const int32_t* xsum, hipStream
     const TileCfg t = prefill_tile(M, p.N, device_cus());
     if (t.mt == 3) launch_single<3, 3, true>(a, stream);
     else if (t.mt == 4) launch_single<4, 2, true>(a, stream);
+    else if (t.mt == 1) launch_single<1, 1, true>(a, stream);
     else launch_single<2, 2, true>(a, stream);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
 }
 
-// Without given row sums: the 64 x 256 and 128 x 256 tiles sum the rows
+// Without given row sums: the 32 x 128, 64 x 256 and 128 x 256 tiles sum the rows
 // from their activation tiles on the way (a few percent of their time);
 // the 96 x 384 tile has no registers to spare for that, so a pre-pass sums
 // them into the workspace (about M * K bytes read, the operand's first
@@ -618,6 +624,7 @@ int launch_gemm(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
     a.p = p;
     a.M = M;
     if (t.mt == 4) launch_single<4, 2, false>(a, stream);
+    else if (t.mt == 1) launch_single<1, 1, false>(a, stream);
     else launch_single<2, 2, false>(a, stream);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
