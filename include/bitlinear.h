@@ -186,8 +186,11 @@ int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t
  *   y      [M][N] float32 (out)
  *   y_int  [M][N] int32   (out, may be NULL): the exact integer sums
  *   ws     workspace of bitlinear_workspace_bytes(M, N, K) bytes, 256-byte
- *          aligned: split-K partial sums at decode sizes, room for the
- *          activation row sums at prefill sizes (M > 64)
+ *          aligned: split-K partial sums for the decode kernels, room for
+ *          the activation row sums for the tiled kernel
+ * Kernel by size: M <= 4 the dot4 GEMV; M > 64 the tiled int8-MFMA kernel;
+ * 4 < M <= 64 the streaming MFMA kernel, except 16 < M <= 64 with
+ * ceil(M/32) * ceil(N/128) >= CUs / 3, which also takes the tiled kernel.
  */
 int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
                       int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,
@@ -195,7 +198,7 @@ int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed,
 
 /*
  * bitlinear_forward with the activation row sums supplied: the same result,
- * bit for bit, when xsum is right.  The prefill contraction (M > 64) of
+ * bit for bit, when xsum is right.  The tiled contraction (see above) of
  * [P2] "3. Additive Integer Accumulation" runs on the stored weight codes
  * c = w + 1 in {0, 1, 2}: sum_k xq w = sum_k xq c - sum_k xq, so it needs
  * each row's sum; the quantizer produces those sums in the same pass that
@@ -204,7 +207,7 @@ int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed,
  *   xsum [M] int32 (in): xsum[m] = sum over k < K of xq[m][k], exactly as
  *        bitlinear_quantize_act or bitlinear_rmsnorm_quantize_act write it.
  *        Not checked: a wrong row sum shifts that row's y_int by the error.
- *        The decode kernels (M <= 64) do not read it.
+ *        The decode kernels (dot4 and streaming MFMA) do not read it.
  *   other arguments, workspace and errors as bitlinear_forward.
  */
 int bitlinear_forward_xsum(const int8_t* xq, const float* eta, const int32_t* xsum,

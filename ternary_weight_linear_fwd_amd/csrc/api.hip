@@ -47,10 +47,23 @@ int check_sizes(int64_t M, int64_t N, int64_t K) {
     return BITLINEAR_OK;
 }
 
+// Contraction kernel for a single problem: the dot4 GEMV (M <= 4), the
+// streaming MFMA decode kernel, or the tiled prefill kernel (M > 64, and
+// 17 .. 64 tokens where its tiles fill the chip better).
+enum class Path { Gemv, Skinny, Tiled };
+
+Path forward_path(int64_t M, int64_t N) {
+    if (M <= kGemvMaxM) return Path::Gemv;
+    if (M <= kSkinnyMaxM && !gemm_beats_skinny(M, N)) return Path::Skinny;
+    return Path::Tiled;
+}
+
 size_t forward_ws_bytes(int64_t M, int64_t N, int64_t K) {
-    if (M <= kGemvMaxM) return gemv_ws_bytes(M, N, K);
-    if (M <= kSkinnyMaxM) return skinny_ws_bytes(M, N, K);
-    return gemm_ws_bytes(M);
+    switch (forward_path(M, N)) {
+        case Path::Gemv: return gemv_ws_bytes(M, N, K);
+        case Path::Skinny: return skinny_ws_bytes(M, N, K);
+        default: return gemm_ws_bytes(M);
+    }
 }
 
 Problem make_problem(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
@@ -76,9 +89,11 @@ int run_forward(const int8_t* xq, const float* eta, const int32_t* xsum, const u
                 hipStream_t stream) {
     if (M == 0) return BITLINEAR_OK;
     const Problem p = make_problem(xq, eta, packed, gamma, N, K, y, y_int);
-    if (M <= kGemvMaxM) return launch_gemv(p, M, ws, stream);
-    if (M <= kSkinnyMaxM) return launch_skinny(p, M, ws, stream);
-    return xsum ? launch_gemm_xsum(p, M, xsum, stream) : launch_gemm(p, M, ws, stream);
+    switch (forward_path(M, N)) {
+        case Path::Gemv: return launch_gemv(p, M, ws, stream);
+        case Path::Skinny: return launch_skinny(p, M, ws, stream);
+        default: return xsum ? launch_gemm_xsum(p, M, xsum, stream) : launch_gemm(p, M, ws, stream);
+    }
 }
 
 // Workspace of the fused float32 forward: xq, eta, then the contraction's
@@ -386,7 +401,7 @@ static int forward_f32_common(const float* x, const uint8_t* packed, float gamma
     int8_t* xq = (int8_t*)ws;
     float* eta = (float*)((char*)ws + w.xq);
     void* rest = (char*)ws + w.xq + w.eta;
-    int32_t* xsum = M > kSkinnyMaxM ? (int32_t*)rest : nullptr;
+    int32_t* xsum = forward_path(M, N) == Path::Tiled ? (int32_t*)rest : nullptr;
     hipStream_t s = (hipStream_t)stream;
     clear_hip_error();
     // The quantizer writes the row sums alongside xq, so the contraction

@@ -632,6 +632,15 @@ int launch_gemm(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
 
 int gemm_tile_n(int64_t M) { return gemm_bn(M); }
 
+// 17 .. 64 tokens: the streaming MFMA kernel splits K to fill the chip, but
+// its per-step work grows with the token tiles; 32 x 128 prefill tiles win
+// once they alone occupy a third of the CUs (measured: M = 64, N = 11008,
+// K = 4096 22.5 -> 11.8 us; N = 4096, K = 11008 stays with the split-K
+// kernel, 22 us either way, 12-15 us at M = 16-32).
+bool gemm_beats_skinny(int64_t M, int64_t N) {
+    return M > 16 && ceil_div(M, 32) * ceil_div(N, 128) * 3 >= device_cus();
+}
+
 int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
                         hipStream_t stream) {
     // Grouped prefill keeps 128 x 256 tiles (grid.y = row tiles).

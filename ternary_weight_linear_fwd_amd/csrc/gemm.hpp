@@ -16,6 +16,10 @@ int launch_rowsum(const int8_t* xq, int64_t M, int64_t K, int32_t* xsum, hipStre
 // activation quantizer).
 int launch_gemm_xsum(const Problem& p, int64_t M, const int32_t* xsum, hipStream_t stream);
 
+// Whether this kernel, rather than the streaming MFMA decode kernel, should
+// contract M <= 64 tokens against N rows.
+bool gemm_beats_skinny(int64_t M, int64_t N);
+
 // The same without row sums; ws holds gemm_ws_bytes(M) bytes.
 int launch_gemm(const Problem& p, int64_t M, void* ws, hipStream_t stream);
 

@@ -218,3 +218,11 @@ def test_non_default_streams():
     for (M, _), r, (y, _, _) in zip(cases, ref, outs):
         say(f"stream case M={M}")
         assert np.array_equal(y.cpu().numpy().view(np.uint32), r.view(np.uint32))
+
+
+# 17 .. 64 tokens against wide weight matrices take the tiled kernel
+# (32 x 128 tiles fill a third of the CUs or more): own row sums, given row
+# sums and the fused float32 forward, with ragged N and K.
+@pytest.mark.parametrize("M,N,K", [(17, 12800, 80), (40, 20000, 208), (64, 11008, 1040)])
+def test_medium_token_counts_tiled(M, N, K):
+    run_case(M, N, K, seed=M * 7 + N + K, latent=False)
