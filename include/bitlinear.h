@@ -186,11 +186,12 @@ int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t
  *   y      [M][N] float32 (out)
  *   y_int  [M][N] int32   (out, may be NULL): the exact integer sums
  *   ws     workspace of bitlinear_workspace_bytes(M, N, K) bytes, 256-byte
- *          aligned: split-K partial sums for the decode kernels, room for
- *          the activation row sums for the tiled kernel
- * Kernel by size: M <= 4 the dot4 GEMV; M > 64 the tiled int8-MFMA kernel;
- * 4 < M <= 64 the streaming MFMA kernel, except 16 < M <= 64 with
- * ceil(M/32) * ceil(N/128) >= CUs / 3, which also takes the tiled kernel.
+ *          aligned: split-K partial sums (decode kernels, and the tiled
+ *          kernel when its 32 x 128 tiles leave CUs idle over a long K), or
+ *          room for the activation row sums of the tiled kernel
+ * Kernel by size: M <= 4 the dot4 GEMV; 4 < M <= 16 the streaming MFMA
+ * kernel; M > 16 the tiled int8-MFMA kernel (its K loop split over several
+ * workgroups per tile when few tiles would leave CUs idle).
  */
 int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
                       int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,
@@ -208,6 +209,7 @@ int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed,
  *        bitlinear_quantize_act or bitlinear_rmsnorm_quantize_act write it.
  *        Not checked: a wrong row sum shifts that row's y_int by the error.
  *        The decode kernels (dot4 and streaming MFMA) do not read it.
+ *        It must not overlap ws.
  *   other arguments, workspace and errors as bitlinear_forward.
  */
 int bitlinear_forward_xsum(const int8_t* xq, const float* eta, const int32_t* xsum,

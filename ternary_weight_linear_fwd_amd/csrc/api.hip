@@ -48,8 +48,7 @@ int check_sizes(int64_t M, int64_t N, int64_t K) {
 }
 
 // Contraction kernel for a single problem: the dot4 GEMV (M <= 4), the
-// streaming MFMA decode kernel, or the tiled prefill kernel (M > 64, and
-// 17 .. 64 tokens where its tiles fill the chip better).
+// streaming MFMA decode kernel (M <= 16), or the tiled prefill kernel.
 enum class Path { Gemv, Skinny, Tiled };
 
 Path forward_path(int64_t M, int64_t N) {
@@ -62,7 +61,7 @@ size_t forward_ws_bytes(int64_t M, int64_t N, int64_t K) {
     switch (forward_path(M, N)) {
         case Path::Gemv: return gemv_ws_bytes(M, N, K);
         case Path::Skinny: return skinny_ws_bytes(M, N, K);
-        default: return gemm_ws_bytes(M);
+        default: return gemm_ws_bytes(M, N, K);
     }
 }
 
@@ -92,21 +91,23 @@ int run_forward(const int8_t* xq, const float* eta, const int32_t* xsum, const u
     switch (forward_path(M, N)) {
         case Path::Gemv: return launch_gemv(p, M, ws, stream);
         case Path::Skinny: return launch_skinny(p, M, ws, stream);
-        default: return xsum ? launch_gemm_xsum(p, M, xsum, stream) : launch_gemm(p, M, ws, stream);
+        default: return xsum ? launch_gemm_xsum(p, M, xsum, ws, stream) : launch_gemm(p, M, ws, stream);
     }
 }
 
-// Workspace of the fused float32 forward: xq, eta, then the contraction's
-// own workspace (at prefill sizes the row sums, which the quantizer fills).
+// Workspace of the fused float32 forward: xq, eta, the row sums (prefill
+// kernel only; the quantizer fills them), then the contraction's own
+// workspace.
 struct F32Ws {
-    size_t xq, eta, bytes;
+    size_t xq, eta, xsum, bytes;
 };
 
 F32Ws f32_ws(int64_t M, int64_t N, int64_t K) {
     F32Ws w;
     w.xq = align256((size_t)(M * K));
     w.eta = align256((size_t)(4 * M));
-    w.bytes = w.xq + w.eta + align256(forward_ws_bytes(M, N, K));
+    w.xsum = forward_path(M, N) == Path::Tiled ? align256((size_t)(4 * M)) : 0;
+    w.bytes = w.xq + w.eta + w.xsum + align256(forward_ws_bytes(M, N, K));
     return w;
 }
 
@@ -400,8 +401,8 @@ static int forward_f32_common(const float* x, const uint8_t* packed, float gamma
     if (M == 0) return BITLINEAR_OK;
     int8_t* xq = (int8_t*)ws;
     float* eta = (float*)((char*)ws + w.xq);
-    void* rest = (char*)ws + w.xq + w.eta;
-    int32_t* xsum = forward_path(M, N) == Path::Tiled ? (int32_t*)rest : nullptr;
+    int32_t* xsum = w.xsum ? (int32_t*)((char*)ws + w.xq + w.eta) : nullptr;
+    void* rest = (char*)ws + w.xq + w.eta + w.xsum;
     hipStream_t s = (hipStream_t)stream;
     clear_hip_error();
     // The quantizer writes the row sums alongside xq, so the contraction

@@ -58,6 +58,9 @@ struct GemmArgs {
     int64_t ntiles_n;         // single: column tiles
     int64_t ntiles_m;         // single: row tiles
     const int32_t* xsum;      // single: the row sums sum_k xq[m][k], or null
+    int32_t* partial;         // single, split K: [S][M][N] int32 partial sums, or null
+    int32_t S;                // single: K-slices per tile (1: no split)
+    int32_t sps;              // single, split K: 128-k steps per slice
 };
 
 // Tile order: each XCD takes a contiguous run of the tile order
@@ -116,6 +119,7 @@ struct PrefillCtx {
     uint32_t afrag[4];      // LDS offset of this lane's A fragment of group d, row tile 0
     uint32_t sxfrag;        // afrag[wave]: the word group this wavefront sums
     int64_t K, Kb, nsteps;
+    int64_t kstep0;         // first step of this workgroup's K-slice (steps count from it)
     int wave, lane, ln, lg;
 };
 
@@ -129,7 +133,8 @@ template <int MT, int NT, bool CHECKED, bool ACT>
 __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT, NT>& c, uint8_t* st, int64_t step, v4i (&bq)[NT]) {
     using Ctx = PrefillCtx<MT, NT>;
     if constexpr (NT == 3) __builtin_amdgcn_sched_barrier(0);
-    const int64_t kbase = step * 128;
+    const int64_t as = c.kstep0 + step;   // step in the whole K loop
+    const int64_t kbase = as * 128;
 #pragma unroll
     for (int j = 0; j < Ctx::NA; ++j) {
         const int8_t* src;
@@ -148,10 +153,10 @@ __device__ __forceinline__ void prefill_issue(const PrefillCtx<MT, NT>& c, uint8
     for (int t = 0; t < (ACT ? NT : 0); ++t) {
         const uint8_t* bsrc;
         if constexpr (CHECKED) {
-            const int64_t kb = step * 2 + c.lg < c.Kb ? step * 2 + c.lg : c.Kb - 1;   // past the end: replaced at use
+            const int64_t kb = as * 2 + c.lg < c.Kb ? as * 2 + c.lg : c.Kb - 1;   // past the end: replaced at use
             bsrc = c.bbase[t] + (uint32_t)(kb * 1024 + (c.boff & 1023u));
         } else {
-            bsrc = (c.bbase[t] + step * 2048) + c.boff;
+            bsrc = (c.bbase[t] + as * 2048) + c.boff;
         }
         bq[t] = *reinterpret_cast<const v4i*>(bsrc);
     }
@@ -175,19 +180,20 @@ __device__ __forceinline__ void prefill_compute(const PrefillCtx<MT, NT>& c, con
 #pragma unroll
     for (int t = 0; t < NT; ++t) bw[t] = bq[t];
     if constexpr (TAIL) {
+        const int64_t as = c.kstep0 + step;   // step in the whole K loop
         if constexpr (RS) {
             // The given row sums cover k < K only, so every k at or past K
             // gets code 00 (c = 0): it adds nothing whatever A holds there.
             // Word d of the lane's chunk is k = 64 kb + 16 d .. + 15, and K
             // is a multiple of 16, so a word is wholly inside or outside.
-            const int64_t k0 = (step * 2 + c.lg) * 64;
+            const int64_t k0 = (as * 2 + c.lg) * 64;
 #pragma unroll
             for (int d = 0; d < 4; ++d)
                 if (k0 + 16 * d >= c.K) {
 #pragma unroll
                     for (int t = 0; t < NT; ++t) bw[t][d] = 0;
                 }
-        } else if (step * 2 + 1 >= c.Kb && c.lg == 1) {   // k-block past the end: code 01
+        } else if (as * 2 + 1 >= c.Kb && c.lg == 1) {   // k-block past the end: code 01
 #pragma unroll
             for (int t = 0; t < NT; ++t) bw[t] = v4i{0x55555555, 0x55555555, 0x55555555, 0x55555555};
         }
@@ -349,6 +355,9 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     static_assert(NS == 3 || NS == 4, "ring of three or four stages");
     using Ctx = PrefillCtx<MT, NT>;
     constexpr int BM = Ctx::BM;
+    // Only single launches of 32 x 128 tiles split K (the larger tiles have
+    // no registers to spare for it).
+    constexpr bool SPLIT = !GROUPED && MT == 1 && NT == 1;
     // Up to four stages, each its own LDS object, so that the compiler can
     // tell a read of one stage from the loads in flight into the others.
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[Ctx::AStage];
@@ -362,7 +371,7 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     Problem p;
-    int64_t tile_n, tile_m;
+    int64_t tile_n, tile_m, slice = 0;
     if constexpr (GROUPED) {
         const Unit un = a.units[blockIdx.x];
         p = a.problems[un.problem];
@@ -370,7 +379,11 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
         tile_m = blockIdx.y;
     } else {
         p = a.p;
-        tile_coords(blockIdx.x, (uint32_t)a.ntiles_m, (uint32_t)a.ntiles_n, 16 / MT, tile_m, tile_n);
+        // Split K: consecutive workgroups are the slices of one tile.
+        const uint32_t S = SPLIT && a.S > 1 ? (uint32_t)a.S : 1u;
+        slice = SPLIT ? blockIdx.x % S : 0;
+        tile_coords(SPLIT ? blockIdx.x / S : blockIdx.x, (uint32_t)a.ntiles_m, (uint32_t)a.ntiles_n, 16 / MT, tile_m,
+                    tile_n);
     }
     const int64_t M = a.M, N = p.N, K = p.K, Kb = p.Kb;
     const int64_t m0 = tile_m * BM;
@@ -382,7 +395,12 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     Ctx c;
     c.K = K;
     c.Kb = Kb;
+    c.kstep0 = 0;
     c.nsteps = ceil_div(Kb, 2);
+    if (SPLIT && a.S > 1) {   // this slice's steps (never empty: the host sizes slices)
+        c.kstep0 = slice * (int64_t)a.sps;
+        c.nsteps = c.nsteps - c.kstep0 < a.sps ? c.nsteps - c.kstep0 : a.sps;
+    }
     c.wave = wave;
     c.lane = lane;
     c.ln = lane & 31;
@@ -436,7 +454,8 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
         const int64_t m = m0 + tid;
         int t = 0;
         if constexpr (RS) {
-            t = m < M ? a.xsum[m] : 0;
+            // Under split K the whole row sum is taken off once, by slice 0.
+            t = m < M && (!SPLIT || slice == 0) ? a.xsum[m] : 0;
         } else {
 #pragma unroll
             for (int w = 0; w < 8; ++w) t += rowsum_part[w][tid];
@@ -452,6 +471,28 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     bool col[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) col[t] = n0 + 32 * t < N;
+    if (SPLIT && a.partial) {
+        // Split K: this slice's integer sums (its own row sums taken off);
+        // the split-K epilogue adds the slices in order and dequantizes.
+        int32_t* pcol = a.partial + (slice * M + m0) * N + n0;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = i * 32 + j * 8 + lg * 4 + q;
+                    if (m0 + r >= M) continue;
+                    const uint32_t xs = (uint32_t)__float_as_int(rowinfo[r].x);
+                    int32_t* pr = pcol + (int64_t)r * N;
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        if (col[t]) pr[32 * t] = (int)((uint32_t)acc[i][t][j * 4 + q] - xs);
+                }
+            }
+        }
+        return;
+    }
     // Non-temporal stores: y is not read again here, so it should not
     // displace the operands from the caches.
     float* ycol = p.y + m0 * N + n0;
@@ -496,8 +537,10 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
 
 // Stages of the LDS ring (steps in flight + 1), as measured fastest: three,
 // and four for 128 x 256 tiles, whose longer steps give fewer wavefronts per
-// SIMD more to hide.
-constexpr int prefill_stages(int mt, int nt) { return mt == 4 ? 4 : 3; }
+// SIMD more to hide, and for 32 x 128 tiles, which run on grids too small to
+// give each SIMD more than one or two wavefronts (3% over 42 shapes with
+// M = 17 .. 128, up to 10% where K or N is long).
+constexpr int prefill_stages(int mt, int nt) { return mt == 4 || mt == 1 ? 4 : 3; }
 
 // Column tile of the grouped prefill launch (output rows of W per workgroup).
 static int gemm_bn(int64_t M) { (void)M; return kPreBN; }
@@ -555,8 +598,59 @@ template <int MT, int NT, bool RS>
 static void launch_single(GemmArgs& a, hipStream_t stream) {
     a.ntiles_m = ceil_div(a.M, 32 * MT);
     a.ntiles_n = ceil_div(a.p.N, 128 * NT);
+    const int64_t S = a.S > 1 ? a.S : 1;
     hipLaunchKernelGGL((gemm_prefill_kernel<MT, NT, false, prefill_stages(MT, NT), RS>),
-                       dim3((unsigned)(a.ntiles_m * a.ntiles_n)), dim3(256), 0, stream, a);
+                       dim3((unsigned)(a.ntiles_m * a.ntiles_n * S)), dim3(256), 0, stream, a);
+}
+
+// Split K for grids of 32 x 128 tiles that leave CUs idle over a long K loop
+// (batched decode against a wide-K projection, e.g. M = 64, N = 4096,
+// K = 11008: 64 tiles for 256 CUs).  Each tile's K loop is cut into S slices
+// of whole 128-k steps, one workgroup each; the slices write int32 partial
+// sums that the split-K epilogue adds in slice order before dequantizing.
+// S comes from a cost estimate fitted to measurements on MI355X: a CU runs
+// kStepRate1 128-k steps per us with one resident workgroup (one wavefront
+// per SIMD: latency-bound) and kStepRate2 with two or more; a split adds
+// kSplitFixedUs (the epilogue launch and the pipeline fill of shorter K
+// loops) and 8 bytes per partial element (written, read back) at
+// kSplitBytesPerUs.  Candidates keep at most two workgroups per CU and four
+// steps per slice.  E.g. M = 96, N = 4096, K = 11008: 96 tiles x 5 slices,
+// 22.6 -> 16.3 us; M = 128, N = 8192, K = 28672: 256 tiles x 2 slices,
+// 66 -> 45 us; M = 128, N = 8192, K = 8192 stays whole (18 us; 22 us split).
+constexpr double kStepRate1 = 3.4;
+constexpr double kStepRate2 = 4.4;
+constexpr double kSplitFixedUs = 2.0;
+constexpr double kSplitBytesPerUs = 4.0e6;
+constexpr int64_t kSplitMinSteps = 4;
+constexpr int64_t kSplitMaxSlices = 16;
+
+struct SplitCfg {
+    int32_t S, sps;   // slices, 128-k steps per slice
+};
+
+static double split_cost_us(int64_t M, int64_t N, int64_t tiles, int64_t nsteps, int64_t S, int cus) {
+    const int64_t sps = ceil_div(nsteps, S);
+    const int64_t per_cu = ceil_div(tiles * ceil_div(nsteps, sps), cus);   // workgroups on the busiest CU
+    const double loop = (double)(per_cu * sps) / (per_cu == 1 ? kStepRate1 : kStepRate2);
+    return S == 1 ? loop : loop + kSplitFixedUs + 8.0 * (double)S * (double)M * (double)N / kSplitBytesPerUs;
+}
+
+static SplitCfg prefill_split(int64_t M, int64_t N, int64_t K, int cus) {
+    const TileCfg t = prefill_tile(M, N, cus);
+    const int64_t nsteps = ceil_div(ceil_div(K, 64), 2);
+    if (t.mt != 1) return {1, (int32_t)nsteps};
+    const int64_t tiles = ceil_div(M, 32) * ceil_div(N, 128);
+    int64_t best = 1;
+    double best_us = split_cost_us(M, N, tiles, nsteps, 1, cus);
+    for (int64_t S = 2; S <= kSplitMaxSlices && tiles * S <= 2 * (int64_t)cus && nsteps / S >= kSplitMinSteps; ++S) {
+        const double us = split_cost_us(M, N, tiles, nsteps, S, cus);
+        if (us < best_us) {
+            best = S;
+            best_us = us;
+        }
+    }
+    const int64_t sps = ceil_div(nsteps, best);
+    return {(int32_t)ceil_div(nsteps, sps), (int32_t)sps};   // no empty slices
 }
 
 // Row sums of the int8 activations, xsum[m] = sum_k xq[m][k] in int32
@@ -583,7 +677,14 @@ __global__ __launch_bounds__(256) void rowsum_kernel(const int8_t* __restrict__ 
     if (lane == 0) xsum[m] = (int32_t)u;
 }
 
-size_t gemm_ws_bytes(int64_t M) { return (size_t)M * sizeof(int32_t); }
+// Either the row sums of the 96 x 384 tile's pre-pass or the split-K
+// partials (never both: split K only takes 32 x 128 tiles).
+size_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+    const SplitCfg sp = prefill_split(M, N, K, device_cus());
+    const size_t rows = (size_t)M * sizeof(int32_t);
+    const size_t part = sp.S > 1 ? (size_t)sp.S * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
+    return rows > part ? rows : part;
+}
 
 int launch_rowsum(const int8_t* xq, int64_t M, int64_t K, int32_t* xsum, hipStream_t stream) {
     if (M == 0) return BITLINEAR_OK;
@@ -592,16 +693,32 @@ int launch_rowsum(const int8_t* xq, int64_t M, int64_t K, int32_t* xsum, hipStre
     return BITLINEAR_OK;
 }
 
-int launch_gemm_xsum(const Problem& p, int64_t M, const int32_t* xsum, hipStream_t stream) {
+// 32 x 128 tiles, split over K when that fills the chip better (the
+// partials go to ws, which must not overlap xsum).
+template <bool RS>
+static int launch_tiny(GemmArgs& a, void* ws, hipStream_t stream) {
+    const SplitCfg sp = prefill_split(a.M, a.p.N, a.p.K, device_cus());
+    if (sp.S > 1) {
+        a.partial = static_cast<int32_t*>(ws);
+        a.S = sp.S;
+        a.sps = sp.sps;
+    }
+    launch_single<1, 1, RS>(a, stream);
+    BL_LAUNCH_CHECK();
+    if (sp.S > 1) return launch_splitk_epilogue(a.partial, sp.S, a.M, a.p, stream);
+    return BITLINEAR_OK;
+}
+
+int launch_gemm_xsum(const Problem& p, int64_t M, const int32_t* xsum, void* ws, hipStream_t stream) {
     if (!xsum) return BITLINEAR_EINVAL;
     GemmArgs a{};
     a.p = p;
     a.M = M;
     a.xsum = xsum;
     const TileCfg t = prefill_tile(M, p.N, device_cus());
+    if (t.mt == 1) return launch_tiny<true>(a, ws, stream);
     if (t.mt == 3) launch_single<3, 3, true>(a, stream);
     else if (t.mt == 4) launch_single<4, 2, true>(a, stream);
-    else if (t.mt == 1) launch_single<1, 1, true>(a, stream);
     else launch_single<2, 2, true>(a, stream);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
@@ -618,13 +735,13 @@ int launch_gemm(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
         int32_t* xsum = static_cast<int32_t*>(ws);
         const int rc = launch_rowsum(p.xq, M, p.K, xsum, stream);
         if (rc) return rc;
-        return launch_gemm_xsum(p, M, xsum, stream);
+        return launch_gemm_xsum(p, M, xsum, nullptr, stream);
     }
     GemmArgs a{};
     a.p = p;
     a.M = M;
+    if (t.mt == 1) return launch_tiny<false>(a, ws, stream);
     if (t.mt == 4) launch_single<4, 2, false>(a, stream);
-    else if (t.mt == 1) launch_single<1, 1, false>(a, stream);
     else launch_single<2, 2, false>(a, stream);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
@@ -632,13 +749,15 @@ int launch_gemm(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
 
 int gemm_tile_n(int64_t M) { return gemm_bn(M); }
 
-// 17 .. 64 tokens: the streaming MFMA kernel splits K to fill the chip, but
-// its per-step work grows with the token tiles; 32 x 128 prefill tiles win
-// once they alone occupy a third of the CUs (measured: M = 64, N = 11008,
-// K = 4096 22.5 -> 11.8 us; N = 4096, K = 11008 stays with the split-K
-// kernel, 22 us either way, 12-15 us at M = 16-32).
+// 17 .. 64 tokens: the streaming MFMA kernel reads each weight once for
+// all rows, but its per-step work grows with the token tiles; the 32 x 128
+// prefill tiles, split over K where they leave CUs idle, measured faster for
+// every shape tried (M = 17 .. 64 against N x K = 4096 x 11008, 11008 x 4096,
+// 8192 x 8192, 3200 x 8640, 8192 x 28672, 28672 x 8192; e.g. M = 64,
+// N = 4096, K = 11008: 22.5 -> 14.8 us; M = 17, N = 8192, K = 8192 is even).
 bool gemm_beats_skinny(int64_t M, int64_t N) {
-    return M > 16 && ceil_div(M, 32) * ceil_div(N, 128) * 3 >= device_cus();
+    (void)N;
+    return M > 16;
 }
 
 int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,

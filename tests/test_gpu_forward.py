@@ -220,9 +220,24 @@ def test_non_default_streams():
         assert np.array_equal(y.cpu().numpy().view(np.uint32), r.view(np.uint32))
 
 
-# 17 .. 64 tokens against wide weight matrices take the tiled kernel
-# (32 x 128 tiles fill a third of the CUs or more): own row sums, given row
-# sums and the fused float32 forward, with ragged N and K.
-@pytest.mark.parametrize("M,N,K", [(17, 12800, 80), (40, 20000, 208), (64, 11008, 1040)])
+# 17 .. 64 tokens take the tiled kernel with 32 x 128 tiles, whole or split
+# over K: own row sums, given row sums and the fused float32 forward, with
+# ragged N and K, from grids of many tiles to a handful of split ones.
+@pytest.mark.parametrize("M,N,K", [(17, 12800, 80), (40, 20000, 208), (64, 11008, 1040), (17, 640, 4160),
+                                   (33, 1000, 2064)])
 def test_medium_token_counts_tiled(M, N, K):
     run_case(M, N, K, seed=M * 7 + N + K, latent=False)
+
+
+# Tiled kernel with the K loop split over several workgroups per tile (few
+# 32 x 128 tiles, long K): the slices' int32 partials are added in slice
+# order, so y_int is exact; own row sums (per slice), given row sums (taken
+# off by the first slice) and the fused float32 forward.  Ragged M and N, K
+# with a half-empty last step (odd number of 64-k blocks) and with a last
+# block only a quarter inside K.
+@pytest.mark.parametrize("M,N,K", [(65, 300, 4160), (96, 1000, 4112), (200, 640, 2064), (96, 2048, 11008)])
+def test_tiled_split_k(M, N, K):
+    L = bl()
+    # the workspace holds xq and the partial sums of at least two slices
+    assert L.bitlinear_workspace_bytes(M, N, K) >= M * K + 2 * M * N * 4
+    run_case(M, N, K, seed=M * 5 + N * 3 + K, latent=False)

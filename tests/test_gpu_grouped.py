@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-@pytest.mark.parametrize("M", [1, 3, 8, 16, 40])
+@pytest.mark.parametrize("M", [1, 3, 8, 16, 40, 64])
 def test_grouped_block_matches_oracle(M):
     torch = torch_cuda()
     L = bl()
