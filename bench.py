@@ -150,6 +150,63 @@ def bench_prefill(torch, L, S, reps: int):
     return out, mfma_ceiling
 
 
+def bench_c5(torch, L, S, reps: int):
+    """Batched decode with skewed sparsity (hidden 4096, FFN 11008; ternary
+    weights drawn directly, P(0) = 0.6; 1% outlier channels): the seven
+    projections of a block from float32 activations to float32 outputs,
+    (a) as one grouped forward (one quantize + one contraction launch) and
+    (b) as seven fused bitlinear_forward_f32 calls, for M = 32, 64, 128."""
+    import ctypes
+    st = torch.cuda.current_stream().cuda_stream
+    packed, gammas = [], []
+    for p in S.C5_PROJS:
+        Wt, g = S.c5_ternary(p)
+        buf = torch.empty(L.bitlinear_packed_bytes(p.N, p.K), dtype=torch.uint8, device="cuda")
+        L.bitlinear_pack_ternary(torch.from_numpy(Wt).cuda(), p.N, p.K, buf)
+        packed.append(buf)
+        gammas.append(float(g))
+    wbytes = sum(int(L.bitlinear_packed_bytes(p.N, p.K)) for p in S.C5_PROJS)
+    out = []
+    for M in (32, 64, 128):
+        xs = [torch.from_numpy(S.c5_x(p, M)).cuda() for p in S.C5_PROJS]
+        ys = [torch.empty((M, p.N), dtype=torch.float32, device="cuda") for p in S.C5_PROJS]
+        xqs = [torch.empty((M, p.K), dtype=torch.int8, device="cuda") for p in S.C5_PROJS]
+        etas = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in S.C5_PROJS]
+        specs = [dict(x=x, xq=xq, eta=eta, packed=w, y=y, y_int=None, gamma=g, N=p.N, K=p.K)
+                 for p, x, xq, eta, w, y, g in zip(S.C5_PROJS, xs, xqs, etas, packed, ys, gammas)]
+        probs = L.make_problems(specs)
+        tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
+        table = torch.empty(tb, dtype=torch.uint8, device="cuda")
+        plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
+        wsb = max(L.bitlinear_workspace_bytes(M, p.N, p.K) for p in S.C5_PROJS)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        # Raw addresses resolved once, outside the timed loops.
+        calls = [(x.data_ptr(), w.data_ptr(), g, p.N, p.K, y.data_ptr())
+                 for p, x, w, y, g in zip(S.C5_PROJS, xs, packed, ys, gammas)]
+        wsp = ws.data_ptr()
+
+        def singles():
+            for xa, wa, g, N, K, ya in calls:
+                L.bitlinear_forward_f32(xa, wa, g, M, N, K, ya, wsp, wsb, st)
+        grouped = lambda: L.bitlinear_forward_grouped(plan)
+        t_end = time.perf_counter() + 0.2
+        while time.perf_counter() < t_end:
+            grouped()
+            singles()
+            torch.cuda.synchronize()
+        g_ms = time_events(torch, grouped, reps)
+        s_ms = time_events(torch, singles, reps)
+        ops = 2 * M * sum(p.N * p.K for p in S.C5_PROJS)
+        best = min(g_ms, s_ms)
+        out.append({"M": M, "grouped_us": round(g_ms * 1e3, 2), "single_calls_us": round(s_ms * 1e3, 2),
+                    "weight_gbs": round(wbytes / (best * 1e-3) / 1e9, 1),
+                    "tops": round(ops / (best * 1e-3) / 1e12, 1)})
+        del xs, ys, xqs, etas, table, ws
+    return {"workload": "hidden 4096, FFN 11008 block (q,k,v,o 4096->4096; gate,up 4096->11008; "
+                        "down 11008->4096), ternary P(0)=0.6, 1% outlier channels x20, float32 in/out",
+            "packed_weight_bytes": wbytes, "per_M": out}
+
+
 def bench_mfma_ceiling(torch, L, xq, packed) -> dict:
     """The int8 matrix-core loop (bitlinear_measure_mfma_i8) fed with the first
     8 KB of these activations and 2 KB of these packed weights: what the
@@ -503,6 +560,12 @@ def main() -> int:
 
     if prefill is not None:
         extra["prefill"] = prefill
+
+    if not args.no_prefill:
+        extra["batched_decode_c5"] = bench_c5(torch, L, S, max(10, args.steps))
+        for r in extra["batched_decode_c5"]["per_M"]:
+            log(f"C5 block M={r['M']}: grouped {r['grouped_us']} us, seven single calls "
+                f"{r['single_calls_us']} us ({r['weight_gbs']} GB/s of weights, {r['tops']} TOP/s)")
 
     if not args.no_prefill:
         extra["rmsnorm_quant"] = bench_rmsnorm(torch, L, S, max(10, args.steps))

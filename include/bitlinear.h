@@ -309,7 +309,10 @@ typedef struct bitlinear_grouped_plan {
     int32_t max_K;         /* longest K among the problems */
 } bitlinear_grouped_plan;
 
-/* Device bytes the work table for these problems needs (host only). */
+/* Device bytes the work table for these problems needs (host only).  Plans
+ * at 5 .. 64 tokens whose 256-row blocks would leave CUs idle (a single
+ * transformer block, say) split their K loops, and the table then also
+ * holds the int32 partial sums (M x 256 x 4 bytes per work unit). */
 size_t bitlinear_grouped_table_bytes(const bitlinear_problem* problems_host, int32_t count,
                                      int64_t M);
 
@@ -321,7 +324,8 @@ int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t 
                                 void* table, size_t table_bytes, bitlinear_grouped_plan* plan,
                                 void* stream);
 
-/* Queue the grouped forward described by a plan. */
+/* Queue the grouped forward described by a plan.  Calls with one plan whose
+ * execution overlaps (other streams) race on its table's partial sums. */
 int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream);
 
 #ifdef __cplusplus

@@ -77,6 +77,7 @@ Problem make_problem(const int8_t* xq, const float* eta, const uint8_t* packed, 
     p.N = (int32_t)N;
     p.K = (int32_t)K;
     p.Kb = (int32_t)ceil_div(K, 64);
+    p.slices = 1;
     return p;
 }
 
@@ -111,37 +112,76 @@ F32Ws f32_ws(int64_t M, int64_t N, int64_t K) {
     return w;
 }
 
+// Contraction kernel of a grouped plan: 0 dot4 GEMV, 1 prefill MFMA, 2 skinny
+// MFMA, 3 skinny MFMA with K split (partials in the table, then an epilogue).
+constexpr int32_t kPlanGemv = 0, kPlanGemm = 1, kPlanSkinny = 2, kPlanSkinnySplit = 3;
+
 struct TableLayout {
-    size_t problems_off, units_off, rows_off, bytes;
+    size_t problems_off, units_off, rows_off, part_off, bytes;
 };
 
-TableLayout table_layout(int64_t count, int64_t nunits, int64_t nrows) {
+// The work table: problem descriptors, work units, quantizer rows and, for
+// split plans, the partial sums (M x 256 int32 per unit).
+TableLayout table_layout(int64_t count, int64_t nunits, int64_t nrows, int32_t kernel, int64_t M) {
     TableLayout t;
     t.problems_off = 0;
     t.units_off = align256((size_t)count * sizeof(Problem));
     t.rows_off = t.units_off + align256((size_t)nunits * sizeof(Unit));
-    t.bytes = t.rows_off + align256((size_t)nrows * sizeof(QuantRow));
+    t.part_off = t.rows_off + align256((size_t)nrows * sizeof(QuantRow));
+    const size_t part = kernel == kPlanSkinnySplit ? (size_t)nunits * (size_t)M * kSkinnyRows * sizeof(int32_t) : 0;
+    t.bytes = t.part_off + align256(part);
     return t;
 }
 
-// Work units of the grouped contraction for one problem.
-int64_t problem_units(int64_t M, int64_t N) {
-    if (M <= kGemvMaxM) return ceil_div(N, 64);      // one wavefront per 64-row group
-    if (M <= kSkinnyMaxM) return ceil_div(N, kSkinnyRows);   // one workgroup per 256 rows
-    return ceil_div(N, gemm_tile_n(M));
+// Work units of the grouped contraction for one problem (before K slices).
+int64_t problem_units(int32_t kernel, int64_t M, int64_t N) {
+    if (kernel == kPlanGemv) return ceil_div(N, 64);   // one wavefront per 64-row group
+    if (kernel == kPlanGemm) return ceil_div(N, gemm_tile_n(M));
+    return ceil_div(N, kSkinnyRows);                   // one workgroup per 256 rows
 }
 
-// Contraction kernel of a grouped plan: 0 dot4 GEMV, 1 prefill MFMA, 2 skinny MFMA.
 int32_t plan_kernel(int64_t M) {
-    if (M <= kGemvMaxM) return 0;
-    if (M <= kSkinnyMaxM) return 2;
-    return 1;
+    if (M <= kGemvMaxM) return kPlanGemv;
+    if (M <= kSkinnyMaxM) return kPlanSkinny;
+    return kPlanGemm;
+}
+
+// K-slices per 256-row block for a grouped skinny plan.  Plans whose blocks
+// alone leave CUs idle (a single transformer block at a few dozen tokens:
+// 166 blocks for hidden 4096 / FFN 11008) cut every problem's K loop into
+// slices of about the same length, aiming at two workgroups per CU up to 32
+// tokens and one above (the partials grow with M), with at least
+// kGroupedSplitMinSteps 256-k steps per slice; the slices write int32
+// partials that a second launch adds in slice order.  Large plans (a whole
+// model's projections) keep whole K loops.  Measured on the seven
+// projections of a hidden-4096 / FFN-11008 block: M = 8 43 -> 20 us,
+// M = 32 50 -> 31 us, M = 64 68 -> 49 us.
+constexpr int64_t kGroupedSplitMinSteps = 2;
+constexpr int64_t kGroupedSplitMaxSlices = kSkinnyMaxSlices;
+
+void choose_slices(std::vector<Problem>& problems, int64_t M, int cus) {
+    const int64_t wg_per_cu = M <= 32 ? 2 : 1;
+    int64_t blocks = 0, work = 0;   // work: 256-row blocks x 256-k steps
+    for (const Problem& p : problems) {
+        blocks += ceil_div(p.N, kSkinnyRows);
+        work += ceil_div(p.N, kSkinnyRows) * ceil_div(p.Kb, 4);
+    }
+    if (blocks >= cus) return;
+    int64_t len = ceil_div(work, wg_per_cu * cus);   // steps per slice
+    if (len < kGroupedSplitMinSteps) len = kGroupedSplitMinSteps;
+    for (Problem& p : problems) {
+        int64_t S = ceil_div(ceil_div(p.Kb, 4), len);
+        if (S > kGroupedSplitMaxSlices) S = kGroupedSplitMaxSlices;
+        while (S > 1 && (S - 1) * skinny_slice_kb(p.Kb, S) >= p.Kb) --S;   // no empty slice
+        p.slices = (int32_t)(S < 1 ? 1 : S);
+    }
 }
 
 struct PlanHost {
     std::vector<Problem> problems;
     std::vector<Unit> units;
     std::vector<QuantRow> rows;
+    int32_t kernel = kPlanGemv;
 };
 
 int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& out) {
@@ -171,13 +211,23 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
         } else if (it->second != q.x) {
             return BITLINEAR_EINVAL;  // one xq buffer fed from two different sources
         }
-        Problem p = make_problem(q.xq, q.eta, q.packed, q.gamma, q.N, q.K, q.y, q.y_int);
-        p.unit_begin = (int32_t)out.units.size();
-        const int64_t nu = problem_units(M, q.N);
-        for (int64_t g = 0; g < nu; ++g) out.units.push_back(Unit{i, (int32_t)g});
-        out.problems.push_back(p);
+        out.problems.push_back(make_problem(q.xq, q.eta, q.packed, q.gamma, q.N, q.K, q.y, q.y_int));
     }
-    if (out.units.size() >= (size_t)kMaxDim) return BITLINEAR_EUNSUPPORTED;
+    out.kernel = plan_kernel(M);
+    if (out.kernel == kPlanSkinny && M > 0) {
+        choose_slices(out.problems, M, device_cus());
+        for (const Problem& p : out.problems)
+            if (p.slices > 1) out.kernel = kPlanSkinnySplit;
+    }
+    // Units: each problem's blocks in order, the K-slices of a block adjacent.
+    for (int32_t i = 0; i < count; ++i) {
+        Problem& p = out.problems[i];
+        p.unit_begin = (int32_t)out.units.size();
+        const int64_t nu = problem_units(out.kernel == kPlanSkinnySplit ? kPlanSkinny : out.kernel, M, p.N);
+        for (int64_t g = 0; g < nu; ++g)
+            for (int32_t s = 0; s < p.slices; ++s) out.units.push_back(Unit{i, (int32_t)g});
+        if (out.units.size() >= (size_t)kMaxDim) return BITLINEAR_EUNSUPPORTED;
+    }
     return BITLINEAR_OK;
 }
 
@@ -428,7 +478,7 @@ size_t bitlinear_grouped_table_bytes(const bitlinear_problem* problems_host, int
                                      int64_t M) {
     PlanHost h;
     if (build_plan(problems_host, count, M, h) != BITLINEAR_OK) return 0;
-    return table_layout(count, (int64_t)h.units.size(), (int64_t)h.rows.size()).bytes;
+    return table_layout(count, (int64_t)h.units.size(), (int64_t)h.rows.size(), h.kernel, M).bytes;
 }
 
 int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t count, int64_t M,
@@ -438,16 +488,16 @@ int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t 
     PlanHost h;
     int rc = build_plan(problems_host, count, M, h);
     if (rc) return rc;
-    const TableLayout L = table_layout(count, (int64_t)h.units.size(), (int64_t)h.rows.size());
+    const TableLayout L = table_layout(count, (int64_t)h.units.size(), (int64_t)h.rows.size(), h.kernel, M);
     if (!table || !aligned(table, 256) || table_bytes < L.bytes) return BITLINEAR_EWORKSPACE;
-    std::vector<uint8_t> host(L.bytes, 0);
+    std::vector<uint8_t> host(L.part_off, 0);   // the partials need no initial value
     std::memcpy(host.data() + L.problems_off, h.problems.data(), h.problems.size() * sizeof(Problem));
     std::memcpy(host.data() + L.units_off, h.units.data(), h.units.size() * sizeof(Unit));
     if (!h.rows.empty())
         std::memcpy(host.data() + L.rows_off, h.rows.data(), h.rows.size() * sizeof(QuantRow));
     hipStream_t s = (hipStream_t)stream;
     clear_hip_error();
-    BL_HIP_CHECK(hipMemcpyAsync(table, host.data(), L.bytes, hipMemcpyHostToDevice, s));
+    BL_HIP_CHECK(hipMemcpyAsync(table, host.data(), L.part_off, hipMemcpyHostToDevice, s));
     BL_HIP_CHECK(hipStreamSynchronize(s));
     int max_K = 0;
     for (const Problem& p : h.problems) max_K = p.K > max_K ? p.K : max_K;
@@ -457,7 +507,7 @@ int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t 
     plan->quant_rows = (int64_t)h.rows.size();
     plan->count = count;
     plan->M = (int32_t)M;
-    plan->kernel = plan_kernel(M);
+    plan->kernel = h.kernel;
     plan->max_K = max_K;
     return BITLINEAR_OK;
 }
@@ -465,7 +515,8 @@ int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t 
 int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) {
     if (!plan || !plan->table || plan->count <= 0 || plan->M < 0) return BITLINEAR_EINVAL;
     if (plan->M == 0) return BITLINEAR_OK;
-    const TableLayout L = table_layout(plan->count, plan->units, plan->quant_rows);
+    if (plan->kernel < kPlanGemv || plan->kernel > kPlanSkinnySplit) return BITLINEAR_EINVAL;
+    const TableLayout L = table_layout(plan->count, plan->units, plan->quant_rows, plan->kernel, plan->M);
     if (plan->table_bytes < L.bytes) return BITLINEAR_EINVAL;
     const char* base = (const char*)plan->table;
     const Problem* problems = (const Problem*)(base + L.problems_off);
@@ -476,9 +527,14 @@ int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) 
     int rc = BITLINEAR_OK;
     if (plan->quant_rows) rc = launch_quantize_grouped(rows, plan->quant_rows, s);
     if (rc) return rc;
-    if (plan->kernel == 0) return launch_gemv_grouped(problems, units, plan->units, plan->M, s);
-    if (plan->kernel == 2) return launch_skinny_grouped(problems, units, plan->units, plan->M, s);
-    return launch_gemm_grouped(problems, units, plan->units, plan->M, s);
+    switch (plan->kernel) {
+        case kPlanGemv: return launch_gemv_grouped(problems, units, plan->units, plan->M, s);
+        case kPlanSkinny: return launch_skinny_grouped(problems, units, plan->units, plan->M, nullptr, s);
+        case kPlanSkinnySplit:
+            return launch_skinny_grouped(problems, units, plan->units, plan->M,
+                                         reinterpret_cast<int32_t*>(static_cast<char*>(plan->table) + L.part_off), s);
+        default: return launch_gemm_grouped(problems, units, plan->units, plan->M, s);
+    }
 }
 
 }  // extern "C"

@@ -578,7 +578,7 @@ static TileCfg prefill_tile(int64_t M, int64_t N, int cus) {
 
 // CUs of the current device, asked of the runtime once per device (the
 // query costs more host time than a short prefill launch can hide).
-static int device_cus() {
+int device_cus() {
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cached[kMaxDevices];
     int dev = 0;

@@ -18,6 +18,9 @@ int launch_rowsum(const int8_t* xq, int64_t M, int64_t K, int32_t* xsum, hipStre
 // not overlap xsum.
 int launch_gemm_xsum(const Problem& p, int64_t M, const int32_t* xsum, void* ws, hipStream_t stream);
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus();
+
 // Whether this kernel, rather than the streaming MFMA decode kernel, should
 // contract M <= 64 tokens against N rows.
 bool gemm_beats_skinny(int64_t M, int64_t N);

@@ -26,7 +26,7 @@ struct Problem {
     int32_t N, K;
     int32_t Kb;             // ceil(K / 64)
     int32_t unit_begin;     // first work unit of this problem in a grouped table
-    int32_t pad;
+    int32_t slices;         // grouped skinny plans: K-slices per 256-row block (1: whole K)
 };
 static_assert(sizeof(Problem) == 64, "Problem descriptor is one 64-byte line");
 
@@ -77,8 +77,18 @@ constexpr int kSkinnyRows = 256;   // output rows per workgroup
 int skinny_split_slices(int64_t M, int64_t N, int64_t K);
 size_t skinny_ws_bytes(int64_t M, int64_t N, int64_t K);
 int launch_skinny(const Problem& p, int64_t M, void* ws, hipStream_t stream);
+// Grouped: problem p's units are its 256-row blocks, each cut into
+// p.slices K-slices (consecutive units, slice innermost).  With any slices
+// > 1, partial holds nunits * M * 256 int32 (unit u's sums at u * M * 256,
+// [m][256]) and a second launch adds the slices and dequantizes.
 int launch_skinny_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
-                          hipStream_t stream);
+                          int32_t* partial, hipStream_t stream);
+constexpr int kSkinnyMaxSlices = 16;   // K-slices per block in a grouped plan, at most
+// k-blocks per slice when a block of Kb k-blocks is cut into S slices
+// (whole 256-k steps; the planner only picks S that leave no slice empty).
+__host__ __device__ inline int64_t skinny_slice_kb(int64_t Kb, int64_t S) {
+    return S > 1 ? ((Kb + S - 1) / S + 3) / 4 * 4 : Kb;
+}
 
 // ---- prefill contraction on int8 MFMA for M > 64 (gemm.hip; the single
 // launch is declared in gemm.hpp)

@@ -37,7 +37,8 @@ struct SkinnyArgs {
     Problem p;                // single-problem mode
     SplitK sk;
     const Problem* problems;  // grouped mode
-    const Unit* units;        // grouped: (problem, 256-row block)
+    const Unit* units;        // grouped: (problem, 256-row block), K-slices innermost
+    int32_t* gpart;           // grouped, K split: [unit][M][256] int32 partial sums
     int64_t nunits;           // work units = workgroups
     int32_t M;
 };
@@ -88,6 +89,12 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
         blk = un.group;
         kb0 = 0;
         kb1 = p.Kb;
+        if (p.slices > 1) {
+            slice = (int64_t)u - p.unit_begin - blk * p.slices;
+            const int64_t kbs = skinny_slice_kb(p.Kb, p.slices);
+            kb0 = slice * kbs;
+            kb1 = kb0 + kbs < p.Kb ? kb0 + kbs : p.Kb;
+        }
     } else {
         p = a.p;
         const int S = a.sk.S;
@@ -170,13 +177,16 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
         for (int r = 0; r < 4; ++r) {
             const int64_t m = i * 16 + lg * 4 + r;
             if (m >= M) continue;
-            const float s = (GROUPED || a.sk.S == 1) ? dequant_scale(p.eta[m], p.gamma) : 0.0f;
+            const bool split = GROUPED ? p.slices > 1 : a.sk.S > 1;
+            const float s = split ? 0.0f : dequant_scale(p.eta[m], p.gamma);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int64_t n = g * 64 + t * 16 + nl;
                 if (n >= N) continue;
                 const int v = acc[i][t][r] - accs[i][r];
-                if (!GROUPED && a.sk.S > 1) {
+                if (GROUPED && split) {
+                    a.gpart[((int64_t)u * M + m) * kSkinnyRows + (n - blk * kSkinnyRows)] = v;
+                } else if (split) {
                     a.sk.partial[(slice * M + m) * N + n] = v;
                 } else {
                     // Device-scope stores write through the XCD's L2: the
@@ -244,14 +254,59 @@ int launch_skinny(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
     return BITLINEAR_OK;
 }
 
+// Grouped split-K epilogue, grid (units, row chunks): the workgroups of a
+// block's first slice add the block's slices in order for kEpiRows token rows
+// (thread = output row n of the block) and apply the dequant; every other
+// unit, and blocks of unsplit problems, exit.  The slice loop is unrolled to
+// its maximum, so that a thread's loads are all in flight at once rather
+// than one memory round trip per slice.
+constexpr int kEpiRows = 4;
+
+__global__ __launch_bounds__(256) void skinny_grouped_epilogue_kernel(const Problem* __restrict__ problems,
+                                                                      const Unit* __restrict__ units, int64_t M,
+                                                                      const int32_t* __restrict__ gpart) {
+    const int64_t u = blockIdx.x;
+    const Unit un = units[u];
+    const Problem p = problems[un.problem];
+    if (p.slices <= 1 || u - p.unit_begin != (int64_t)un.group * p.slices) return;
+    const int64_t n = (int64_t)un.group * kSkinnyRows + threadIdx.x;
+    const int64_t m0 = (int64_t)blockIdx.y * kEpiRows;
+    if (n >= p.N || m0 >= M) return;
+    const int rows = M - m0 < kEpiRows ? (int)(M - m0) : kEpiRows;
+    const int S = p.slices;
+    const int32_t* __restrict__ src = gpart + (u * M + m0) * kSkinnyRows + threadIdx.x;
+    int part[kSkinnyMaxSlices][kEpiRows];
+#pragma unroll
+    for (int s = 0; s < kSkinnyMaxSlices; ++s)
+#pragma unroll
+        for (int r = 0; r < kEpiRows; ++r)
+            part[s][r] = s < S && r < rows ? src[((int64_t)s * M + r) * kSkinnyRows] : 0;
+#pragma unroll
+    for (int r = 0; r < kEpiRows; ++r) {
+        if (r >= rows) break;
+        int v = 0;
+#pragma unroll
+        for (int s = 0; s < kSkinnyMaxSlices; ++s) v += part[s][r];   // slice order
+        const int64_t m = m0 + r;
+        p.y[m * p.N + n] = dequant(v, dequant_scale(p.eta[m], p.gamma));
+        if (p.y_int) p.y_int[m * p.N + n] = v;
+    }
+}
+
 int launch_skinny_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
-                          hipStream_t stream) {
+                          int32_t* partial, hipStream_t stream) {
     SkinnyArgs a{};
     a.problems = problems;
     a.units = units;
+    a.gpart = partial;
     a.nunits = nunits;
     a.M = (int32_t)M;
-    return launch_skinny_any(a, true, stream);
+    const int rc = launch_skinny_any(a, true, stream);
+    if (rc || !partial) return rc;
+    hipLaunchKernelGGL(skinny_grouped_epilogue_kernel, dim3((unsigned)nunits, (unsigned)ceil_div(M, kEpiRows)),
+                       dim3(256), 0, stream, problems, units, M, (const int32_t*)partial);
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
 }
 
 }  // namespace bl

@@ -118,3 +118,75 @@ def test_grouped_mixed_row_lengths(M):
         assert np.array_equal(s["eta"].cpu().numpy().view(np.uint32), eta_ref.view(np.uint32))
         assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref)
         assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+# A small grouped plan at 5 .. 64 tokens (fewer 256-row blocks than CUs)
+# splits every problem's K loop in the streaming MFMA kernel: problems whose
+# K gives 1 .. 15 slices (one 16-k problem stays whole), ragged N and K, run
+# twice on the same table.
+@pytest.mark.parametrize("M", [24, 64])
+def test_grouped_split_k_small_plan(M):
+    torch = torch_cuda()
+    L = bl()
+    shapes = [(300, 4160), (64, 16), (1000, 11008), (257, 2064)]
+    specs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        say(f"grouped split plan M={M} problem {i}: N={N} K={K}")
+        x_np = S.random_x(900 + 10 * i + M, M, K, "t3")
+        Wt = S.random_ternary(901 + 10 * i, N, K)
+        g = np.float32(0.0131 + 0.001 * i)
+        packed = torch.empty(L.bitlinear_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+        L.bitlinear_pack_ternary(torch.from_numpy(Wt).cuda(), N, K, packed)
+        specs.append(dict(x=torch.from_numpy(x_np).cuda(), xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                          eta=torch.empty(M, dtype=torch.float32, device="cuda"), packed=packed,
+                          y=torch.empty((M, N), dtype=torch.float32, device="cuda"),
+                          y_int=torch.empty((M, N), dtype=torch.int32, device="cuda"), gamma=g, N=N, K=K))
+        refs.append((x_np, Wt, g))
+    probs = L.make_problems(specs)
+    tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
+    table = torch.empty(tb, dtype=torch.uint8, device="cuda")
+    plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
+    # split: more work units than 256-row blocks, partials in the table
+    assert plan.units > sum((N + 255) // 256 for N, _ in shapes)
+    assert tb >= plan.units * M * 256 * 4
+    for rep in range(2):
+        L.bitlinear_forward_grouped(plan)
+        torch.cuda.synchronize()
+        for s, (x_np, Wt, g) in zip(specs, refs):
+            y_ref, _, _, y_int_ref = oracle.forward(x_np, Wt, g, threads=THREADS)
+            assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref)
+            assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+# A grouped plan past 64 tokens with enough 256-row blocks to fill the chip
+# takes the prefill tiles (128 x 256 per workgroup): ragged N (whole waves
+# past N), K with tail blocks, own row sums per tile.
+@pytest.mark.parametrize("M", [130, 200])
+def test_grouped_prefill_tiles(M):
+    torch = torch_cuda()
+    L = bl()
+    shapes = [(33000, 80), (32832, 208), (300, 1040)]
+    specs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        say(f"grouped prefill M={M} problem {i}: N={N} K={K}")
+        x_np = S.random_x(700 + 10 * i + M, M, K, "t3")
+        Wt = S.random_ternary(701 + 10 * i, N, K)
+        g = np.float32(0.021 + 0.002 * i)
+        packed = torch.empty(L.bitlinear_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+        L.bitlinear_pack_ternary(torch.from_numpy(Wt).cuda(), N, K, packed)
+        specs.append(dict(x=torch.from_numpy(x_np).cuda(), xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                          eta=torch.empty(M, dtype=torch.float32, device="cuda"), packed=packed,
+                          y=torch.empty((M, N), dtype=torch.float32, device="cuda"),
+                          y_int=torch.empty((M, N), dtype=torch.int32, device="cuda"), gamma=g, N=N, K=K))
+        refs.append((x_np, Wt, g))
+    probs = L.make_problems(specs)
+    tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
+    table = torch.empty(tb, dtype=torch.uint8, device="cuda")
+    plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
+    assert plan.units == sum((N + 255) // 256 for N, _ in shapes)   # one unit per 256 columns
+    L.bitlinear_forward_grouped(plan)
+    torch.cuda.synchronize()
+    for s, (x_np, Wt, g) in zip(specs, refs):
+        y_ref, _, _, y_int_ref = oracle.forward(x_np, Wt, g, threads=THREADS)
+        assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref)
+        assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
