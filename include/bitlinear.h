@@ -310,8 +310,8 @@ typedef struct bitlinear_grouped_plan {
 } bitlinear_grouped_plan;
 
 /* Device bytes the work table for these problems needs (host only).  Plans
- * at 5 .. 64 tokens whose 256-row blocks would leave CUs idle (a single
- * transformer block, say) split their K loops, and the table then also
+ * past 4 tokens whose 256-row blocks would leave CUs idle (a single
+ * transformer block, say) may split their K loops, and the table then also
  * holds the int32 partial sums (M x 256 x 4 bytes per work unit). */
 size_t bitlinear_grouped_table_bytes(const bitlinear_problem* problems_host, int32_t count,
                                      int64_t M);

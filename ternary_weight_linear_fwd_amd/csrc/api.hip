@@ -112,9 +112,12 @@ F32Ws f32_ws(int64_t M, int64_t N, int64_t K) {
     return w;
 }
 
-// Contraction kernel of a grouped plan: 0 dot4 GEMV, 1 prefill MFMA, 2 skinny
-// MFMA, 3 skinny MFMA with K split (partials in the table, then an epilogue).
-constexpr int32_t kPlanGemv = 0, kPlanGemm = 1, kPlanSkinny = 2, kPlanSkinnySplit = 3;
+// Contraction kernel of a grouped plan: 0 dot4 GEMV, 1 prefill MFMA (128 x
+// 256 tiles), 2 skinny MFMA, 3 skinny MFMA with K split, 4 prefill MFMA
+// (64 x 256 tiles) with K split (split plans: partials in the table, then an
+// epilogue), 5 prefill MFMA (64 x 256 tiles).
+constexpr int32_t kPlanGemv = 0, kPlanGemm = 1, kPlanSkinny = 2, kPlanSkinnySplit = 3, kPlanGemmSplit = 4,
+                  kPlanGemmSmall = 5;
 
 struct TableLayout {
     size_t problems_off, units_off, rows_off, part_off, bytes;
@@ -128,7 +131,8 @@ TableLayout table_layout(int64_t count, int64_t nunits, int64_t nrows, int32_t k
     t.units_off = align256((size_t)count * sizeof(Problem));
     t.rows_off = t.units_off + align256((size_t)nunits * sizeof(Unit));
     t.part_off = t.rows_off + align256((size_t)nrows * sizeof(QuantRow));
-    const size_t part = kernel == kPlanSkinnySplit ? (size_t)nunits * (size_t)M * kSkinnyRows * sizeof(int32_t) : 0;
+    const bool split = kernel == kPlanSkinnySplit || kernel == kPlanGemmSplit;   // 256-column units, both
+    const size_t part = split ? (size_t)nunits * (size_t)M * kSkinnyRows * sizeof(int32_t) : 0;
     t.bytes = t.part_off + align256(part);
     return t;
 }
@@ -177,6 +181,39 @@ void choose_slices(std::vector<Problem>& problems, int64_t M, int cus) {
     }
 }
 
+// A grouped prefill plan past 64 tokens whose 128 x 256 tiles would not give
+// every CU kGemmSmallBelow of them (one block at 65 .. a few hundred tokens)
+// takes 64 x 256 tiles instead, and problems with long K loops are cut into
+// slices of about equal length (whole 128-k steps, at least
+// kGemmSplitMinSteps), aiming at three workgroups per two CUs.  Few slices
+// measured best (the partials cost more than a deeper grid gains), so only
+// the long projections split: hidden 4096 / FFN 11008 at M = 128, the down
+// projection in three.  Returns whether the plan is small; slices > 1
+// where a problem is split.
+constexpr int64_t kGemmSmallBelow = 2;
+constexpr int64_t kGemmSplitMinSteps = 32;
+
+bool choose_gemm_slices(std::vector<Problem>& problems, int64_t M, int cus) {
+    int64_t big = 0, work = 0;   // work: 64 x 256 tiles x 128-k steps
+    for (const Problem& p : problems) {
+        big += ceil_div(p.N, 256) * ceil_div(M, 128);
+        work += ceil_div(p.N, 256) * ceil_div(M, 64) * ceil_div(p.Kb, 2);
+    }
+    if (big >= kGemmSmallBelow * cus) return false;
+    int64_t len = ceil_div(2 * work, 3 * (int64_t)cus);   // steps per slice
+    if (len < kGemmSplitMinSteps) len = kGemmSplitMinSteps;
+    for (Problem& p : problems) {
+        const int64_t nsteps = ceil_div(p.Kb, 2);
+        int64_t S = ceil_div(nsteps, len);
+        if (S > kGroupedSplitMaxSlices) S = kGroupedSplitMaxSlices;
+        while (S > 1 && (S - 1) * ceil_div(nsteps, S) >= nsteps) --S;   // no empty slice
+        p.slices = (int32_t)(S < 1 ? 1 : S);
+    }
+    return true;
+}
+
+constexpr int64_t kSmallPlanTiledFromM = 17;
+
 struct PlanHost {
     std::vector<Problem> problems;
     std::vector<Unit> units;
@@ -214,16 +251,35 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
         out.problems.push_back(make_problem(q.xq, q.eta, q.packed, q.gamma, q.N, q.K, q.y, q.y_int));
     }
     out.kernel = plan_kernel(M);
+    if (out.kernel == kPlanSkinny && M >= kSmallPlanTiledFromM) {
+        // Small plans take the 64 x 256 prefill tiles from kSmallPlanTiledFromM
+        // tokens on (every 64-row tile then at least half used).
+        std::vector<Problem> trial = out.problems;
+        if (choose_gemm_slices(trial, M, device_cus())) {
+            out.problems = trial;
+            out.kernel = kPlanGemmSmall;
+            for (const Problem& p : out.problems)
+                if (p.slices > 1) out.kernel = kPlanGemmSplit;
+        }
+    }
     if (out.kernel == kPlanSkinny && M > 0) {
         choose_slices(out.problems, M, device_cus());
         for (const Problem& p : out.problems)
             if (p.slices > 1) out.kernel = kPlanSkinnySplit;
     }
+    if (out.kernel == kPlanGemm && choose_gemm_slices(out.problems, M, device_cus())) {
+        out.kernel = kPlanGemmSmall;
+        for (const Problem& p : out.problems)
+            if (p.slices > 1) out.kernel = kPlanGemmSplit;
+    }
     // Units: each problem's blocks in order, the K-slices of a block adjacent.
     for (int32_t i = 0; i < count; ++i) {
         Problem& p = out.problems[i];
         p.unit_begin = (int32_t)out.units.size();
-        const int64_t nu = problem_units(out.kernel == kPlanSkinnySplit ? kPlanSkinny : out.kernel, M, p.N);
+        const int32_t k = out.kernel == kPlanSkinnySplit ? kPlanSkinny
+                          : (out.kernel == kPlanGemmSplit || out.kernel == kPlanGemmSmall) ? kPlanGemm
+                                                                                          : out.kernel;
+        const int64_t nu = problem_units(k, M, p.N);
         for (int64_t g = 0; g < nu; ++g)
             for (int32_t s = 0; s < p.slices; ++s) out.units.push_back(Unit{i, (int32_t)g});
         if (out.units.size() >= (size_t)kMaxDim) return BITLINEAR_EUNSUPPORTED;
@@ -515,7 +571,7 @@ int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t 
 int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) {
     if (!plan || !plan->table || plan->count <= 0 || plan->M < 0) return BITLINEAR_EINVAL;
     if (plan->M == 0) return BITLINEAR_OK;
-    if (plan->kernel < kPlanGemv || plan->kernel > kPlanSkinnySplit) return BITLINEAR_EINVAL;
+    if (plan->kernel < kPlanGemv || plan->kernel > kPlanGemmSmall) return BITLINEAR_EINVAL;
     const TableLayout L = table_layout(plan->count, plan->units, plan->quant_rows, plan->kernel, plan->M);
     if (plan->table_bytes < L.bytes) return BITLINEAR_EINVAL;
     const char* base = (const char*)plan->table;
@@ -533,7 +589,11 @@ int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) 
         case kPlanSkinnySplit:
             return launch_skinny_grouped(problems, units, plan->units, plan->M,
                                          reinterpret_cast<int32_t*>(static_cast<char*>(plan->table) + L.part_off), s);
-        default: return launch_gemm_grouped(problems, units, plan->units, plan->M, s);
+        case kPlanGemmSplit:
+            return launch_gemm_grouped(problems, units, plan->units, plan->M, true,
+                                       reinterpret_cast<int32_t*>(static_cast<char*>(plan->table) + L.part_off), s);
+        case kPlanGemmSmall: return launch_gemm_grouped(problems, units, plan->units, plan->M, true, nullptr, s);
+        default: return launch_gemm_grouped(problems, units, plan->units, plan->M, false, nullptr, s);
     }
 }
 

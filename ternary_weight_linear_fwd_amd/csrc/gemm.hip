@@ -355,9 +355,9 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     static_assert(NS == 3 || NS == 4, "ring of three or four stages");
     using Ctx = PrefillCtx<MT, NT>;
     constexpr int BM = Ctx::BM;
-    // Only single launches of 32 x 128 tiles split K (the larger tiles have
-    // no registers to spare for it).
-    constexpr bool SPLIT = !GROUPED && MT == 1 && NT == 1;
+    // K split: single launches of 32 x 128 tiles, grouped launches of
+    // 64 x 256 tiles (the larger tiles have no registers to spare for it).
+    constexpr bool SPLIT = (!GROUPED && MT == 1 && NT == 1) || (GROUPED && MT == 2 && NT == 2);
     // Up to four stages, each its own LDS object, so that the compiler can
     // tell a read of one stage from the loads in flight into the others.
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[Ctx::AStage];
@@ -377,6 +377,8 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
         p = a.problems[un.problem];
         tile_n = un.group;
         tile_m = blockIdx.y;
+        // Split plans: the K-slices of a column tile are adjacent units.
+        if (SPLIT && p.slices > 1) slice = (int64_t)blockIdx.x - p.unit_begin - tile_n * p.slices;
     } else {
         p = a.p;
         // Split K: consecutive workgroups are the slices of one tile.
@@ -397,9 +399,11 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     c.Kb = Kb;
     c.kstep0 = 0;
     c.nsteps = ceil_div(Kb, 2);
-    if (SPLIT && a.S > 1) {   // this slice's steps (never empty: the host sizes slices)
-        c.kstep0 = slice * (int64_t)a.sps;
-        c.nsteps = c.nsteps - c.kstep0 < a.sps ? c.nsteps - c.kstep0 : a.sps;
+    const bool split = SPLIT && (GROUPED ? p.slices > 1 : a.S > 1);
+    if (split) {   // this slice's steps (never empty: the host sizes slices)
+        const int64_t sps = GROUPED ? ceil_div(c.nsteps, (int64_t)p.slices) : (int64_t)a.sps;
+        c.kstep0 = slice * sps;
+        c.nsteps = c.nsteps - c.kstep0 < sps ? c.nsteps - c.kstep0 : sps;
     }
     c.wave = wave;
     c.lane = lane;
@@ -471,10 +475,13 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
     bool col[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) col[t] = n0 + 32 * t < N;
-    if (SPLIT && a.partial) {
+    if (split) {
         // Split K: this slice's integer sums (its own row sums taken off);
         // the split-K epilogue adds the slices in order and dequantizes.
-        int32_t* pcol = a.partial + (slice * M + m0) * N + n0;
+        // Single: [S][M][N]; grouped: [unit][M][256].
+        int32_t* pcol = GROUPED ? a.partial + ((int64_t)blockIdx.x * M + m0) * kPreBN + (n0 - tile_n * kPreBN)
+                                : a.partial + (slice * M + m0) * N + n0;
+        const int64_t ld = GROUPED ? kPreBN : N;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -484,7 +491,7 @@ __global__ __launch_bounds__(256, prefill_occupancy(MT, NT)) void gemm_prefill_k
                     const int r = i * 32 + j * 8 + lg * 4 + q;
                     if (m0 + r >= M) continue;
                     const uint32_t xs = (uint32_t)__float_as_int(rowinfo[r].x);
-                    int32_t* pr = pcol + (int64_t)r * N;
+                    int32_t* pr = pcol + (int64_t)r * ld;
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
                         if (col[t]) pr[32 * t] = (int)((uint32_t)acc[i][t][j * 4 + q] - xs);
@@ -760,17 +767,25 @@ bool gemm_beats_skinny(int64_t M, int64_t N) {
     return M > 16;
 }
 
-int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
-                        hipStream_t stream) {
-    // Grouped prefill keeps 128 x 256 tiles (grid.y = row tiles).
+int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M, bool small,
+                        int32_t* partial, hipStream_t stream) {
+    // Grouped prefill: 128 x 256 tiles (grid.y = row tiles); plans too small
+    // to fill the chip with them take 64 x 256 tiles, some with split K.
     GemmArgs a{};
     a.problems = problems;
     a.units = units;
     a.M = M;
-    hipLaunchKernelGGL((gemm_prefill_kernel<4, 2, true, prefill_stages(4, 2), false>), dim3((unsigned)nunits, (unsigned)ceil_div(M, 128)),
-                       dim3(256), 0, stream, a);
+    a.partial = partial;
+    if (!small) {
+        hipLaunchKernelGGL((gemm_prefill_kernel<4, 2, true, prefill_stages(4, 2), false>),
+                           dim3((unsigned)nunits, (unsigned)ceil_div(M, 128)), dim3(256), 0, stream, a);
+        BL_LAUNCH_CHECK();
+        return BITLINEAR_OK;
+    }
+    hipLaunchKernelGGL((gemm_prefill_kernel<2, 2, true, prefill_stages(2, 2), false>),
+                       dim3((unsigned)nunits, (unsigned)ceil_div(M, 64)), dim3(256), 0, stream, a);
     BL_LAUNCH_CHECK();
-    return BITLINEAR_OK;
+    return partial ? launch_grouped_splitk_epilogue(problems, units, nunits, M, partial, stream) : BITLINEAR_OK;
 }
 
 }  // namespace bl

@@ -70,6 +70,12 @@ int launch_gemv_grouped(const Problem* problems, const Unit* units, int64_t nuni
 // Sum split-K partials [S][M][N] in slice order and apply the dequant epilogue.
 int launch_splitk_epilogue(const int32_t* partial, int S, int64_t M, const Problem& p,
                            hipStream_t stream);
+// Grouped: problem p's units are its 256-column blocks, each cut into
+// p.slices K-slices (consecutive units); unit u's int32 sums sit at
+// partial + u * M * 256 as [m][256].  Adds each block's slices in order and
+// dequantizes (problems with p.slices == 1 are left alone).
+int launch_grouped_splitk_epilogue(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
+                                   const int32_t* partial, hipStream_t stream);
 
 // ---- decode contraction on int8 MFMA for 4 < M <= 64 (skinny.hip)
 constexpr int kSkinnyMaxM = 64;
@@ -93,7 +99,10 @@ __host__ __device__ inline int64_t skinny_slice_kb(int64_t Kb, int64_t S) {
 // ---- prefill contraction on int8 MFMA for M > 64 (gemm.hip; the single
 // launch is declared in gemm.hpp)
 int gemm_tile_n(int64_t M);  // output rows per workgroup (column tile) for M
-int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
-                        hipStream_t stream);
+// small false: 128 x 256 tiles over whole K loops.  small true: 64 x 256
+// tiles; with partial, problem p's K loop in p.slices slices (units and
+// partials as for launch_grouped_splitk_epilogue, which follows).
+int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M, bool small,
+                        int32_t* partial, hipStream_t stream);
 
 }  // namespace bl

@@ -254,15 +254,16 @@ int launch_skinny(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
     return BITLINEAR_OK;
 }
 
-// Grouped split-K epilogue, grid (units, row chunks): the workgroups of a
-// block's first slice add the block's slices in order for kEpiRows token rows
+// Grouped split-K epilogue (shared with the grouped prefill tiles, whose
+// column tiles are 256 wide too), grid (units, row chunks): the workgroups
+// of a block's first slice add the block's slices in order for kEpiRows token rows
 // (thread = output row n of the block) and apply the dequant; every other
 // unit, and blocks of unsplit problems, exit.  The slice loop is unrolled to
 // its maximum, so that a thread's loads are all in flight at once rather
 // than one memory round trip per slice.
 constexpr int kEpiRows = 4;
 
-__global__ __launch_bounds__(256) void skinny_grouped_epilogue_kernel(const Problem* __restrict__ problems,
+__global__ __launch_bounds__(256) void grouped_splitk_epilogue_kernel(const Problem* __restrict__ problems,
                                                                       const Unit* __restrict__ units, int64_t M,
                                                                       const int32_t* __restrict__ gpart) {
     const int64_t u = blockIdx.x;
@@ -303,8 +304,13 @@ int launch_skinny_grouped(const Problem* problems, const Unit* units, int64_t nu
     a.M = (int32_t)M;
     const int rc = launch_skinny_any(a, true, stream);
     if (rc || !partial) return rc;
-    hipLaunchKernelGGL(skinny_grouped_epilogue_kernel, dim3((unsigned)nunits, (unsigned)ceil_div(M, kEpiRows)),
-                       dim3(256), 0, stream, problems, units, M, (const int32_t*)partial);
+    return launch_grouped_splitk_epilogue(problems, units, nunits, M, partial, stream);
+}
+
+int launch_grouped_splitk_epilogue(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
+                                   const int32_t* partial, hipStream_t stream) {
+    hipLaunchKernelGGL(grouped_splitk_epilogue_kernel, dim3((unsigned)nunits, (unsigned)ceil_div(M, kEpiRows)),
+                       dim3(256), 0, stream, problems, units, M, partial);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
 }

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-@pytest.mark.parametrize("M", [1, 3, 8, 16, 40, 64])
+@pytest.mark.parametrize("M", [1, 3, 8, 16, 40, 64, 96])
 def test_grouped_block_matches_oracle(M):
     torch = torch_cuda()
     L = bl()
@@ -120,11 +120,11 @@ def test_grouped_mixed_row_lengths(M):
         assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
 
 
-# A small grouped plan at 5 .. 64 tokens (fewer 256-row blocks than CUs)
-# splits every problem's K loop in the streaming MFMA kernel: problems whose
-# K gives 1 .. 15 slices (one 16-k problem stays whole), ragged N and K, run
-# twice on the same table.
-@pytest.mark.parametrize("M", [24, 64])
+# A small grouped plan (fewer 256-row blocks than CUs) splits long K loops:
+# in the streaming MFMA kernel up to 16 tokens, in 64 x 256 prefill tiles
+# above.  Problems whose K gives one to many slices (a 16-k problem stays
+# whole), ragged M, N and K, run twice on the same table.
+@pytest.mark.parametrize("M", [12, 24, 64, 65, 128, 200])
 def test_grouped_split_k_small_plan(M):
     torch = torch_cuda()
     L = bl()
@@ -158,14 +158,16 @@ def test_grouped_split_k_small_plan(M):
             assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
 
 
-# A grouped plan past 64 tokens with enough 256-row blocks to fill the chip
-# takes the prefill tiles (128 x 256 per workgroup): ragged N (whole waves
-# past N), K with tail blocks, own row sums per tile.
-@pytest.mark.parametrize("M", [130, 200])
-def test_grouped_prefill_tiles(M):
+# A grouped plan past 64 tokens with enough 256-column blocks to fill the
+# chip takes the 128 x 256 prefill tiles; a small one with short K loops the
+# 64 x 256 tiles without split: ragged N (whole waves past N), K with tail
+# blocks, own row sums per tile.
+@pytest.mark.parametrize("M,shapes", [(130, [(33000, 80), (32832, 208), (300, 1040)]),
+                                      (200, [(33000, 80), (32832, 208), (300, 1040)]),
+                                      (100, [(2000, 80), (1500, 208), (300, 1008)])])
+def test_grouped_prefill_tiles(M, shapes):
     torch = torch_cuda()
     L = bl()
-    shapes = [(33000, 80), (32832, 208), (300, 1040)]
     specs, refs = [], []
     for i, (N, K) in enumerate(shapes):
         say(f"grouped prefill M={M} problem {i}: N={N} K={K}")
