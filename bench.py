@@ -150,39 +150,51 @@ def bench_prefill(torch, L, S, reps: int):
     return out, mfma_ceiling
 
 
-def bench_c5(torch, L, S, reps: int):
-    """Batched decode with skewed sparsity (hidden 4096, FFN 11008; ternary
-    weights drawn directly, P(0) = 0.6; 1% outlier channels): the seven
-    projections of a block from float32 activations to float32 outputs,
-    (a) as one grouped forward (one quantize + one contraction launch) and
-    (b) as seven fused bitlinear_forward_f32 calls, for M = 32, 64, 128."""
+def bench_block(torch, L, S, reps: int, which: int):
+    """One transformer block's seven projections from float32 activations to
+    float32 outputs, (a) as one grouped forward (quantize + contraction, and
+    the split-K epilogue where the plan splits) and (b) as seven fused
+    bitlinear_forward_f32 calls.  which = 5: batched decode with skewed
+    sparsity (hidden 4096, FFN 11008; ternary weights drawn directly,
+    P(0) = 0.6; 1% outlier channels), M = 32, 64, 128.  which = 2: the
+    3B-shaped block (hidden 3200, FFN 8640; latent N(0, 0.02) weights), M = 1, 8."""
     import ctypes
     st = torch.cuda.current_stream().cuda_stream
+    projs = S.C5_PROJS if which == 5 else S.C2_PROJS
     packed, gammas = [], []
-    for p in S.C5_PROJS:
-        Wt, g = S.c5_ternary(p)
+    for p in projs:
         buf = torch.empty(L.bitlinear_packed_bytes(p.N, p.K), dtype=torch.uint8, device="cuda")
-        L.bitlinear_pack_ternary(torch.from_numpy(Wt).cuda(), p.N, p.K, buf)
+        if which == 5:
+            Wt, g = S.c5_ternary(p)
+            L.bitlinear_pack_ternary(torch.from_numpy(Wt).cuda(), p.N, p.K, buf)
+        else:
+            W = torch.from_numpy(S.c2_weight(p)).cuda()
+            wsb = L.bitlinear_workspace_bytes(0, p.N, p.K)
+            ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+            gh = ctypes.c_float()
+            L.bitlinear_pack_weights(W, p.N, p.K, buf, None, gh, ws, wsb)
+            g = gh.value
+            del W, ws
         packed.append(buf)
         gammas.append(float(g))
-    wbytes = sum(int(L.bitlinear_packed_bytes(p.N, p.K)) for p in S.C5_PROJS)
+    wbytes = sum(int(L.bitlinear_packed_bytes(p.N, p.K)) for p in projs)
     out = []
-    for M in (32, 64, 128):
-        xs = [torch.from_numpy(S.c5_x(p, M)).cuda() for p in S.C5_PROJS]
-        ys = [torch.empty((M, p.N), dtype=torch.float32, device="cuda") for p in S.C5_PROJS]
-        xqs = [torch.empty((M, p.K), dtype=torch.int8, device="cuda") for p in S.C5_PROJS]
-        etas = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in S.C5_PROJS]
+    for M in ((32, 64, 128) if which == 5 else (1, 8)):
+        xs = [torch.from_numpy(S.c5_x(p, M) if which == 5 else S.c2_x(p, M)).cuda() for p in projs]
+        ys = [torch.empty((M, p.N), dtype=torch.float32, device="cuda") for p in projs]
+        xqs = [torch.empty((M, p.K), dtype=torch.int8, device="cuda") for p in projs]
+        etas = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in projs]
         specs = [dict(x=x, xq=xq, eta=eta, packed=w, y=y, y_int=None, gamma=g, N=p.N, K=p.K)
-                 for p, x, xq, eta, w, y, g in zip(S.C5_PROJS, xs, xqs, etas, packed, ys, gammas)]
+                 for p, x, xq, eta, w, y, g in zip(projs, xs, xqs, etas, packed, ys, gammas)]
         probs = L.make_problems(specs)
         tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
         table = torch.empty(tb, dtype=torch.uint8, device="cuda")
         plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
-        wsb = max(L.bitlinear_workspace_bytes(M, p.N, p.K) for p in S.C5_PROJS)
+        wsb = max(L.bitlinear_workspace_bytes(M, p.N, p.K) for p in projs)
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
         # Raw addresses resolved once, outside the timed loops.
         calls = [(x.data_ptr(), w.data_ptr(), g, p.N, p.K, y.data_ptr())
-                 for p, x, w, y, g in zip(S.C5_PROJS, xs, packed, ys, gammas)]
+                 for p, x, w, y, g in zip(projs, xs, packed, ys, gammas)]
         wsp = ws.data_ptr()
 
         def singles():
@@ -196,15 +208,17 @@ def bench_c5(torch, L, S, reps: int):
             torch.cuda.synchronize()
         g_ms = time_events(torch, grouped, reps)
         s_ms = time_events(torch, singles, reps)
-        ops = 2 * M * sum(p.N * p.K for p in S.C5_PROJS)
+        ops = 2 * M * sum(p.N * p.K for p in projs)
         best = min(g_ms, s_ms)
         out.append({"M": M, "grouped_us": round(g_ms * 1e3, 2), "single_calls_us": round(s_ms * 1e3, 2),
                     "weight_gbs": round(wbytes / (best * 1e-3) / 1e9, 1),
                     "tops": round(ops / (best * 1e-3) / 1e12, 1)})
         del xs, ys, xqs, etas, table, ws
-    return {"workload": "hidden 4096, FFN 11008 block (q,k,v,o 4096->4096; gate,up 4096->11008; "
-                        "down 11008->4096), ternary P(0)=0.6, 1% outlier channels x20, float32 in/out",
-            "packed_weight_bytes": wbytes, "per_M": out}
+    workload = ("hidden 4096, FFN 11008 block (q,k,v,o 4096->4096; gate,up 4096->11008; down 11008->4096), "
+                "ternary P(0)=0.6, 1% outlier channels x20, float32 in/out") if which == 5 else \
+               ("hidden 3200, FFN 8640 block (q,k,v,o 3200->3200; gate,up 3200->8640; down 8640->3200), "
+                "latent N(0,0.02) weights, x ~ N(0,1), float32 in/out")
+    return {"workload": workload, "packed_weight_bytes": wbytes, "per_M": out}
 
 
 def bench_mfma_ceiling(torch, L, xq, packed) -> dict:
@@ -562,10 +576,11 @@ def main() -> int:
         extra["prefill"] = prefill
 
     if not args.no_prefill:
-        extra["batched_decode_c5"] = bench_c5(torch, L, S, max(10, args.steps))
-        for r in extra["batched_decode_c5"]["per_M"]:
-            log(f"C5 block M={r['M']}: grouped {r['grouped_us']} us, seven single calls "
-                f"{r['single_calls_us']} us ({r['weight_gbs']} GB/s of weights, {r['tops']} TOP/s)")
+        for which, key in ((2, "block_decode_c2"), (5, "batched_decode_c5")):
+            extra[key] = bench_block(torch, L, S, max(10, args.steps), which)
+            for r in extra[key]["per_M"]:
+                log(f"C{which} block M={r['M']}: grouped {r['grouped_us']} us, seven single calls "
+                    f"{r['single_calls_us']} us ({r['weight_gbs']} GB/s of weights, {r['tops']} TOP/s)")
 
     if not args.no_prefill:
         extra["rmsnorm_quant"] = bench_rmsnorm(torch, L, S, max(10, args.steps))

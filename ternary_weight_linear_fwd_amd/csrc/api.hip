@@ -115,9 +115,9 @@ F32Ws f32_ws(int64_t M, int64_t N, int64_t K) {
 // Contraction kernel of a grouped plan: 0 dot4 GEMV, 1 prefill MFMA (128 x
 // 256 tiles), 2 skinny MFMA, 3 skinny MFMA with K split, 4 prefill MFMA
 // (64 x 256 tiles) with K split (split plans: partials in the table, then an
-// epilogue), 5 prefill MFMA (64 x 256 tiles).
+// epilogue), 5 prefill MFMA (64 x 256 tiles), 6 dot4 GEMV with K split.
 constexpr int32_t kPlanGemv = 0, kPlanGemm = 1, kPlanSkinny = 2, kPlanSkinnySplit = 3, kPlanGemmSplit = 4,
-                  kPlanGemmSmall = 5;
+                  kPlanGemmSmall = 5, kPlanGemvSplit = 6;
 
 struct TableLayout {
     size_t problems_off, units_off, rows_off, part_off, bytes;
@@ -131,8 +131,9 @@ TableLayout table_layout(int64_t count, int64_t nunits, int64_t nrows, int32_t k
     t.units_off = align256((size_t)count * sizeof(Problem));
     t.rows_off = t.units_off + align256((size_t)nunits * sizeof(Unit));
     t.part_off = t.rows_off + align256((size_t)nrows * sizeof(QuantRow));
-    const bool split = kernel == kPlanSkinnySplit || kernel == kPlanGemmSplit;   // 256-column units, both
-    const size_t part = split ? (size_t)nunits * (size_t)M * kSkinnyRows * sizeof(int32_t) : 0;
+    const size_t width = kernel == kPlanGemvSplit ? 64   // output rows per work unit
+                         : (kernel == kPlanSkinnySplit || kernel == kPlanGemmSplit) ? kSkinnyRows : 0;
+    const size_t part = (size_t)nunits * (size_t)M * width * sizeof(int32_t);
     t.bytes = t.part_off + align256(part);
     return t;
 }
@@ -214,6 +215,35 @@ bool choose_gemm_slices(std::vector<Problem>& problems, int64_t M, int cus) {
 
 constexpr int64_t kSmallPlanTiledFromM = 17;
 
+// K-slices per 64-row group for a grouped dot4 plan (M <= 4) whose groups
+// alone give the chip fewer than kGemvSmallWaves wavefronts (one transformer
+// block: 520 groups for hidden 3200 / FFN 8640), cut into slices of about
+// equal length aiming at kGemvSplitWaves wavefronts, at least
+// kGemvSplitMinKb k-blocks each.
+constexpr int64_t kGemvSmallWaves = 8192;
+constexpr int64_t kGemvSplitWaves = 4096;
+constexpr int64_t kGemvSplitMinKb = 8;
+
+bool choose_gemv_slices(std::vector<Problem>& problems) {
+    int64_t groups = 0, work = 0;   // work: 64-row groups x k-blocks
+    for (const Problem& p : problems) {
+        groups += ceil_div(p.N, 64);
+        work += ceil_div(p.N, 64) * p.Kb;
+    }
+    if (groups >= kGemvSmallWaves) return false;
+    int64_t len = ceil_div(work, kGemvSplitWaves);
+    if (len < kGemvSplitMinKb) len = kGemvSplitMinKb;
+    bool any = false;
+    for (Problem& p : problems) {
+        int64_t S = ceil_div(p.Kb, len);
+        if (S > kSkinnyMaxSlices) S = kSkinnyMaxSlices;
+        while (S > 1 && (S - 1) * ceil_div(p.Kb, S) >= p.Kb) --S;   // no empty slice
+        p.slices = (int32_t)(S < 1 ? 1 : S);
+        any = any || p.slices > 1;
+    }
+    return any;
+}
+
 struct PlanHost {
     std::vector<Problem> problems;
     std::vector<Unit> units;
@@ -251,6 +281,7 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
         out.problems.push_back(make_problem(q.xq, q.eta, q.packed, q.gamma, q.N, q.K, q.y, q.y_int));
     }
     out.kernel = plan_kernel(M);
+    if (out.kernel == kPlanGemv && M > 0 && choose_gemv_slices(out.problems)) out.kernel = kPlanGemvSplit;
     if (out.kernel == kPlanSkinny && M >= kSmallPlanTiledFromM) {
         // Small plans take the 64 x 256 prefill tiles from kSmallPlanTiledFromM
         // tokens on (every 64-row tile then at least half used).
@@ -278,6 +309,7 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
         p.unit_begin = (int32_t)out.units.size();
         const int32_t k = out.kernel == kPlanSkinnySplit ? kPlanSkinny
                           : (out.kernel == kPlanGemmSplit || out.kernel == kPlanGemmSmall) ? kPlanGemm
+                          : out.kernel == kPlanGemvSplit                                  ? kPlanGemv
                                                                                           : out.kernel;
         const int64_t nu = problem_units(k, M, p.N);
         for (int64_t g = 0; g < nu; ++g)
@@ -571,7 +603,7 @@ int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t 
 int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) {
     if (!plan || !plan->table || plan->count <= 0 || plan->M < 0) return BITLINEAR_EINVAL;
     if (plan->M == 0) return BITLINEAR_OK;
-    if (plan->kernel < kPlanGemv || plan->kernel > kPlanGemmSmall) return BITLINEAR_EINVAL;
+    if (plan->kernel < kPlanGemv || plan->kernel > kPlanGemvSplit) return BITLINEAR_EINVAL;
     const TableLayout L = table_layout(plan->count, plan->units, plan->quant_rows, plan->kernel, plan->M);
     if (plan->table_bytes < L.bytes) return BITLINEAR_EINVAL;
     const char* base = (const char*)plan->table;
@@ -584,7 +616,10 @@ int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) 
     if (plan->quant_rows) rc = launch_quantize_grouped(rows, plan->quant_rows, s);
     if (rc) return rc;
     switch (plan->kernel) {
-        case kPlanGemv: return launch_gemv_grouped(problems, units, plan->units, plan->M, s);
+        case kPlanGemv: return launch_gemv_grouped(problems, units, plan->units, plan->M, nullptr, s);
+        case kPlanGemvSplit:
+            return launch_gemv_grouped(problems, units, plan->units, plan->M,
+                                       reinterpret_cast<int32_t*>(static_cast<char*>(plan->table) + L.part_off), s);
         case kPlanSkinny: return launch_skinny_grouped(problems, units, plan->units, plan->M, nullptr, s);
         case kPlanSkinnySplit:
             return launch_skinny_grouped(problems, units, plan->units, plan->M,

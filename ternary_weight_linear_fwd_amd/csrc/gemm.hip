@@ -785,7 +785,7 @@ int launch_gemm_grouped(const Problem* problems, const Unit* units, int64_t nuni
     hipLaunchKernelGGL((gemm_prefill_kernel<2, 2, true, prefill_stages(2, 2), false>),
                        dim3((unsigned)nunits, (unsigned)ceil_div(M, 64)), dim3(256), 0, stream, a);
     BL_LAUNCH_CHECK();
-    return partial ? launch_grouped_splitk_epilogue(problems, units, nunits, M, partial, stream) : BITLINEAR_OK;
+    return partial ? launch_grouped_splitk_epilogue(problems, units, nunits, M, kPreBN, partial, stream) : BITLINEAR_OK;
 }
 
 }  // namespace bl

@@ -71,7 +71,8 @@ struct GemvArgs {
     Problem p;              // single-problem mode
     SplitK sk;
     const Problem* problems;  // grouped mode
-    const Unit* units;
+    const Unit* units;        // K-slices of a 64-row group in adjacent units
+    int32_t* gpart;           // grouped, K split: [unit][M][64] int32 partial sums
     int64_t nunits;
 };
 
@@ -91,6 +92,12 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs a) {
         g = un.group;
         kb0 = 0;
         kb1 = p.Kb;
+        if (p.slices > 1) {
+            slice = u - p.unit_begin - g * p.slices;
+            const int64_t kbs = (p.Kb + p.slices - 1) / p.slices;
+            kb0 = slice * kbs;
+            kb1 = kb0 + kbs < p.Kb ? kb0 + kbs : p.Kb;
+        }
     } else {
         p = a.p;
         const int S = a.sk.S;
@@ -151,6 +158,11 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs a) {
     }
 
     if (row >= N) return;
+    if (GROUPED && p.slices > 1) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) a.gpart[(u * M + m) * 64 + lane] = res[m];
+        return;
+    }
     if (!GROUPED && a.sk.S > 1) {
 #pragma unroll
         for (int m = 0; m < M; ++m) a.sk.partial[(slice * M + m) * N + row] = res[m];
@@ -241,10 +253,11 @@ static void launch_grouped(const GemvArgs& a, int64_t blocks, hipStream_t stream
 }
 
 int launch_gemv_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
-                        hipStream_t stream) {
+                        int32_t* partial, hipStream_t stream) {
     GemvArgs a{};
     a.problems = problems;
     a.units = units;
+    a.gpart = partial;
     a.nunits = nunits;
     const int64_t blocks = ceil_div(nunits, kGemvWaves);
     switch (M) {
@@ -255,7 +268,7 @@ int launch_gemv_grouped(const Problem* problems, const Unit* units, int64_t nuni
         default: return BITLINEAR_EUNSUPPORTED;
     }
     BL_LAUNCH_CHECK();
-    return BITLINEAR_OK;
+    return partial ? launch_grouped_splitk_epilogue(problems, units, nunits, M, 64, partial, stream) : BITLINEAR_OK;
 }
 
 }  // namespace bl

@@ -64,18 +64,21 @@ constexpr int kGemvMaxM = 4;
 int gemv_split_slices(int64_t M, int64_t N, int64_t K);
 size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K);
 int launch_gemv(const Problem& p, int64_t M, void* ws, hipStream_t stream);
+// partial: null, or (problems with slices > 1) [unit][M][64] int32 partial
+// sums added by launch_grouped_splitk_epilogue (width 64), which follows.
 int launch_gemv_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
-                        hipStream_t stream);
+                        int32_t* partial, hipStream_t stream);
 
 // Sum split-K partials [S][M][N] in slice order and apply the dequant epilogue.
 int launch_splitk_epilogue(const int32_t* partial, int S, int64_t M, const Problem& p,
                            hipStream_t stream);
-// Grouped: problem p's units are its 256-column blocks, each cut into
-// p.slices K-slices (consecutive units); unit u's int32 sums sit at
-// partial + u * M * 256 as [m][256].  Adds each block's slices in order and
-// dequantizes (problems with p.slices == 1 are left alone).
+// Grouped: problem p's units are its blocks of `width` (64 or 256) output
+// rows, each cut into p.slices K-slices (consecutive units); unit u's int32
+// sums sit at partial + u * M * width as [m][width].  Adds each block's
+// slices in order and dequantizes (problems with p.slices == 1 are left
+// alone).
 int launch_grouped_splitk_epilogue(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
-                                   const int32_t* partial, hipStream_t stream);
+                                   int width, const int32_t* partial, hipStream_t stream);
 
 // ---- decode contraction on int8 MFMA for 4 < M <= 64 (skinny.hip)
 constexpr int kSkinnyMaxM = 64;

@@ -263,25 +263,26 @@ int launch_skinny(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
 // than one memory round trip per slice.
 constexpr int kEpiRows = 4;
 
-__global__ __launch_bounds__(256) void grouped_splitk_epilogue_kernel(const Problem* __restrict__ problems,
-                                                                      const Unit* __restrict__ units, int64_t M,
-                                                                      const int32_t* __restrict__ gpart) {
+template <int W>   // unit width: output rows of a unit = threads of a workgroup
+__global__ __launch_bounds__(W) void grouped_splitk_epilogue_kernel(const Problem* __restrict__ problems,
+                                                                    const Unit* __restrict__ units, int64_t M,
+                                                                    const int32_t* __restrict__ gpart) {
     const int64_t u = blockIdx.x;
     const Unit un = units[u];
     const Problem p = problems[un.problem];
     if (p.slices <= 1 || u - p.unit_begin != (int64_t)un.group * p.slices) return;
-    const int64_t n = (int64_t)un.group * kSkinnyRows + threadIdx.x;
+    const int64_t n = (int64_t)un.group * W + threadIdx.x;
     const int64_t m0 = (int64_t)blockIdx.y * kEpiRows;
     if (n >= p.N || m0 >= M) return;
     const int rows = M - m0 < kEpiRows ? (int)(M - m0) : kEpiRows;
     const int S = p.slices;
-    const int32_t* __restrict__ src = gpart + (u * M + m0) * kSkinnyRows + threadIdx.x;
+    const int32_t* __restrict__ src = gpart + (u * M + m0) * W + threadIdx.x;
     int part[kSkinnyMaxSlices][kEpiRows];
 #pragma unroll
     for (int s = 0; s < kSkinnyMaxSlices; ++s)
 #pragma unroll
         for (int r = 0; r < kEpiRows; ++r)
-            part[s][r] = s < S && r < rows ? src[((int64_t)s * M + r) * kSkinnyRows] : 0;
+            part[s][r] = s < S && r < rows ? src[((int64_t)s * M + r) * W] : 0;
 #pragma unroll
     for (int r = 0; r < kEpiRows; ++r) {
         if (r >= rows) break;
@@ -304,13 +305,18 @@ int launch_skinny_grouped(const Problem* problems, const Unit* units, int64_t nu
     a.M = (int32_t)M;
     const int rc = launch_skinny_any(a, true, stream);
     if (rc || !partial) return rc;
-    return launch_grouped_splitk_epilogue(problems, units, nunits, M, partial, stream);
+    return launch_grouped_splitk_epilogue(problems, units, nunits, M, kSkinnyRows, partial, stream);
 }
 
 int launch_grouped_splitk_epilogue(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
-                                   const int32_t* partial, hipStream_t stream) {
-    hipLaunchKernelGGL(grouped_splitk_epilogue_kernel, dim3((unsigned)nunits, (unsigned)ceil_div(M, kEpiRows)),
-                       dim3(256), 0, stream, problems, units, M, partial);
+                                   int width, const int32_t* partial, hipStream_t stream) {
+    const dim3 grid((unsigned)nunits, (unsigned)ceil_div(M, kEpiRows));
+    if (width == 64)
+        hipLaunchKernelGGL(grouped_splitk_epilogue_kernel<64>, grid, dim3(64), 0, stream, problems, units, M, partial);
+    else if (width == 256)
+        hipLaunchKernelGGL(grouped_splitk_epilogue_kernel<256>, grid, dim3(256), 0, stream, problems, units, M, partial);
+    else
+        return BITLINEAR_EINVAL;
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
 }

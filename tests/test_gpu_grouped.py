@@ -120,11 +120,11 @@ def test_grouped_mixed_row_lengths(M):
         assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
 
 
-# A small grouped plan (fewer 256-row blocks than CUs) splits long K loops:
-# in the streaming MFMA kernel up to 16 tokens, in 64 x 256 prefill tiles
-# above.  Problems whose K gives one to many slices (a 16-k problem stays
+# A small grouped plan (too few row blocks to fill the chip) splits long K
+# loops: in the dot4 GEMV up to 4 tokens, the streaming MFMA kernel up to 16,
+# 64 x 256 prefill tiles above.  Problems whose K gives one to many slices (a 16-k problem stays
 # whole), ragged M, N and K, run twice on the same table.
-@pytest.mark.parametrize("M", [12, 24, 64, 65, 128, 200])
+@pytest.mark.parametrize("M", [2, 4, 12, 24, 64, 65, 128, 200])
 def test_grouped_split_k_small_plan(M):
     torch = torch_cuda()
     L = bl()
@@ -146,9 +146,11 @@ def test_grouped_split_k_small_plan(M):
     tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
     table = torch.empty(tb, dtype=torch.uint8, device="cuda")
     plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
-    # split: more work units than 256-row blocks, partials in the table
-    assert plan.units > sum((N + 255) // 256 for N, _ in shapes)
-    assert tb >= plan.units * M * 256 * 4
+    # split: more work units than row blocks (64 rows per unit for the
+    # dot4 GEMV, 256 otherwise), and the partials in the table
+    width = 64 if M <= 4 else 256
+    assert plan.units > sum((N + width - 1) // width for N, _ in shapes)
+    assert tb >= plan.units * M * width * 4
     for rep in range(2):
         L.bitlinear_forward_grouped(plan)
         torch.cuda.synchronize()
