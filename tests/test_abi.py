@@ -200,3 +200,35 @@ def test_no_undefined_library_symbols():
     # every kernel stub and helper of the library is defined in the .so
     out = subprocess.check_output(["nm", "-D", "--undefined-only", bl.LIB_PATH], text=True)
     assert not [l for l in out.splitlines() if "_ZN2bl" in l]
+
+
+def test_grouped_planner_splits_only_small_plans():
+    """Host logic of the grouped planner (no GPU: table sizes only).  A plan
+    whose row blocks leave CUs idle (one transformer block) splits its long K
+    loops and keeps int32 partial sums in the table, so the table grows by
+    at least one partial row per work unit for each extra token; a whole
+    model's plan, or a small one whose K loops are all short, keeps whole K
+    loops and its table does not grow with M (no activations to quantize
+    here, so no per-row entries either)."""
+    def plan_bytes(shapes, M, copies=1):
+        specs = [dict(x=None, xq=FAKE + 4096 * i, eta=FAKE + 256, packed=FAKE, y=FAKE, gamma=0.5, N=N, K=K)
+                 for i, (N, K) in enumerate(shapes * copies)]
+        n = bl.bitlinear_grouped_table_bytes(bl.make_problems(specs), len(specs), M)
+        assert n > 0
+        return n
+
+    block = [(3200, 3200)] * 4 + [(8640, 3200)] * 2 + [(3200, 8640)]   # hidden 3200 / FFN 8640
+    model = [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192), (28672, 8192), (28672, 8192),
+             (8192, 28672)]
+    groups64 = sum((N + 63) // 64 for N, _ in block)
+    blocks256 = sum((N + 255) // 256 for N, _ in block)
+    # dot4 GEMV (M <= 4): 64-row units
+    assert plan_bytes(block, 2) - plan_bytes(block, 1) >= groups64 * 64 * 4
+    assert plan_bytes(model, 2, copies=80) == plan_bytes(model, 1, copies=80)
+    # streaming MFMA kernel (5 .. 16 tokens): 256-row units
+    assert plan_bytes(block, 9) - plan_bytes(block, 8) >= blocks256 * 256 * 4
+    assert plan_bytes(model, 9, copies=80) == plan_bytes(model, 8, copies=80)
+    # 64 x 256 prefill tiles (17 tokens and up): only the long down projection splits
+    assert plan_bytes(block, 97) - plan_bytes(block, 96) >= 256 * 4 * ((3200 + 255) // 256)
+    short = [(2000, 80), (1500, 208), (300, 1008)]
+    assert plan_bytes(short, 97) == plan_bytes(short, 96)
