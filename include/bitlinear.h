@@ -282,7 +282,9 @@ int bitlinear_forward_lut(const int8_t* xq, const float* eta, const uint8_t* pac
  * Grouped forward: many independent BitLinear problems of the same token
  * count M in one pass (e.g. every projection of every layer of a decode
  * step).  Planning builds a work table in caller-owned device memory once;
- * each forward then queues at most two kernels (quantize all, contract all).
+ * each forward then queues at most three kernels: quantize all, contract all,
+ * and -- for a plan too small to fill the chip, whose long K loops the
+ * planner splits -- add the split partial sums and dequantize.
  */
 typedef struct bitlinear_problem {
     const float* x;        /* [M][K] float32, or NULL: xq/eta already hold the quantized rows */
