@@ -492,6 +492,9 @@ def main() -> int:
                          "1 GiB copy whose counters calibrate FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--profile-prefill", action="store_true",
                     help="short run for rocprofv3: the two 3B prefill GEMMs and a calibration copy")
+    ap.add_argument("--profile-blocks", action="store_true",
+                    help="time only the single-block grouped forwards (3B block at M=1, 8; "
+                         "hidden-4096 block at M=32, 64, 128), for a rocprofv3 run")
     ap.add_argument("--summarize", metavar="DIR", help="summarize rocprofv3 output under DIR")
     args = ap.parse_args()
     if args.summarize:
@@ -513,6 +516,12 @@ def main() -> int:
     Ms = (1,) if args.no_m16 else (1, 16)
     if args.profile_run:
         Ms = (args.profile_m,)
+    if args.profile_blocks:
+        for which in (2, 5):
+            for r in bench_block(torch, L, S, max(1, args.steps), which)["per_M"]:
+                log(f"C{which} block M={r['M']}: grouped {r['grouped_us']} us, seven single calls "
+                    f"{r['single_calls_us']} us")
+        return 0
     if args.profile_prefill:
         for r in bench_prefill(torch, L, S, max(1, args.steps))[0]:
             log(f"prefill {r['gemm']}: {r['us']} us; own row sums {r['us_own_row_sums']} us; "
