@@ -67,7 +67,9 @@ __global__ __launch_bounds__(THREADS) void quant_rows_kernel(const float* __rest
                                                              float* __restrict__ eta,
                                                              int32_t* __restrict__ xsum) {
     const int64_t m = blockIdx.x;
-    quant_row<THREADS, R>(x + m * K, K, xq + m * K, eta + m, xsum ? xsum + m : nullptr);
+    // Plain loads: 4 - 7% faster than non-temporal ones on 2048-row
+    // activations with K = 3200 .. 11008 (as for the grouped kernel).
+    quant_row<THREADS, R, false>(x + m * K, K, xq + m * K, eta + m, xsum ? xsum + m : nullptr);
 }
 
 // Grouped: one workgroup per row descriptor; rows of up to 32768 floats stay
