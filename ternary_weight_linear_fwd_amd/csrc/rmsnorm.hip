@@ -75,37 +75,51 @@ __device__ inline void f32_rounding_interval(float r, double& lo, double& hi) {
     hi = r == 3.40282347e38f ? over : 0.5 * (dr + (double)nextafterf(r, INFINITY));
 }
 
-// big += v * 2^s  (v < 2^56, s + 88 <= 32 * kLimbs)
-__device__ inline void big_add(uint32_t* big, uint64_t v, int s) {
-    const int limb = s >> 5, bit = s & 31;
-    const uint64_t a = (v & 0xffffffffull) << bit;   // bits [0, 63)
-    const uint64_t b = (v >> 32) << bit;             // bits [32, 32 + 55)
-    uint64_t acc = (uint64_t)big[limb] + (a & 0xffffffffull);
-    big[limb] = (uint32_t)acc;
-    acc = (acc >> 32) + (a >> 32) + (b & 0xffffffffull) + big[limb + 1];
-    big[limb + 1] = (uint32_t)acc;
-    acc = (acc >> 32) + (b >> 32) + big[limb + 2];
-    big[limb + 2] = (uint32_t)acc;
-    acc >>= 32;
-    for (int i = limb + 3; acc && i < kLimbs; ++i) {
-        acc += big[i];
-        big[i] = (uint32_t)acc;
-        acc >>= 32;
-    }
-}
-
 __device__ inline int big_getbit(const uint32_t* big, int p) { return (big[p >> 5] >> (p & 31)) & 1; }
 
-// The float32 nearest to (sum over bins) / K, by exact integer arithmetic (one
-// thread).  bins[t] = {sum of hi halves, sum of lo halves}: the squares in bin t
-// add up to (hi * 2^24 + lo) * 2^(2t - 298).
-__device__ float exact_mean_f32(const unsigned long long (*bins)[2], uint32_t* big, uint64_t K) {
-    for (int i = 0; i < kLimbs; ++i) big[i] = 0;
-    for (int t = 0; t < kBins; ++t) {
-        const uint64_t hi = bins[t][0], lo = bins[t][1];
-        if (lo) big_add(big, lo, 2 * t);
-        if (hi) big_add(big, hi, 2 * t + 24);
+// Bits [32j, 32j + 32) of v * 2^s, where rel = s - 32j and v < 2^56: the low
+// 32 bits of v << rel (bits past 64 do not reach them), or of v >> -rel.
+__device__ inline uint64_t limb_piece(uint64_t v, int rel) {
+    if (rel >= 32 || rel <= -64) return 0;
+    return (rel >= 0 ? v << rel : v >> -rel) & 0xffffffffull;
+}
+
+// big = the exact sum over bins (as in exact_mean_f32), limb by limb in
+// parallel: lane j of the first wave adds the pieces of every bin value that
+// fall into limb j (at most 2 * kBins pieces below 2^32: no overflow of 64
+// bits), then one thread propagates the carries.  Called by every thread of
+// the workgroup (it synchronizes).
+__device__ void exact_limbs(const unsigned long long (*bins)[2], uint32_t* big, unsigned long long* raw, int t) {
+    if (t < kLimbs) {
+        const int j = t;
+        // lo halves sit at 2^(2b), hi halves at 2^(2b + 24); only bins with
+        // -64 < shift - 32j < 32 reach limb j.
+        const int b0 = 16 * j - 44 > 0 ? 16 * j - 44 : 0;
+        const int b1 = 16 * j + 16 < kBins ? 16 * j + 16 : kBins;
+        uint64_t acc = 0;
+        for (int b = b0; b < b1; ++b) {
+            acc += limb_piece(bins[b][1], 2 * b - 32 * j);
+            acc += limb_piece(bins[b][0], 2 * b + 24 - 32 * j);
+        }
+        raw[j] = acc;
     }
+    __syncthreads();
+    if (t == 0) {
+        uint64_t carry = 0;
+        for (int j = 0; j < kLimbs; ++j) {
+            const uint64_t a = raw[j] + carry;
+            big[j] = (uint32_t)a;
+            carry = a >> 32;
+        }
+    }
+    __syncthreads();
+}
+
+// The float32 nearest to S / K, by exact integer arithmetic (one thread), S
+// the sum over bins: bins[t] = {sum of hi halves, sum of lo halves}, the
+// squares in bin t adding up to (hi * 2^24 + lo) * 2^(2t - 298).
+__device__ float exact_mean_f32(uint32_t* big, uint64_t K) {
+    // big holds S, the exact sum over bins (exact_limbs).
     // Q = floor(S / K) limb by limb (rem < K < 2^31), in units of 2^-298.
     uint64_t rem = 0;
     for (int i = kLimbs - 1; i >= 0; --i) {
@@ -176,6 +190,7 @@ __device__ void rmsnorm_quant_row(const float* __restrict__ x, int64_t K, int8_t
     __shared__ int redi[W];
     __shared__ unsigned long long bins[kBins][2];
     __shared__ uint32_t big[kLimbs];
+    __shared__ unsigned long long raw[kLimbs];
     __shared__ float ms_sh;
     const float4* x4 = reinterpret_cast<const float4*>(x);
     uint32_t* q4 = reinterpret_cast<uint32_t*>(xq);
@@ -236,7 +251,8 @@ __device__ void rmsnorm_quant_row(const float* __restrict__ x, int64_t K, int8_t
             for (int64_t i = t; i < n4; i += THREADS) bin_square4(bins, x4[i]);
         }
         __syncthreads();
-        if (t == 0) ms_sh = exact_mean_f32(bins, big, (uint64_t)K);
+        exact_limbs(bins, big, raw, t);
+        if (t == 0) ms_sh = exact_mean_f32(big, (uint64_t)K);
         __syncthreads();
         ms = ms_sh;
     }
