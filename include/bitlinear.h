@@ -32,7 +32,8 @@
  *    has finished.
  *  - `stream` is a hipStream_t (NULL is the default stream).  Every call only
  *    queues work on it and returns, except where a call says it synchronizes.
- *  - K must be a multiple of 16.  M may be 0 (nothing is queued).  N, K >= 1.
+ *  - K must be a multiple of 16 and at most BITLINEAR_MAX_K.  M may be 0
+ *    (nothing is queued).  N, K >= 1.
  *  - Inputs must be finite; NaN or Inf give unspecified (but bounded) output.
  *  - Arguments are validated before anything is queued: on a non-zero return
  *    nothing has been written.
@@ -61,7 +62,15 @@ extern "C" {
 /* Status codes returned by every int-valued call. */
 #define BITLINEAR_OK 0
 #define BITLINEAR_EINVAL (-1)       /* null pointer, negative or zero size, bad count */
-#define BITLINEAR_EUNSUPPORTED (-2) /* K not a multiple of 16, or a size beyond 2^31 */
+#define BITLINEAR_EUNSUPPORTED (-2) /* K not a multiple of 16, K above BITLINEAR_MAX_K,
+                                       or another size beyond 2^31 */
+
+/* Longest reduction (input features K) any call accepts.  Every kernel keeps
+ * its int32 partial sums and 32-bit operand offsets exact up to this K (the
+ * dot4 decode path keeps one code field scaled by 16: |sum| <= 1016 K < 2^31;
+ * a 128-row prefill tile spans 128 K < 2^32 activation bytes); the int32
+ * result itself needs only 127 K < 2^31. */
+#define BITLINEAR_MAX_K (1 << 21)
 #define BITLINEAR_EWORKSPACE (-3)   /* workspace missing or smaller than required */
 #define BITLINEAR_EBADCODE (-4)     /* a ternary input outside {-1, 0, 1} */
 #define BITLINEAR_EHIP (-5)         /* a HIP runtime call or kernel launch failed */
@@ -141,9 +150,8 @@ int bitlinear_pack_weights(const float* W, int64_t N, int64_t K, uint8_t* packed
 
 /*
  * Absmedian variant of bitlinear_pack_weights: gamma is the median of |W| in
- * place of the mean.  [P2] the paragraph after "Real-World Production
- * Benchmarks" (BitNet b1.58 Reloaded's absmedian baseline).  For an even
- * count N*K the median is the mean of the two middle magnitudes, rounded once
+ * place of the mean.  [P2] "Scaling Laws and Empirical Benchmarks" (BitNet
+ * b1.58 Reloaded's absmedian baseline).  For an even count N*K the median is the mean of the two middle magnitudes, rounded once
  * to the nearest float32 (ties to even); it is clamped below at 1e-5 and the
  * ternarization and 2-bit layout are those of bitlinear_pack_weights.  Same
  * arguments; ws of bitlinear_workspace_bytes(0, N, K) bytes.
@@ -312,9 +320,10 @@ typedef struct bitlinear_grouped_plan {
 } bitlinear_grouped_plan;
 
 /* Device bytes the work table for these problems needs (host only).  Plans
- * past 4 tokens whose 256-row blocks would leave CUs idle (a single
- * transformer block, say) may split their K loops, and the table then also
- * holds the int32 partial sums (M x 256 x 4 bytes per work unit). */
+ * whose work units would leave CUs idle (a single transformer block, say) may
+ * split their K loops, and the table then also holds the int32 partial sums:
+ * M x 64 x 4 bytes per work unit of the dot4 decode path (up to 4 tokens),
+ * M x 256 x 4 bytes per unit past 4 tokens. */
 size_t bitlinear_grouped_table_bytes(const bitlinear_problem* problems_host, int32_t count,
                                      int64_t M);
 

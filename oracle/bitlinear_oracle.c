@@ -137,8 +137,8 @@ static float big_ratio_to_f32(const or_big* S, int unit, uint64_t D) {
  *
  * Every finite float32 magnitude is sig * 2^(t - 149) with an integer sig <
  * 2^24 and 0 <= t <= 253, so the sum of all |W| is an exact integer count of
- * 2^-149 units.  The mean S / (N*K) is then rounded to float32 by plain long
- * division, bit by bit.
+ * 2^-149 units.  The mean S / (N*K) is then rounded to float32 by the exact
+ * ratio rounding above.
  */
 int oracle_absmean_gamma(const float* W, int64_t N, int64_t K, float* gamma_out) {
     if (!W || !gamma_out || N <= 0 || K <= 0) return -1;
@@ -156,38 +156,9 @@ int oracle_absmean_gamma(const float* W, int64_t N, int64_t K, float* gamma_out)
         int t = e ? (int)e - 1 : 0;      /* |w| = sig * 2^(t-149) */
         if (sig) big_add_shifted(&S, sig, t);
     }
-    /* Long division S / D, producing quotient bits from the top. */
-    int L = big_bitlen(&S);
-    /* quotient bits q_i for bit positions i = L-1 .. -(guard) relative to the
-       2^-149 unit; keep the first 26 significant ones and a sticky flag */
-    uint64_t rem = 0;                    /* rem < D < 2^40 at all times */
-    uint32_t q = 0;                      /* significant quotient bits so far */
-    int nsig = 0, qexp = 0, sticky = 0;  /* qexp: position of the last kept bit */
-    for (int pos = L - 1; pos >= -200; --pos) {
-        rem = (rem << 1) | (uint64_t)big_bit(&S, pos);
-        int qb = 0;
-        if (rem >= D) { rem -= D; qb = 1; }
-        if (nsig == 0 && !qb) continue;  /* leading zeros of the quotient */
-        if (nsig < 26) { q = (q << 1) | (uint32_t)qb; ++nsig; qexp = pos; }
-        else if (qb) sticky = 1;
-        if (nsig == 26 && pos < -160) break;
-    }
-    if (rem) sticky = 1;
-    float g;
-    if (nsig == 0) {
-        g = 0.0f;
-    } else {
-        /* normalise to exactly 26 bits: q = 24-bit significand, round, sticky */
-        while (nsig < 26) { q <<= 1; ++nsig; --qexp; }
-        uint32_t sig = q >> 2, rb = (q >> 1) & 1u, lb = q & 1u;
-        int exp2 = qexp + 2;             /* value = sig * 2^(exp2 - 149) */
-        if (rb && (lb || sticky || (sig & 1u))) ++sig;
-        if (sig == (1u << 24)) { sig >>= 1; ++exp2; }
-        /* value = sig * 2^(exp2-149); means below 2^-126 are under the clamp */
-        double v = ldexp((double)sig, exp2 - 149);
-        g = (float)v; /* exact: sig has 24 bits and the exponent is in range */
-        if (exp2 - 149 + 23 < -126) g = 0.0f; /* subnormal means: clamp below */
-    }
+    /* S * 2^-149 / D, rounded once to the nearest float32 (ties to even);
+       a subnormal or zero mean falls under the clamp below. */
+    float g = big_ratio_to_f32(&S, -149, D);
     if (g < OR_SCALE_FLOOR) g = OR_SCALE_FLOOR;
     *gamma_out = g;
     return 0;
@@ -195,7 +166,7 @@ int oracle_absmean_gamma(const float* W, int64_t N, int64_t K, float* gamma_out)
 
 /*
  * Absmedian weight scale: the median of |W| over the whole matrix in place of
- * the mean.  [P2] the paragraph after "Real-World Production Benchmarks"
+ * the mean.  [P2] "Scaling Laws and Empirical Benchmarks"
  * (BitNet b1.58 Reloaded: adjusting the quantization baseline to the median,
  * "Absmedian", rather than the mean).  Readings: the median of the N*K
  * magnitudes; for an even count it is the mean of the two middle ones, that

@@ -35,6 +35,7 @@ BITLINEAR_EUNSUPPORTED = -2
 BITLINEAR_EWORKSPACE = -3
 BITLINEAR_EBADCODE = -4
 BITLINEAR_EHIP = -5
+BITLINEAR_MAX_K = 1 << 21
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64

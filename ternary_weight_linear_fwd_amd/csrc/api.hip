@@ -37,10 +37,11 @@ constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Shared size rules: N, K in [1, 2^31), K % 16 == 0, N*K < 2^40, M in [0, 2^31).
+// Shared size rules: N in [1, 2^31), K in [1, BITLINEAR_MAX_K], K % 16 == 0,
+// N*K < 2^40, M in [0, 2^31).
 int check_sizes(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N <= 0 || K <= 0) return BITLINEAR_EINVAL;
-    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return BITLINEAR_EUNSUPPORTED;
+    if (M > kMaxDim || N > kMaxDim || K > BITLINEAR_MAX_K) return BITLINEAR_EUNSUPPORTED;
     if (K % 16 != 0) return BITLINEAR_EUNSUPPORTED;
     if (N * K >= (int64_t(1) << 40)) return BITLINEAR_EUNSUPPORTED;
     if (M * K >= (int64_t(1) << 40) || M * N >= (int64_t(1) << 40)) return BITLINEAR_EUNSUPPORTED;

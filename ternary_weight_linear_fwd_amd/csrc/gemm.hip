@@ -110,7 +110,7 @@ struct PrefillCtx {
     static constexpr int ops(bool act) { return NA + (act ? NT : 0); }
     // DMA sources are a wave-uniform base (scalar registers) plus a 32-bit
     // per-lane offset, so that the main loop spends no vector ALU work on
-    // addresses (row offsets stay below 2^32 since K <= 2^24).
+    // addresses (row offsets stay below 2^32: 128 rows x K <= 2^21).
     const int8_t* abase;    // the tile's first activation row
     uint32_t aoff[NA];      // (row in the tile, clamped below M) * K + byte column
     uint32_t acol[NA];      // byte column inside the 128-k step

@@ -1,6 +1,6 @@
 // median.hip -- the absmedian weight scale on gfx950.
 //
-// [P2] the paragraph after "Real-World Production Benchmarks" (BitNet b1.58
+// [P2] "Scaling Laws and Empirical Benchmarks" (BitNet b1.58
 // Reloaded: the quantization baseline adjusted to the median, "Absmedian",
 // rather than the mean).  gamma = median of |W| over the matrix; for an even
 // count the mean of the two middle magnitudes, rounded once to float32;

@@ -416,6 +416,44 @@ def pin_dequant(O):
                      f32(1.0)).tolist() == [[5.0, -9.0]]
 
 
+def _signed_nearest_f32(fr: Fraction) -> np.float32:
+    if fr == 0:
+        return f32(0.0)
+    v = nearest_f32(abs(fr))
+    return v if fr > 0 else -v
+
+
+def pin_dequant_association(O):
+    # The scale is (eta * gamma) / 127 in this order, each step rounded to
+    # float32 (BitLinear158.forward step 5 of the first page's production
+    # listing; the fifth page's bitlinear_forward listing).  Pairs are chosen
+    # where the other two associations, eta * (gamma / 127) and
+    # gamma * (eta / 127), give three different float32 scales; the expected
+    # bits come from exact rational arithmetic, rounded once per step.
+    qb = int(page_constants()["qb"][0][0])
+    rng = np.random.default_rng(2024)
+    etas, gammas = [], []
+    for _ in range(40000):
+        eta = f32(rng.uniform(0.5, 40.0))
+        g = f32(rng.uniform(0.005, 0.05))
+        a = f32(f32(eta * g) / f32(qb))
+        b = f32(eta * f32(g / f32(qb)))
+        c = f32(g * f32(eta / f32(qb)))
+        if len({float(a), float(b), float(c)}) == 3:
+            etas.append(eta)
+            gammas.append(g)
+        if len(etas) == 8:
+            break
+    assert len(etas) == 8
+    y_int = np.array([1, -1, 7, 1 << 20, -3_641_344, 2_000_001], np.int32)
+    for eta, g in zip(etas, gammas):
+        eg = nearest_f32(Fraction(float(eta)) * Fraction(float(g)))
+        s = nearest_f32(Fraction(float(eg)) / qb)
+        want = [_signed_nearest_f32(int(v) * Fraction(float(s))) for v in y_int]
+        got = O.dequant(y_int[None, :], np.array([eta], np.float32), g)[0]
+        assert got.tolist() == [float(w) for w in want], (eta, g, got, want)
+
+
 def pin_chain_hand(O):
     # W = [1,-1,0,1,-1,1,1,-1]: gamma = 7/8; W/gamma = +-8/7 or 0 -> W~ = W
     W = np.array([[1, -1, 0, 1, -1, 1, 1, -1]], np.float32)

@@ -156,6 +156,33 @@ def test_validation_before_any_device_work():
     assert _rc("bitlinear_forward_rmsnorm_f32", FAKE, None, ctypes.c_float(1.0), 4, 64, 64, FAKE, FAKE, 1 << 20, None) == L.BITLINEAR_EINVAL
 
 
+def test_k_limit():
+    """K above BITLINEAR_MAX_K (2^21) is refused by every call before any device
+    work: past it the dot4 path's scaled field sums and the prefill tiles'
+    32-bit operand offsets would wrap."""
+    L = bl
+    big = L.BITLINEAR_MAX_K + 16
+    assert L.bitlinear_packed_bytes(64, L.BITLINEAR_MAX_K) > 0
+    assert L.bitlinear_packed_bytes(64, big) == 0
+    assert L.bitlinear_workspace_bytes(1, 64, big) == 0
+    assert L.bitlinear_packed3_bytes(64, big) == 0
+    assert L.bitlinear_lut_workspace_bytes(1, 64, big, 0) == 0
+    f1 = ctypes.c_float(1.0)
+    assert _rc("bitlinear_quantize_act", FAKE, 1, big, FAKE, FAKE, None, None) == L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, f1, 1, 64, big, FAKE, None, FAKE, 1 << 30, None) == \
+        L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_forward_xsum", FAKE, FAKE, FAKE, FAKE, f1, 128, 64, big, FAKE, None, FAKE, 1 << 30,
+               None) == L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_forward_f32", FAKE, FAKE, f1, 4, 64, big, FAKE, FAKE, 1 << 30, None) == \
+        L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_pack_weights", FAKE, 64, big, FAKE, None, None, FAKE, 1 << 20, None) == \
+        L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_forward_lut", FAKE, FAKE, FAKE, 0, f1, 1, 64, big, FAKE, None, FAKE, 1 << 30, None) == \
+        L.BITLINEAR_EUNSUPPORTED
+    specs = [dict(x=None, xq=FAKE, eta=FAKE + 256, packed=FAKE, y=FAKE, gamma=0.5, N=128, K=big)]
+    assert bl.bitlinear_grouped_table_bytes(bl.make_problems(specs), 1, 1) == 0
+
+
 def test_grouped_planner_validation():
     def probs(n, **over):
         specs = []

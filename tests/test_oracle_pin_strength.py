@@ -26,8 +26,9 @@ MUTANTS = {
     "gamma_divides_by_rows": ("const uint64_t D = (uint64_t)N * (uint64_t)K;",
                               "const uint64_t D = (uint64_t)N;"),
     "gamma_exponent_off_by_one": ("int t = e ? (int)e - 1 : 0;", "int t = e ? (int)e : 0;"),
-    "gamma_no_sticky": ("else if (qb) sticky = 1;", "else if (qb) sticky = 0;"),
-    "gamma_truncates": ("if (rb && (lb || sticky || (sig & 1u))) ++sig;", ""),
+    "gamma_unit_off_by_one": ("float g = big_ratio_to_f32(&S, -149, D);", "float g = big_ratio_to_f32(&S, -148, D);"),
+    "gamma_divides_by_one_less": ("float g = big_ratio_to_f32(&S, -149, D);",
+                                  "float g = big_ratio_to_f32(&S, -149, D > 1 ? D - 1 : 1);"),
     "gamma_no_floor": ("if (g < OR_SCALE_FLOOR) g = OR_SCALE_FLOOR;", ""),
     "ternary_round_half_away": ("float r = nearbyintf(t);", "float r = roundf(t);"),
     "ternary_no_clip": ("if (r > 1.0f) r = 1.0f;", ""),
@@ -88,6 +89,10 @@ MUTANTS = {
     # dequant
     "dequant_drops_gamma": ("float eg = eta[m] * gamma;", "float eg = eta[m];"),
     "dequant_divides_by_128": ("float s = eg / OR_QB;", "float s = eg / 128.0f;"),
+    "dequant_reciprocal_association": ("float s = eg / OR_QB;        /* ... / 127.0 */",
+                                       "float s = eta[m] * (gamma / OR_QB);"),
+    "dequant_eta_over_127_first": ("float s = eg / OR_QB;        /* ... / 127.0 */",
+                                   "float s = (eta[m] / OR_QB) * gamma;"),
 }
 
 
