@@ -78,6 +78,37 @@ def time_events(torch, fn, reps: int) -> float:
     return start.elapsed_time(end) / reps
 
 
+def time_graph(torch, call, count: int, replays: int = 10) -> float:
+    """Mean milliseconds per call of call(i, stream) for i = 0 .. count - 1,
+    captured once into a HIP graph (on a side stream of default priority)
+    and replayed: the device time of the sequence without the host's
+    per-call issue cost (Python and ctypes take several microseconds per
+    call, more than a single-layer decode kernel runs)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(count):          # eager pass: first-touch work outside the capture
+            call(i, side.cuda_stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(count):
+            call(i, side.cuda_stream)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(cur)
+    for _ in range(replays):
+        graph.replay()
+    end.record(cur)
+    end.synchronize()
+    ms = start.elapsed_time(end) / (replays * count)
+    del graph
+    return ms
+
+
 def contraction_only_plan(sw, M):
     """A plan over the same problems whose activations are already quantized
     (x = NULL): forward then launches the contraction kernel alone."""
@@ -150,6 +181,9 @@ def bench_prefill(torch, L, S, reps: int):
     return out, mfma_ceiling
 
 
+COLD_BYTES = 1_200_000_000   # distinct data cycled through for cold timings (> 4x the 256 MB MALL)
+
+
 def bench_block(torch, L, S, reps: int, which: int):
     """One transformer block's seven projections from float32 activations to
     float32 outputs, (a) as one grouped forward (quantize + contraction, and
@@ -157,7 +191,12 @@ def bench_block(torch, L, S, reps: int, which: int):
     bitlinear_forward_f32 calls.  which = 5: batched decode with skewed
     sparsity (hidden 4096, FFN 11008; ternary weights drawn directly,
     P(0) = 0.6; 1% outlier channels), M = 32, 64, 128.  which = 2: the
-    3B-shaped block (hidden 3200, FFN 8640; latent N(0, 0.02) weights), M = 1, 8."""
+    3B-shaped block (hidden 3200, FFN 8640; latent N(0, 0.02) weights), M = 1, 8.
+
+    Cold: the block is copied (packed weights, activations, outputs, plan)
+    until the copies hold COLD_BYTES, and consecutive calls cycle through the
+    copies, so every call reads its weights from HBM.  Hot: one copy, called
+    repeatedly, stays in the caches (the block is smaller than the MALL)."""
     import ctypes
     st = torch.cuda.current_stream().cuda_stream
     projs = S.C5_PROJS if which == 5 else S.C2_PROJS
@@ -178,47 +217,151 @@ def bench_block(torch, L, S, reps: int, which: int):
         packed.append(buf)
         gammas.append(float(g))
     wbytes = sum(int(L.bitlinear_packed_bytes(p.N, p.K)) for p in projs)
+    ncopies = -(-COLD_BYTES // wbytes)
+    copies = [packed] + [[b.clone() for b in packed] for _ in range(ncopies - 1)]
     out = []
     for M in ((32, 64, 128) if which == 5 else (1, 8)):
-        xs = [torch.from_numpy(S.c5_x(p, M) if which == 5 else S.c2_x(p, M)).cuda() for p in projs]
-        ys = [torch.empty((M, p.N), dtype=torch.float32, device="cuda") for p in projs]
-        xqs = [torch.empty((M, p.K), dtype=torch.int8, device="cuda") for p in projs]
-        etas = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in projs]
-        specs = [dict(x=x, xq=xq, eta=eta, packed=w, y=y, y_int=None, gamma=g, N=p.N, K=p.K)
-                 for p, x, xq, eta, w, y, g in zip(projs, xs, xqs, etas, packed, ys, gammas)]
-        probs = L.make_problems(specs)
-        tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
-        table = torch.empty(tb, dtype=torch.uint8, device="cuda")
-        plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
+        xs0 = [torch.from_numpy(S.c5_x(p, M) if which == 5 else S.c2_x(p, M)).cuda() for p in projs]
+        plans, keep, singles_calls = [], [], []
+        for c, wts in enumerate(copies):
+            xs = xs0 if c == 0 else [x.clone() for x in xs0]
+            ys = [torch.empty((M, p.N), dtype=torch.float32, device="cuda") for p in projs]
+            xqs = [torch.empty((M, p.K), dtype=torch.int8, device="cuda") for p in projs]
+            etas = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in projs]
+            specs = [dict(x=x, xq=xq, eta=eta, packed=w, y=y, y_int=None, gamma=g, N=p.N, K=p.K)
+                     for p, x, xq, eta, w, y, g in zip(projs, xs, xqs, etas, wts, ys, gammas)]
+            probs = L.make_problems(specs)
+            tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
+            table = torch.empty(tb, dtype=torch.uint8, device="cuda")
+            plans.append(L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb))
+            keep.append((xs, ys, xqs, etas, table))
+            # Raw addresses resolved once, outside the timed loops.
+            singles_calls.append([(x.data_ptr(), w.data_ptr(), g, p.N, p.K, y.data_ptr())
+                                  for p, x, w, y, g in zip(projs, xs, wts, ys, gammas)])
         wsb = max(L.bitlinear_workspace_bytes(M, p.N, p.K) for p in projs)
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-        # Raw addresses resolved once, outside the timed loops.
-        calls = [(x.data_ptr(), w.data_ptr(), g, p.N, p.K, y.data_ptr())
-                 for p, x, w, y, g in zip(projs, xs, packed, ys, gammas)]
         wsp = ws.data_ptr()
+        fwd = L._lib.bitlinear_forward_grouped
+        plan_refs = [ctypes.byref(pl) for pl in plans]
+        f32 = L._lib.bitlinear_forward_f32
 
-        def singles():
+        def singles(calls):
             for xa, wa, g, N, K, ya in calls:
-                L.bitlinear_forward_f32(xa, wa, g, M, N, K, ya, wsp, wsb, st)
-        grouped = lambda: L.bitlinear_forward_grouped(plan)
+                f32(xa, wa, g, M, N, K, ya, wsp, wsb, st)
+        rot = {"i": 0}
+
+        def grouped_cold():
+            i = rot["i"]
+            fwd(plan_refs[i], st)
+            rot["i"] = (i + 1) % len(plans)
+
+        def singles_cold():
+            i = rot["i"]
+            singles(singles_calls[i])
+            rot["i"] = (i + 1) % len(plans)
+        grouped_hot = lambda: fwd(plan_refs[0], st)
+        singles_hot = lambda: singles(singles_calls[0])
         t_end = time.perf_counter() + 0.2
         while time.perf_counter() < t_end:
-            grouped()
-            singles()
+            grouped_hot()
+            singles_hot()
             torch.cuda.synchronize()
-        g_ms = time_events(torch, grouped, reps)
-        s_ms = time_events(torch, singles, reps)
+        # Issued call by call from Python (host issue cost included) ...
+        g_hot_eager = time_events(torch, grouped_hot, reps)
+        s_hot = time_events(torch, singles_hot, reps)
+        cold_reps = max(reps, 2 * len(plans))
+        for _ in range(len(plans)):
+            grouped_cold()
+        g_cold_eager = time_events(torch, grouped_cold, cold_reps)
+        s_cold = time_events(torch, singles_cold, cold_reps)
+        # ... and as the device runs them, replayed from a HIP graph: hot = one
+        # copy 50 times, cold = each copy once in turn.
+        g_hot = time_graph(torch, lambda i, s: fwd(plan_refs[0], s), 50)
+        g_cold = time_graph(torch, lambda i, s: fwd(plan_refs[i], s), len(plans))
         ops = 2 * M * sum(p.N * p.K for p in projs)
-        best = min(g_ms, s_ms)
-        out.append({"M": M, "grouped_us": round(g_ms * 1e3, 2), "single_calls_us": round(s_ms * 1e3, 2),
-                    "weight_gbs": round(wbytes / (best * 1e-3) / 1e9, 1),
-                    "tops": round(ops / (best * 1e-3) / 1e12, 1)})
-        del xs, ys, xqs, etas, table, ws
+        fbytes = wbytes + sum(4 * M * p.K + 4 * M * p.N for p in projs)
+        floor_us = max(fbytes / HBM_PEAK_GBS / 1e3, ops / INT8_PEAK_TOPS / 1e6)
+        out.append({"M": M, "grouped_us_cold": round(g_cold * 1e3, 2), "grouped_us_hot": round(g_hot * 1e3, 2),
+                    "grouped_us_cold_eager": round(g_cold_eager * 1e3, 2),
+                    "grouped_us_hot_eager": round(g_hot_eager * 1e3, 2),
+                    "single_calls_us_cold_eager": round(s_cold * 1e3, 2),
+                    "single_calls_us_hot_eager": round(s_hot * 1e3, 2),
+                    "algorithmic_bytes": fbytes, "roofline_floor_us": round(floor_us, 2),
+                    "frac_of_roofline_cold": round(floor_us / (g_cold * 1e3), 4),
+                    "weight_gbs_cold": round(wbytes / (g_cold * 1e-3) / 1e9, 1),
+                    "tops_cold": round(ops / (g_cold * 1e-3) / 1e12, 1)})
+        del keep, plans, ws
     workload = ("hidden 4096, FFN 11008 block (q,k,v,o 4096->4096; gate,up 4096->11008; down 11008->4096), "
                 "ternary P(0)=0.6, 1% outlier channels x20, float32 in/out") if which == 5 else \
                ("hidden 3200, FFN 8640 block (q,k,v,o 3200->3200; gate,up 3200->8640; down 8640->3200), "
                 "latent N(0,0.02) weights, x ~ N(0,1), float32 in/out")
-    return {"workload": workload, "packed_weight_bytes": wbytes, "per_M": out}
+    return {"workload": workload, "packed_weight_bytes": wbytes, "cold_copies": ncopies,
+            "cold": f"{ncopies} copies of the block ({ncopies * wbytes / 1e9:.2f} GB of weights) cycled, "
+                    "one copy per call; hot: one copy called repeatedly",
+            "timing": "grouped_us_*: device time per call, the calls replayed from one HIP graph; *_eager: "
+                      "issued call by call from Python (host issue cost included)", "per_M": out}
+
+
+def bench_c1(torch, L, S, reps: int):
+    """The single 2048 x 2048 layer at M = 1 (seed 0): the contraction with
+    its dequant (bitlinear_forward on x~), the quantizer, and the fused
+    forward from float32, each hot (one weight copy) and cold (COLD_BYTES of
+    weight copies cycled).  Algorithmic bytes: packed weights + x~ + eta + y
+    (the fused forward reads float32 x instead of x~)."""
+    import ctypes
+    W, x = S.c1_inputs()
+    M, K = x.shape
+    N = W.shape[0]
+    st = torch.cuda.current_stream().cuda_stream
+    wsb = L.bitlinear_workspace_bytes(M, N, K)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    packed = torch.empty(L.bitlinear_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+    gh = ctypes.c_float()
+    L.bitlinear_pack_weights(torch.from_numpy(W).cuda(), N, K, packed, None, gh, ws, wsb)
+    g = gh.value
+    xd = torch.from_numpy(x).cuda()
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    eta = torch.empty(M, dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    L.bitlinear_quantize_act(xd, M, K, xq, eta)
+    ncopies = -(-COLD_BYTES // packed.numel())
+    copies = [packed] + [packed.clone() for _ in range(ncopies - 1)]
+    wp = [c.data_ptr() for c in copies]
+    a = [t.data_ptr() for t in (xd, xq, eta, y, ws)]
+    fwd, q, f32 = L._lib.bitlinear_forward, L._lib.bitlinear_quantize_act, L._lib.bitlinear_forward_f32
+    rot = {"i": 0}
+
+    def nxt():
+        i = rot["i"]
+        rot["i"] = (i + 1) % ncopies
+        return wp[i]
+    runs = {
+        "forward": (lambda w, s: fwd(a[1], a[2], w, g, M, N, K, a[3], None, a[4], wsb, s),
+                    N * K // 4 + M * K + 4 * M + 4 * M * N),
+        "fused_f32": (lambda w, s: f32(a[0], w, g, M, N, K, a[3], a[4], wsb, s),
+                      N * K // 4 + 4 * M * K + 4 * M + 4 * M * N),
+    }
+    out = {"layer": f"M={M} K={K} N={N}", "cold": f"{ncopies} weight copies "
+           f"({ncopies * packed.numel() / 1e9:.2f} GB) cycled, one per call"}
+    for name, (fn, nbytes) in runs.items():
+        for _ in range(200):
+            fn(wp[0], st)
+        hot_eager = time_events(torch, lambda: fn(wp[0], st), max(reps, 200))
+        for _ in range(ncopies):
+            fn(nxt(), st)
+        cold_eager = time_events(torch, lambda: fn(nxt(), st), max(reps, 2 * ncopies))
+        hot = time_graph(torch, lambda i, s: fn(wp[0], s), 200)
+        cold = time_graph(torch, lambda i, s: fn(wp[i], s), ncopies, replays=3)
+        out[name] = {"us_hot": round(hot * 1e3, 2), "us_cold": round(cold * 1e3, 2),
+                     "gbs_hot": round(nbytes / (hot * 1e-3) / 1e9, 1),
+                     "gbs_cold": round(nbytes / (cold * 1e-3) / 1e9, 1), "algorithmic_bytes": nbytes,
+                     "us_hot_eager": round(hot_eager * 1e3, 2), "us_cold_eager": round(cold_eager * 1e3, 2)}
+    qt = time_graph(torch, lambda i, s: q(a[0], M, K, a[1], a[2], None, s), 200)
+    out["quantize_us_hot"] = round(qt * 1e3, 2)
+    out["timing"] = ("us_*: device time per call, the calls replayed from one HIP graph; *_eager: issued call "
+                     "by call from Python (host issue cost included)")
+    del copies, ws
+    return out
 
 
 def bench_mfma_ceiling(torch, L, xq, packed) -> dict:
@@ -356,10 +499,14 @@ def bench_pack(torch, L, reps: int):
     return out
 
 
-def cpu_baseline(sw, S, budget_s: float = 12.0):
-    """The oracle (unchanged) on a bounded sample of the sweep: layer 0's seven
-    projections at M = 1 (quantize + contract + dequant), run repeatedly until
-    about budget_s seconds of CPU time have been timed."""
+def cpu_baseline(sw, S, budget_s: float = 8.0):
+    """The oracle (unchanged) on bounded samples of the workloads, timed on
+    this host's cores: (a) layer 0's seven projections of the 70B-shaped
+    sweep at M = 1 (quantize + contract + dequant) on all host threads, run
+    repeatedly for about budget_s seconds -- the reported value; (b) the same
+    on one thread over layer 0's q and k projections; (c) the 3B prefill GEMM
+    3200 -> 8640 on a sample of its 2048 Student-t token rows (quantize +
+    contract + dequant), on all threads and on one."""
     import oracle
     threads = len(os.sched_getaffinity(0))
     O = oracle.default()
@@ -370,20 +517,45 @@ def cpu_baseline(sw, S, budget_s: float = 12.0):
         del W
         prepared.append((sw.x[(0, p.name, 1)].cpu().numpy(), Wt, g, p))
         log(f"cpu oracle: prepared layer 0 {p.name}")
-    layer_bytes = sum(p.N * p.K // 4 + 4 * p.K + 4 * p.N + 4 for *_, p in prepared)
-    t_total, passes = 0.0, 0
-    while t_total < budget_s and passes < 200:
+
+    def timed(items, nthreads, budget, what):
+        nbytes = sum(p.N * p.K // 4 + 4 * p.K + 4 * p.N + 4 for *_, p in items)
+        t_total, passes = 0.0, 0
+        while t_total < budget and passes < 200:
+            t0 = time.perf_counter()
+            for x, Wt, g, p in items:
+                O.forward(x, Wt, g, threads=nthreads)
+            t_total += time.perf_counter() - t0
+            passes += 1
+        log(f"cpu oracle ({what}, {nthreads} threads): {passes} passes, {t_total:.1f} s")
+        return nbytes, passes, t_total
+
+    nb, passes, t_all = timed(prepared, threads, budget_s, "layer 0")
+    value = nb * passes / t_all / 1e9
+    qk = [it for it in prepared if it[3].name in ("q", "k")]
+    nb1, passes1, t_one = timed(qk, 1, budget_s / 2, "layer 0 q, k")
+    single = {"value": round(nb1 * passes1 / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+              "sample": f"layer 0 q and k projections ({nb1 / 1e6:.1f} MB of packed weights) at M=1, "
+                        f"{passes1} passes, {t_one:.1f} s timed"}
+
+    W, x = S.c3_inputs(0)
+    Wt, g = O.quantize_weights(W)
+    del W
+    prefill = {}
+    for nthreads, rows in ((threads, 64), (1, 4)):
         t0 = time.perf_counter()
-        for x, Wt, g, p in prepared:
-            O.forward(x, Wt, g, threads=threads)
-        t_total += time.perf_counter() - t0
-        passes += 1
-        log(f"cpu oracle: pass {passes}, {t_total:.1f} s")
-    return {"value": round(layer_bytes * passes / t_total / 1e9, 3), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"layer 0 of the 70B-shaped sweep (7 projections, {layer_bytes / 1e6:.1f} MB "
+        O.forward(x[:rows], Wt, g, threads=nthreads)
+        t = time.perf_counter() - t0
+        ops = 2 * rows * Wt.shape[0] * Wt.shape[1]
+        key = "all_threads" if nthreads == threads else "single_thread"
+        prefill[key] = {"value": round(ops / t / 1e12, 6), "unit": "TOP/s", "cores": nthreads,
+                        "sample": f"{rows} of the 2048 token rows of the 3200->8640 prefill GEMM, {t:.2f} s"}
+        log(f"cpu oracle prefill ({nthreads} threads, {rows} rows): {t:.2f} s")
+    return {"value": round(value, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer 0 of the 70B-shaped sweep (7 projections, {nb / 1e6:.1f} MB "
                       f"of packed weights) at M=1, quantize+contract+dequant, {passes} passes, "
-                      f"{t_total:.1f} s timed"}
+                      f"{t_all:.1f} s timed",
+            "single_thread": single, "prefill_c3": prefill}
 
 
 COPY_BYTES = 1 << 30
@@ -519,8 +691,8 @@ def main() -> int:
     if args.profile_blocks:
         for which in (2, 5):
             for r in bench_block(torch, L, S, max(1, args.steps), which)["per_M"]:
-                log(f"C{which} block M={r['M']}: grouped {r['grouped_us']} us, seven single calls "
-                    f"{r['single_calls_us']} us")
+                log(f"C{which} block M={r['M']}: grouped {r['grouped_us_cold']} us cold / "
+                    f"{r['grouped_us_hot']} us hot")
         return 0
     if args.profile_prefill:
         for r in bench_prefill(torch, L, S, max(1, args.steps))[0]:
@@ -585,11 +757,16 @@ def main() -> int:
         extra["prefill"] = prefill
 
     if not args.no_prefill:
+        extra["single_layer_c1"] = bench_c1(torch, L, S, max(10, args.steps))
+        c1 = extra["single_layer_c1"]
+        log(f"C1 forward: {c1['forward']['us_cold']} us cold, {c1['forward']['us_hot']} us hot; fused "
+            f"{c1['fused_f32']['us_cold']} / {c1['fused_f32']['us_hot']} us; quantize {c1['quantize_us_hot']} us")
         for which, key in ((2, "block_decode_c2"), (5, "batched_decode_c5")):
             extra[key] = bench_block(torch, L, S, max(10, args.steps), which)
             for r in extra[key]["per_M"]:
-                log(f"C{which} block M={r['M']}: grouped {r['grouped_us']} us, seven single calls "
-                    f"{r['single_calls_us']} us ({r['weight_gbs']} GB/s of weights, {r['tops']} TOP/s)")
+                log(f"C{which} block M={r['M']}: grouped {r['grouped_us_cold']} us cold / {r['grouped_us_hot']} "
+                    f"hot, seven single calls {r['single_calls_us_cold']} / {r['single_calls_us_hot']} us "
+                    f"(floor {r['roofline_floor_us']} us, {r['frac_of_roofline_cold']:.1%} cold)")
 
     if not args.no_prefill:
         extra["rmsnorm_quant"] = bench_rmsnorm(torch, L, S, max(10, args.steps))
@@ -613,7 +790,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the sweep")
         cpu = cpu_baseline(sw, S)
-        log(f"cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads")
+        log(f"cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads, "
+            f"{cpu['single_thread']['value']} GB/s on one")
 
     line = {
         "metric": METRIC,

@@ -53,7 +53,8 @@ def test_grouped_block_matches_oracle(M):
             assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
 
 
-SAMPLES = [(0, "q"), (17, "k"), (33, "v"), (42, "gate"), (63, "o"), (79, "down")]
+# One matrix from every band of ten layers, every projection kind at least once.
+SAMPLES = [(0, "q"), (17, "k"), (25, "up"), (33, "v"), (42, "gate"), (56, "up"), (63, "o"), (79, "down")]
 
 
 @pytest.mark.timeout(900)
