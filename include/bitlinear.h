@@ -235,6 +235,25 @@ int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, in
                           void* stream);
 
 /*
+ * Allocation-free bitlinear_forward_f32, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same kernels and the same result bits as
+ * bitlinear_forward_f32; its workspace is a fixed device array inside the
+ * library, BITLINEAR_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library
+ * runs on holds until the process ends.  The first call on a device looks up
+ * that array's address with the device current; no call allocates.
+ *   x, packed, gamma, M, N, K, y, stream as bitlinear_forward_f32.
+ * Returns BITLINEAR_EWORKSPACE, before anything is queued, for sizes whose
+ * bitlinear_workspace_bytes(M, N, K) exceeds the array.  Every call on one GPU
+ * shares the array: calls whose execution overlaps on one GPU (several
+ * streams, several host threads) race and give undefined results, so
+ * serialize them.  Nothing in the array needs a starting value.
+ */
+#define BITLINEAR_NOALLOC_SCRATCH_BYTES (64 << 20)
+int bitlinear_forward_f32_noalloc(const float* x, const uint8_t* packed, float gamma, int64_t M,
+                                  int64_t N, int64_t K, float* y, void* stream);
+
+/*
  * Fused forward with the RMSNorm prologue: normalize and quantize (into the
  * workspace), contract, dequantize.  Same arguments and workspace as
  * bitlinear_forward_f32.  [P1] BitLinear158.forward steps 1, 2, 4 and 5.

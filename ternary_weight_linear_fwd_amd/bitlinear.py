@@ -74,6 +74,7 @@ _SIGS = {
     "bitlinear_forward_f32": ([_P, _P, _F, _I64, _I64, _I64, _P, _P, _SZ, _P], ctypes.c_int),
     "bitlinear_forward_rmsnorm_f32": ([_P, _P, _F, _I64, _I64, _I64, _P, _P, _SZ, _P],
                                       ctypes.c_int),
+    "bitlinear_forward_f32_noalloc": ([_P, _P, _F, _I64, _I64, _I64, _P, _P], ctypes.c_int),
     "bitlinear_packed3_bytes": ([_I64, _I64], _SZ),
     "bitlinear_pack_weights3": ([_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "bitlinear_pack_ternary3": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
@@ -197,6 +198,16 @@ def bitlinear_forward_f32(x, packed, gamma: float, M: int, N: int, K: int, y, ws
     _check(_lib.bitlinear_forward_f32(_ptr(x), _ptr(packed), float(gamma), M, N, K, _ptr(y),
                                       _ptr(ws), ws_bytes, _stream(stream)),
            "bitlinear_forward_f32")
+
+
+BITLINEAR_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def bitlinear_forward_f32_noalloc(x, packed, gamma: float, M: int, N: int, K: int, y,
+                                  stream=None) -> None:
+    _check(_lib.bitlinear_forward_f32_noalloc(_ptr(x), _ptr(packed), float(gamma), M, N, K,
+                                              _ptr(y), _stream(stream)),
+           "bitlinear_forward_f32_noalloc")
 
 
 def bitlinear_rmsnorm_quantize_act(x, M: int, K: int, xq, eta, xsum=None, ms=None,

@@ -4,9 +4,11 @@
 // carving, kernel choice by token count and the grouped planner.  All the
 // arithmetic of the forward pass runs in the kernels of quant.hip, pack.hip,
 // gemv.hip and gemm.hip.  Nothing here allocates device memory.
+#include <atomic>
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <vector>
 
 #include "gemm.hpp"
@@ -17,6 +19,12 @@
 #include "rmsnorm.hpp"
 
 using namespace bl;
+
+// Workspace of the allocation-free fused forward: a fixed device array, one
+// copy per GPU that loads the library.  In host code its name is only a
+// stand-in, never a device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[BITLINEAR_NOALLOC_SCRATCH_BYTES];
 
 namespace bl {
 static thread_local char g_last_error[256] = "no error";
@@ -320,6 +328,35 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
     return BITLINEAR_OK;
 }
 
+// Device addresses of `scratch` (top of this file), one per device, looked up on a
+// device's first allocation-free call.
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mutex;
+
+// The device address of `scratch` on the current device, or null after a
+// failed lookup (the HIP error is recorded for bitlinear_last_error()).
+void* scratch_for_current_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+        bl::set_hip_error(e != hipSuccess ? e : hipErrorInvalidDevice, "hipGetDevice (scratch lookup)");
+        return nullptr;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+        bl::set_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        return nullptr;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -550,6 +587,24 @@ static int forward_f32_common(const float* x, const uint8_t* packed, float gamma
                  : launch_quantize(x, M, K, xq, eta, xsum, s);
     if (rc) return rc;
     return run_forward(xq, eta, xsum, packed, gamma, M, N, K, y, nullptr, rest, s);
+}
+
+int bitlinear_forward_f32_noalloc(const float* x, const uint8_t* packed, float gamma, int64_t M,
+                                  int64_t N, int64_t K, float* y, void* stream) {
+    int rc = check_sizes(M, N, K);
+    if (rc) return rc;
+    if (!x || !packed || !y) return BITLINEAR_EINVAL;
+    if (!aligned(x, 16) || !aligned(packed, 16)) return BITLINEAR_EINVAL;
+    if (f32_ws(M, N, K).bytes > (size_t)BITLINEAR_NOALLOC_SCRATCH_BYTES) return BITLINEAR_EWORKSPACE;
+    if (M == 0) return BITLINEAR_OK;
+    clear_hip_error();
+    void* ws = scratch_for_current_device();
+    if (!ws) return BITLINEAR_EHIP;
+    // Nothing in the workspace needs a starting value: x~, eta and the row
+    // sums are written by the quantizer, split-K partials by every slice
+    // before the epilogue reads them.
+    return forward_f32_common(x, packed, gamma, M, N, K, y, ws, (size_t)BITLINEAR_NOALLOC_SCRATCH_BYTES,
+                              stream, false);
 }
 
 int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, int64_t M, int64_t N,

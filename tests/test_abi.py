@@ -183,6 +183,21 @@ def test_k_limit():
     assert bl.bitlinear_grouped_table_bytes(bl.make_problems(specs), 1, 1) == 0
 
 
+def test_noalloc_validation():
+    """The allocation-free forward refuses, before any device work, sizes whose
+    workspace exceeds its fixed device array, and the usual bad arguments."""
+    L = bl
+    f1 = ctypes.c_float(1.0)
+    M, N, K = 4096, 1024, 1 << 20
+    assert L.bitlinear_workspace_bytes(M, N, K) > L.BITLINEAR_NOALLOC_SCRATCH_BYTES
+    assert _rc("bitlinear_forward_f32_noalloc", FAKE, FAKE, f1, M, N, K, FAKE, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_forward_f32_noalloc", None, FAKE, f1, 4, 64, 64, FAKE, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward_f32_noalloc", FAKE, FAKE, f1, 4, 64, 64, None, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward_f32_noalloc", FAKE + 4, FAKE, f1, 4, 64, 64, FAKE, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward_f32_noalloc", FAKE, FAKE, f1, 4, 64, 40, FAKE, None) == L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_forward_f32_noalloc", FAKE, FAKE, f1, 0, 64, 64, FAKE, None) == L.BITLINEAR_OK
+
+
 def test_grouped_planner_validation():
     def probs(n, **over):
         specs = []
