@@ -23,10 +23,16 @@
 // when the interval S/K * (1 +- (K+4) 2^-52) holds no float32 rounding
 // boundary, the float32 nearest to S/K is the correctly rounded exact mean.
 // Otherwise (exact ties, results within ~2^-40 of a boundary, very long rows)
-// the row takes the exact path: every square sig^2 * 2^(2t-298) (|x| = sig *
-// 2^(t-149)) is added, split in two 24-bit halves, to a per-exponent 64-bit
-// LDS bin, and one thread assembles the 640-bit sum, divides it by K limb by
-// limb and rounds the quotient.
+// the row takes an exact path in two tiers.  First every square is summed in
+// 128-bit integers of a fixed-point window below the row's largest square
+// (window_add): exact for every element within 2^28 of the largest, and the
+// rest contribute their whole units while flagging their dropped remainders;
+// the quotient by K is then rounded exactly, or -- when remainders were
+// dropped -- accepted only if both ends of the interval they span round
+// alike.  Rows that stay undecided (remainders that could tip a tie) add every
+// square sig^2 * 2^(2t-298) (|x| = sig * 2^(t-149)), split in two 24-bit
+// halves, to a per-exponent 64-bit LDS bin; one thread assembles the 640-bit
+// sum, divides it by K limb by limb and rounds the quotient.
 #include "quant_row.hpp"
 #include "rmsnorm.hpp"
 
@@ -151,6 +157,125 @@ __device__ float exact_mean_f32(uint32_t* big, uint64_t K) {
     return __uint_as_float(((uint32_t)(p_lsb + 23 + 127) << 23) | (sig & 0x7fffffu));
 }
 
+// ---- the windowed exact sum (the first exact tier)
+//
+// With T the exponent index of the row's largest |x| (|x| = sig * 2^(t - 149)),
+// every square sig^2 * 2^(2t - 298) is a whole number of units
+// u = 2^(2T - 354) when t >= T - 28: sig^2 * 2^(2(t - T) + 56) < 2^104, and
+// K <= 2^21 of them sum below 2^125.  Squares of elements more than 2^28
+// below the largest keep their whole units and flag the dropped remainder
+// ("lost"), which adds less than one unit each.
+struct U128 {
+    uint64_t lo, hi;
+};
+
+__host__ __device__ inline void add128(U128& a, uint64_t lo, uint64_t hi) {
+    a.lo += lo;
+    a.hi += hi + (a.lo < lo ? 1u : 0u);
+}
+
+__host__ __device__ inline void window_add(U128& acc, bool& lost, float v, int T) {
+    const uint32_t bits = __float_as_uint(v) & 0x7fffffffu;
+    const uint32_t e = bits >> 23, f = bits & 0x7fffffu;
+    const uint64_t sig = e ? (f | 0x800000u) : f;
+    if (!sig) return;
+    const int t = e ? (int)e - 1 : 0;
+    const uint64_t sq = sig * sig;   // < 2^48
+    const int sh = 2 * (t - T) + 56;  // <= 56 (t <= T)
+    if (sh >= 0) {
+        add128(acc, sq << sh, sh == 0 ? 0ull : sq >> (64 - sh));
+    } else if (sh > -48) {
+        const uint64_t q = sq >> -sh;
+        if ((q << -sh) != sq) lost = true;
+        add128(acc, q, 0ull);
+    } else {
+        lost = true;
+    }
+}
+
+__host__ __device__ inline int bit128(uint64_t hi, uint64_t lo, int p) {
+    if (p < 0 || p >= 128) return 0;
+    return p < 64 ? (int)((lo >> p) & 1u) : (int)((hi >> (p - 64)) & 1u);
+}
+
+// Whether any bit of (hi, lo) below position p is set.
+__host__ __device__ inline bool any_below128(uint64_t hi, uint64_t lo, int p) {
+    if (p <= 0) return false;
+    if (p >= 128) return (hi | lo) != 0;
+    if (p <= 64) return (lo & (p == 64 ? ~0ull : ((1ull << p) - 1ull))) != 0;
+    return lo != 0 || (hi & ((1ull << (p - 64)) - 1ull)) != 0;
+}
+
+// The float32 nearest (ties to even) to (Q + f) * 2^E for an integer Q >= 1
+// and a fraction f in [0, 1) that is zero exactly when sticky_extra is false.
+__host__ __device__ inline float round_units(uint64_t qhi, uint64_t qlo, int E, bool sticky_extra) {
+    const int L = qhi ? 128 - __builtin_clzll(qhi) : 64 - __builtin_clzll(qlo);   // bit length, >= 1
+    const int a_lead = L - 1 + E;
+    if (a_lead > 127) return INFINITY;
+    int p_lsb = a_lead - 23 > -149 ? a_lead - 23 : -149;
+    const int b = p_lsb - E;   // bit of Q that is the float's last significand bit
+    uint32_t sig = 0;
+    for (int p = L - 1; p >= b && p >= 0; --p) sig = (sig << 1) | (uint32_t)bit128(qhi, qlo, p);
+    // b >= 12 here: S holds at least one square of >= 2^56 units, so Q >= 2^35.
+    const int rb = bit128(qhi, qlo, b - 1);
+    const bool sticky = sticky_extra || any_below128(qhi, qlo, b - 1);
+    if (rb && (sticky || (sig & 1u))) ++sig;
+    if (sig == (1u << 24)) {
+        sig >>= 1;
+        ++p_lsb;
+    }
+    if (p_lsb + 23 > 127) return INFINITY;
+    if (sig < (1u << 23)) return __uint_as_float(sig);   // subnormal: p_lsb == -149
+    return __uint_as_float(((uint32_t)(p_lsb + 23 + 127) << 23) | (sig & 0x7fffffu));
+}
+
+// The exactly rounded mean from the window sum S (units u = 2^E) over K
+// terms; false when the dropped remainders could decide the rounding.
+__host__ __device__ inline bool window_mean_f32(U128 S, bool lost, uint64_t K, int E, float& out) {
+    if ((S.hi | S.lo) == 0) {
+        if (lost) return false;
+        out = 0.0f;
+        return true;
+    }
+    // Q = floor(S / K), R = S mod K, 32 bits at a time (R < K <= 2^21).
+    const uint32_t limb[4] = {(uint32_t)(S.hi >> 32), (uint32_t)S.hi, (uint32_t)(S.lo >> 32), (uint32_t)S.lo};
+    uint32_t q[4];
+    uint64_t r = 0;
+    for (int i = 0; i < 4; ++i) {
+        const uint64_t cur = (r << 32) | limb[i];
+        q[i] = (uint32_t)(cur / K);
+        r = cur % K;
+    }
+    const uint64_t qhi = ((uint64_t)q[0] << 32) | q[1], qlo = ((uint64_t)q[2] << 32) | q[3];
+    if ((qhi | qlo) == 0) return false;   // mean below one unit: leave it to the bins
+    if (!lost) {   // exact: S / K = Q + R / K
+        out = round_units(qhi, qlo, E, r != 0);
+        return true;
+    }
+    // S / K lies in (Q, Q + 2) units: decided when both ends round alike.
+    const uint64_t q1lo = qlo + 1, q1hi = qhi + (q1lo == 0 ? 1u : 0u);
+    const float lo_end = round_units(qhi, qlo, E, true), hi_end = round_units(q1hi, q1lo, E, true);
+    if (__float_as_uint(lo_end) != __float_as_uint(hi_end)) return false;
+    out = lo_end;
+    return true;
+}
+
+__device__ inline void window_add4(U128& acc, bool& lost, float4 v, int T) {
+    window_add(acc, lost, v.x, T);
+    window_add(acc, lost, v.y, T);
+    window_add(acc, lost, v.z, T);
+    window_add(acc, lost, v.w, T);
+}
+
+__device__ inline U128 wave_sum128(U128 v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t lo = __shfl_xor(v.lo, off, 64), hi = __shfl_xor(v.hi, off, 64);
+        add128(v, lo, hi);
+    }
+    return v;
+}
+
 __device__ inline void bin_square(unsigned long long (*bins)[2], float v) {
     const uint32_t bits = __float_as_uint(v) & 0x7fffffffu;
     const uint32_t e = bits >> 23, f = bits & 0x7fffffu;
@@ -192,6 +317,9 @@ __device__ void rmsnorm_quant_row(const float* __restrict__ x, int64_t K, int8_t
     __shared__ uint32_t big[kLimbs];
     __shared__ unsigned long long raw[kLimbs];
     __shared__ float ms_sh;
+    __shared__ int ok_sh;
+    __shared__ unsigned long long red_lo[W], red_hi[W];
+    __shared__ int red_lost[W];
     const float4* x4 = reinterpret_cast<const float4*>(x);
     uint32_t* q4 = reinterpret_cast<uint32_t*>(xq);
     const int64_t n4 = K >> 2;
@@ -240,7 +368,45 @@ __device__ void rmsnorm_quant_row(const float* __restrict__ x, int64_t K, int8_t
     double lo, hi;
     f32_rounding_interval(ms, lo, hi);
     const bool ambiguous = !(q - q * d > lo && q + q * d < hi);
-    if (ambiguous) {   // uniform: the exact path
+    bool resolved = !ambiguous;
+    if (ambiguous) {   // uniform: the windowed exact sum
+        const uint32_t ab = __float_as_uint(amax);
+        const int T = (ab >> 23) ? (int)(ab >> 23) - 1 : 0;
+        U128 acc{0ull, 0ull};
+        bool lost = false;
+        if constexpr (R > 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (t + (int64_t)r * THREADS < n4) window_add4(acc, lost, cache[r], T);
+        } else {
+            for (int64_t i = t; i < n4; i += THREADS) window_add4(acc, lost, x4[i], T);
+        }
+        acc = wave_sum128(acc);
+        const bool lost_w = __any(lost);
+        if (lane == 0) {
+            red_lo[wave] = acc.lo;
+            red_hi[wave] = acc.hi;
+            red_lost[wave] = lost_w ? 1 : 0;
+        }
+        __syncthreads();
+        if (t == 0) {
+            U128 S{0ull, 0ull};
+            bool any_lost = false;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                add128(S, red_lo[w], red_hi[w]);
+                any_lost = any_lost || red_lost[w];
+            }
+            float m = 0.0f;
+            const bool ok = window_mean_f32(S, any_lost, (uint64_t)K, 2 * T - 354, m);
+            ms_sh = m;
+            ok_sh = ok ? 1 : 0;
+        }
+        __syncthreads();
+        resolved = ok_sh != 0;
+        ms = ms_sh;
+    }
+    if (!resolved) {   // uniform: the binned exact path
         for (int i = t; i < 2 * kBins; i += THREADS) (&bins[0][0])[i] = 0ull;
         __syncthreads();
         if constexpr (R > 0) {

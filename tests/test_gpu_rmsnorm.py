@@ -72,6 +72,85 @@ def test_exact_path_rows():
     check(np.array(rows, np.float32))
 
 
+# ---- rows the windowed exact sum cannot decide
+# The kernel first sums the squares exactly in 128-bit integers of units
+# u = 2^(2T - 354) (T: exponent index of the row's largest |x|); squares of
+# elements more than 2^28 below the largest keep their whole units and drop a
+# remainder.  When remainders were dropped and the window sum S_w leaves the
+# mean within two units below a float32 rounding midpoint, both roundings are
+# possible and the row takes the binned exact path.  The rows below are built
+# to land there: a largest element 1.0, then elements chosen greedily (exact
+# integer arithmetic) so that S_w = K * midpoint - c exactly, then one element
+# 2^86 times smaller whose square leaves only a dropped remainder.
+
+def _parts(v):
+    b = int(np.float32(abs(v)).view(np.uint32))
+    e, f = b >> 23, b & 0x7FFFFF
+    return ((f | 0x800000) if e else f), (e - 1 if e else 0)
+
+
+def _window(xs, T):
+    S, lost = 0, False
+    for v in xs:
+        sig, t = _parts(v)
+        if not sig:
+            continue
+        sq, sh = sig * sig, 2 * (t - T) + 56
+        if sh >= 0:
+            S += sq << sh
+        elif sh > -48:
+            lost = lost or (sq >> -sh) << -sh != sq
+            S += sq >> -sh
+        else:
+            lost = True
+    return S, lost
+
+
+def _undecided_row(K, j, c, seed):
+    from fractions import Fraction
+    from math import isqrt, ldexp
+    from oracle_pins import nearest_f32
+    rng = np.random.default_rng(seed)
+    T, E = 126, 2 * 126 - 354                      # largest element 1.0; units 2^-102
+    target = K * (2 * j + 1) * 2 ** (-25 - E) - c   # K * (float32 midpoint in [0.5, 1)) - c
+    xs, rem = [1.0], target - (2 ** 46 << 56)
+    for t in range(T, 74, -1):
+        sh = 2 * (t - T) + 56
+        while len(xs) < K - 2 and rem > 0:
+            if sh >= 0:
+                sig = min(isqrt(rem >> sh), 2 ** 24 - 1)
+                part = lambda s: (s * s) << sh
+            else:
+                sig = min(isqrt((rem << -sh) + (1 << -sh) - 1), 2 ** 24 - 1)
+                while ((sig * sig) >> -sh) > rem:
+                    sig -= 1
+                part = lambda s: (s * s) >> -sh
+            if sig < 2 ** 23:
+                break
+            xs.append(float(np.float32(ldexp(sig, t - 149))) * (1 if rng.random() < 0.5 else -1))
+            rem -= part(sig)
+    assert rem == 0
+    xs.append(float(np.float32(ldexp(2 ** 23 + 12345, 40 - 149))))
+    x = np.array(xs + [0.0] * (K - len(xs)), np.float32)
+    rng.shuffle(x)
+    S, lost = _window(x, T)
+    Q = S // K
+    lo = nearest_f32((Fraction(Q) + Fraction(1, 2)) * Fraction(2) ** E)
+    hi = nearest_f32((Fraction(Q + 1) + Fraction(1, 2)) * Fraction(2) ** E)
+    assert lost and lo != hi   # the window tier cannot decide this row
+    return x
+
+
+def test_binned_tier_rows():
+    rows = [_undecided_row(64, j, c, 10 * c + i) for i, j in enumerate((12582911, 9000001, 16000000))
+            for c in (1, 7, 31)]
+    check(np.array(rows, np.float32))
+    # the same rows among ordinary ones in a longer launch
+    x = S.random_x(4242, 12, 64)
+    x[::4] = np.array(rows[:3], np.float32)
+    check(x)
+
+
 def test_wide_range_rows():
     rng = np.random.default_rng(77)
     for K in (16, 64, 1040, 8192):
