@@ -169,6 +169,43 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
         }
     }
 
+    const bool split = GROUPED ? p.slices > 1 : a.sk.S > 1;
+    if (MT == 1 && !split && !p.y_int && (N & 3) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0) {
+        // Up to 16 token rows: the block's 16 x 256 outputs go through LDS (8
+        // rows at a time, in the stage buffers, free after the K loop) and
+        // leave as whole row runs, 16 bytes per lane and 1 KB per wave store,
+        // with non-temporal stores.  Measured 3.7% faster over the 70B-shaped
+        // sweep at 16 tokens than per-element device-scope stores.
+        float* stage = reinterpret_cast<float*>(lds);   // [8][256]
+        const int t = threadIdx.x;
+        const int64_t n0 = blk * kSkinnyRows;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            __syncthreads();   // the last K step's reads (or the previous half's stores) are done
+            if (group_ok) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = lg * 4 + r;
+                    if ((m >> 3) != h || m >= M) continue;
+                    const float sc = dequant_scale(p.eta[m], p.gamma);
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+                        stage[(m & 7) * 256 + wave * 64 + tt * 16 + nl] = dequant(acc[0][tt][r] - accs[0][r], sc);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int idx = t + 256 * q;
+                const int row = idx >> 6, c4 = idx & 63;
+                const int64_t m = 8 * h + row, n = n0 + c4 * 4;
+                if (m >= M || n >= N) continue;   // N % 4 == 0: a float4 is wholly inside or outside
+                const nv_f32x4 v = *reinterpret_cast<const nv_f32x4*>(stage + row * 256 + c4 * 4);
+                __builtin_nontemporal_store(v, reinterpret_cast<nv_f32x4*>(p.y + m * N + n));
+            }
+        }
+        return;
+    }
     // Epilogue: element r of tile (i, t) is row 16i + 4lg + r, column 16t + nl.
     if (!group_ok) return;
 #pragma unroll
@@ -177,7 +214,6 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
         for (int r = 0; r < 4; ++r) {
             const int64_t m = i * 16 + lg * 4 + r;
             if (m >= M) continue;
-            const bool split = GROUPED ? p.slices > 1 : a.sk.S > 1;
             const float s = split ? 0.0f : dequant_scale(p.eta[m], p.gamma);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
