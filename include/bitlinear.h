@@ -311,7 +311,10 @@ int bitlinear_forward_lut(const int8_t* xq, const float* eta, const uint8_t* pac
  * step).  Planning builds a work table in caller-owned device memory once;
  * each forward then queues at most three kernels: quantize all, contract all,
  * and -- for a plan too small to fill the chip, whose long K loops the
- * planner splits -- add the split partial sums and dequantize.
+ * planner splits -- add the split partial sums and dequantize.  A plan of up
+ * to two tokens too small to fill the chip (one transformer block, say), with
+ * every K at most 16384, queues one kernel that quantizes, contracts and
+ * dequantizes; it writes xq and eta of problems with x != NULL all the same.
  */
 typedef struct bitlinear_problem {
     const float* x;        /* [M][K] float32, or NULL: xq/eta already hold the quantized rows */

@@ -75,8 +75,9 @@ size_t forward_ws_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 Problem make_problem(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
-                     int64_t N, int64_t K, float* y, int32_t* y_int) {
+                     int64_t N, int64_t K, float* y, int32_t* y_int, const float* x = nullptr) {
     Problem p{};
+    p.x = x;
     p.xq = xq;
     p.eta = eta;
     p.packed = reinterpret_cast<const uint4*>(packed);
@@ -124,9 +125,11 @@ F32Ws f32_ws(int64_t M, int64_t N, int64_t K) {
 // Contraction kernel of a grouped plan: 0 dot4 GEMV, 1 prefill MFMA (128 x
 // 256 tiles), 2 skinny MFMA, 3 skinny MFMA with K split, 4 prefill MFMA
 // (64 x 256 tiles) with K split (split plans: partials in the table, then an
-// epilogue), 5 prefill MFMA (64 x 256 tiles), 6 dot4 GEMV with K split.
+// epilogue), 5 prefill MFMA (64 x 256 tiles), 6 dot4 GEMV with K split,
+// 7 fused dot4 GEMV (quantize + contract + dequant in one launch, whole K
+// per workgroup; no quantize stage).
 constexpr int32_t kPlanGemv = 0, kPlanGemm = 1, kPlanSkinny = 2, kPlanSkinnySplit = 3, kPlanGemmSplit = 4,
-                  kPlanGemmSmall = 5, kPlanGemvSplit = 6;
+                  kPlanGemmSmall = 5, kPlanGemvSplit = 6, kPlanGemvFused = 7, kPlanLast = 7;
 
 struct TableLayout {
     size_t problems_off, units_off, rows_off, part_off, bytes;
@@ -149,7 +152,7 @@ TableLayout table_layout(int64_t count, int64_t nunits, int64_t nrows, int32_t k
 
 // Work units of the grouped contraction for one problem (before K slices).
 int64_t problem_units(int32_t kernel, int64_t M, int64_t N) {
-    if (kernel == kPlanGemv) return ceil_div(N, 64);   // one wavefront per 64-row group
+    if (kernel == kPlanGemv || kernel == kPlanGemvFused) return ceil_div(N, 64);   // per 64-row group
     if (kernel == kPlanGemm) return ceil_div(N, gemm_tile_n(M));
     return ceil_div(N, kSkinnyRows);                   // one workgroup per 256 rows
 }
@@ -233,6 +236,20 @@ constexpr int64_t kGemvSmallWaves = 8192;
 constexpr int64_t kGemvSplitWaves = 4096;
 constexpr int64_t kGemvSplitMinKb = 8;
 
+// A dot4 plan of at most kFusedMaxM tokens whose 64-row groups give the chip
+// fewer than kGemvSmallWaves wavefronts, and whose K fits the fused kernel's
+// LDS, takes the fused kernel: one workgroup per group quantizes, contracts
+// the whole K loop and dequantizes.
+bool fused_gemv_plan(const std::vector<Problem>& problems, int64_t M) {
+    if (M <= 0 || M > kFusedMaxM) return false;
+    int64_t groups = 0;
+    for (const Problem& p : problems) {
+        if (p.K > kFusedMaxK) return false;
+        groups += ceil_div(p.N, 64);
+    }
+    return groups < kGemvSmallWaves;
+}
+
 bool choose_gemv_slices(std::vector<Problem>& problems) {
     int64_t groups = 0, work = 0;   // work: 64-row groups x k-blocks
     for (const Problem& p : problems) {
@@ -287,9 +304,13 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
         } else if (it->second != q.x) {
             return BITLINEAR_EINVAL;  // one xq buffer fed from two different sources
         }
-        out.problems.push_back(make_problem(q.xq, q.eta, q.packed, q.gamma, q.N, q.K, q.y, q.y_int));
+        out.problems.push_back(make_problem(q.xq, q.eta, q.packed, q.gamma, q.N, q.K, q.y, q.y_int, q.x));
     }
     out.kernel = plan_kernel(M);
+    if (out.kernel == kPlanGemv && fused_gemv_plan(out.problems, M)) {
+        out.kernel = kPlanGemvFused;
+        out.rows.clear();   // each workgroup quantizes its problem's rows itself
+    }
     if (out.kernel == kPlanGemv && M > 0 && choose_gemv_slices(out.problems)) out.kernel = kPlanGemvSplit;
     if (out.kernel == kPlanSkinny && M >= kSmallPlanTiledFromM) {
         // Small plans take the 64 x 256 prefill tiles from kSmallPlanTiledFromM
@@ -659,7 +680,7 @@ int bitlinear_grouped_plan_init(const bitlinear_problem* problems_host, int32_t 
 int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) {
     if (!plan || !plan->table || plan->count <= 0 || plan->M < 0) return BITLINEAR_EINVAL;
     if (plan->M == 0) return BITLINEAR_OK;
-    if (plan->kernel < kPlanGemv || plan->kernel > kPlanGemvSplit) return BITLINEAR_EINVAL;
+    if (plan->kernel < kPlanGemv || plan->kernel > kPlanLast) return BITLINEAR_EINVAL;
     const TableLayout L = table_layout(plan->count, plan->units, plan->quant_rows, plan->kernel, plan->M);
     if (plan->table_bytes < L.bytes) return BITLINEAR_EINVAL;
     const char* base = (const char*)plan->table;
@@ -673,6 +694,7 @@ int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) 
     if (rc) return rc;
     switch (plan->kernel) {
         case kPlanGemv: return launch_gemv_grouped(problems, units, plan->units, plan->M, nullptr, s);
+        case kPlanGemvFused: return launch_gemv_fused(problems, units, plan->units, plan->M, plan->max_K, s);
         case kPlanGemvSplit:
             return launch_gemv_grouped(problems, units, plan->units, plan->M,
                                        reinterpret_cast<int32_t*>(static_cast<char*>(plan->table) + L.part_off), s);

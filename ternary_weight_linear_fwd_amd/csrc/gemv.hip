@@ -17,6 +17,7 @@
 // accumulator), so one packed word costs 5 VALU ops + 4 dot4 per token.  The
 // activation bytes are wave-uniform and come from scalar loads.
 #include "kernels.hpp"
+#include "quant_row.hpp"
 #include "xcd.hpp"
 
 namespace bl {
@@ -174,6 +175,203 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs a) {
         p.y[m * N + row] = dequant(res[m], s);
         if (p.y_int) p.y_int[m * N + row] = res[m];
     }
+}
+
+// ---- fused grouped decode (M <= 2, small plans)
+//
+// A plan too small to fill the chip (one transformer block at a few tokens:
+// 520 row groups for hidden 3200 / FFN 8640) gives each (problem, 64-row
+// group) one workgroup of kFusedWaves wavefronts that covers the whole K
+// loop: wavefront w streams a contiguous run of the group's k-blocks (all of
+// its loads in flight at once up to kFusedBatch blocks).  Before contracting,
+// the workgroup quantizes the problem's M activation rows itself with the
+// quantizer's own arithmetic ([P1] "2. Absmax Dynamic Activation
+// Quantization": eta = max(max_k |x|, 1e-5), x~ = clamp(rne((x * 127) / eta),
+// -128, 127)) into LDS, along with each row's sum of x~; every workgroup of a
+// problem reads the same rows (from L2 after the first) and reaches the same
+// bits.  The wavefronts' partial sums meet in LDS and one pass subtracts
+// sum x~, dequantizes and stores.  The workgroup of row group 0 also writes
+// x~ and eta to the problem's xq / eta buffers, as the separate quantize stage
+// would.  No second launch, no partial sums in memory.
+constexpr int kFusedWaves = 8;
+constexpr int kFusedThreads = 64 * kFusedWaves;
+// k-blocks in flight per wavefront (registers: six wavefronts per SIMD, so
+// that three 8-wave workgroups fit on a CU)
+template <int M>
+constexpr int fused_batch() { return M == 1 ? 12 : 8; }
+constexpr int kFusedChunks = kFusedMaxK / 4 / kFusedThreads;   // float4 of a row per thread
+
+
+// Accumulate one k-block (16 bytes of codes per lane) against x~ rows in LDS
+// (row m at xs + m * kpad; every lane reads the same bytes: a broadcast).
+template <int M>
+__device__ __forceinline__ void dot_block_lds(Acc<M>& acc, const uint4 w, const uint8_t* xs, int64_t kpad,
+                                              int64_t kb) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t c0 = wd[d] & 0x03030303u;
+        const uint32_t c1 = wd[d] & 0x0C0C0C0Cu;
+        const uint32_t c2 = wd[d] & 0x30303030u;
+        const uint32_t c3 = (wd[d] >> 6) & 0x03030303u;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const nv_i32x4 x = *reinterpret_cast<const nv_i32x4*>(xs + m * kpad + kb * 64 + d * 16);
+            acc.a0[m] = __builtin_amdgcn_sdot4(x.x, (int)c0, acc.a0[m], false);
+            acc.a1[m] = __builtin_amdgcn_sdot4(x.y, (int)c1, acc.a1[m], false);
+            acc.a2[m] = __builtin_amdgcn_sdot4(x.z, (int)c2, acc.a2[m], false);
+            acc.a0[m] = __builtin_amdgcn_sdot4(x.w, (int)c3, acc.a0[m], false);
+        }
+    }
+}
+
+template <int M>
+__global__ __launch_bounds__(kFusedThreads, 6) void gemv_fused_kernel(const Problem* __restrict__ problems,
+                                                                   const Unit* __restrict__ units, int64_t nunits) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // [M][Kb * 64] x~, zero at k >= K
+    __shared__ float red_max[M][kFusedWaves];
+    __shared__ int red_sum[M][kFusedWaves];
+    __shared__ int xsum_sh[M];
+    __shared__ float eta_sh[M];
+    __shared__ int part[kFusedWaves][M][64];
+
+    const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lane = t & 63;
+    // Units in table order, which the dispatcher deals round-robin to the
+    // XCDs: problems of different K (the long down projection) spread evenly
+    // over the XCDs' shares of memory bandwidth.
+    const Unit un = units[blockIdx.x];
+    const Problem p = problems[un.problem];
+    const int64_t K = p.K, N = p.N, Kb = p.Kb, g = un.group;
+    const int64_t kpad = Kb * 64;
+
+    // This wavefront's contiguous run of k-blocks.
+    const int64_t nbw = (Kb + kFusedWaves - 1) / kFusedWaves;
+    const int64_t kb0 = (int64_t)wave * nbw;
+    const int64_t kb1 = kb0 + nbw < Kb ? kb0 + nbw : Kb;
+    const uint4* wp = p.packed + (g * Kb) * 64 + lane;
+
+    // x~ rows into LDS, with eta and sum x~ per row (the float32 chunks and the
+    // weight words below are never live together: registers for occupancy).
+    const int64_t n4 = K >> 2;
+#pragma unroll 1
+    for (int m = 0; m < M; ++m) {
+        uint32_t* q4 = reinterpret_cast<uint32_t*>(xs + m * kpad);
+        int sum = 0;
+        if (p.x) {
+            const float4* x4 = reinterpret_cast<const float4*>(p.x + m * K);
+            float4 v[kFusedChunks];
+            float amax = 0.0f;
+#pragma unroll
+            for (int r = 0; r < kFusedChunks; ++r) {
+                const int64_t i = t + (int64_t)r * kFusedThreads;
+                v[r] = i < n4 ? x4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[r].x), fabsf(v[r].y)), fmaxf(fabsf(v[r].z), fabsf(v[r].w))));
+            }
+            amax = wave_max(amax);
+            if (lane == 0) red_max[m][wave] = amax;
+            __syncthreads();
+            amax = red_max[m][0];
+#pragma unroll
+            for (int w = 1; w < kFusedWaves; ++w) amax = fmaxf(amax, red_max[m][w]);
+            const float eta = amax < kScaleFloor ? kScaleFloor : amax;
+#pragma unroll
+            for (int r = 0; r < kFusedChunks; ++r) {
+                const int64_t i = t + (int64_t)r * kFusedThreads;
+                if (i < n4) q4[i] = quant4(v[r], eta, sum);
+            }
+            if (t == 0) eta_sh[m] = eta;
+        } else {
+            // Already quantized: copy x~ (16 bytes per thread and pass) and sum it.
+            const uint4* src = reinterpret_cast<const uint4*>(p.xq + m * K);
+            for (int64_t i = t; i < K / 16; i += kFusedThreads) {
+                const uint4 v = src[i];
+                reinterpret_cast<uint4*>(q4)[i] = v;
+                sum = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, sum, false);
+                sum = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, sum, false);
+                sum = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, sum, false);
+                sum = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, sum, false);
+            }
+            if (t == 0) eta_sh[m] = p.eta[m];
+        }
+        // k in [K, kpad): zero activations against the pad codes.
+        for (int64_t i = n4 + t; i < kpad / 4; i += kFusedThreads) q4[i] = 0u;
+        sum = wave_sum(sum);
+        if (lane == 0) red_sum[m][wave] = sum;
+    }
+    __syncthreads();
+    if (t < M) {
+        int s = 0;
+#pragma unroll
+        for (int w = 0; w < kFusedWaves; ++w) s += red_sum[t][w];
+        xsum_sh[t] = s;
+    }
+
+    __syncthreads();   // x~, eta and the row sums are in LDS (a full barrier: no loads in flight here)
+
+    // The run's k-blocks, up to kFusedBatch in flight.
+    constexpr int kFusedBatch = fused_batch<M>();
+    uint4 wq[kFusedBatch];
+#pragma unroll
+    for (int i = 0; i < kFusedBatch; ++i)
+        if (kb0 + i < kb1) wq[i] = ldnt_u4(wp + (kb0 + i) * 64);
+
+    // Row group 0 hands x~ and eta on, as the quantize stage does.
+    if (g == 0 && p.x) {
+        for (int m = 0; m < M; ++m) {
+            const uint4* src = reinterpret_cast<const uint4*>(xs + m * kpad);
+            uint4* dst = reinterpret_cast<uint4*>(const_cast<int8_t*>(p.xq) + m * K);
+            for (int64_t i = t; i < K / 16; i += kFusedThreads) dst[i] = src[i];
+            if (t == 0) const_cast<float*>(p.eta)[m] = eta_sh[m];
+        }
+    }
+
+    Acc<M> acc;
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc.a0[m] = acc.a1[m] = acc.a2[m] = 0;
+#pragma unroll
+    for (int i = 0; i < kFusedBatch; ++i)
+        if (kb0 + i < kb1) dot_block_lds<M>(acc, wq[i], xs, kpad, kb0 + i);
+    // Runs longer than one batch.
+    for (int64_t kb = kb0 + kFusedBatch; kb < kb1; kb += kFusedBatch) {
+#pragma unroll
+        for (int i = 0; i < kFusedBatch; ++i)
+            if (kb + i < kb1) wq[i] = ldnt_u4(wp + (kb + i) * 64);
+#pragma unroll
+        for (int i = 0; i < kFusedBatch; ++i)
+            if (kb + i < kb1) dot_block_lds<M>(acc, wq[i], xs, kpad, kb + i);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[wave][m][lane] = acc.a0[m] + (acc.a1[m] >> 2) + (acc.a2[m] >> 4);
+    __syncthreads();
+
+    if (t < 64 * M) {
+        const int m = t >> 6;
+        const int64_t row = g * 64 + lane;
+        int v = 0;
+#pragma unroll
+        for (int w = 0; w < kFusedWaves; ++w) v += part[w][m][lane];
+        v -= xsum_sh[m];
+        if (row < N) {
+            p.y[m * N + row] = dequant(v, dequant_scale(eta_sh[m], p.gamma));
+            if (p.y_int) p.y_int[m * N + row] = v;
+        }
+    }
+}
+
+int launch_gemv_fused(const Problem* problems, const Unit* units, int64_t nunits, int64_t M, int64_t max_K,
+                      hipStream_t stream) {
+    if (max_K > kFusedMaxK) return BITLINEAR_EUNSUPPORTED;
+    const size_t lds = (size_t)M * (size_t)(ceil_div(max_K, 64) * 64);
+    const dim3 grid((unsigned)nunits), block(kFusedThreads);
+    switch (M) {
+        case 1: hipLaunchKernelGGL(gemv_fused_kernel<1>, grid, block, lds, stream, problems, units, nunits); break;
+        case 2: hipLaunchKernelGGL(gemv_fused_kernel<2>, grid, block, lds, stream, problems, units, nunits); break;
+        default: return BITLINEAR_EUNSUPPORTED;
+    }
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
 }
 
 // Sum the split-K partials in slice order and apply the dequant epilogue.

@@ -27,8 +27,10 @@ struct Problem {
     int32_t Kb;             // ceil(K / 64)
     int32_t unit_begin;     // first work unit of this problem in a grouped table
     int32_t slices;         // grouped skinny plans: K-slices per 256-row block (1: whole K)
+    const float* x;         // [M][K] float32 activations (fused grouped decode), or null
+    int32_t pad[2];
 };
-static_assert(sizeof(Problem) == 64, "Problem descriptor is one 64-byte line");
+static_assert(sizeof(Problem) == 80, "Problem descriptor: 80 bytes");
 
 // One work unit of the grouped decode kernel: (problem, 64-row group).
 struct Unit {
@@ -68,6 +70,16 @@ int launch_gemv(const Problem& p, int64_t M, void* ws, hipStream_t stream);
 // sums added by launch_grouped_splitk_epilogue (width 64), which follows.
 int launch_gemv_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
                         int32_t* partial, hipStream_t stream);
+
+// Fused grouped decode for M <= kFusedMaxM tokens on plans too small to fill the chip:
+// one workgroup per (problem, 64-row group) quantizes the problem's float32
+// rows itself (or copies x~ when the problem has no x), contracts the whole K
+// loop across its wavefronts and dequantizes -- one launch, no partial sums
+// in memory.  Problems' K at most kFusedMaxK; max_K the longest of them.
+constexpr int kFusedMaxK = 16384;
+constexpr int kFusedMaxM = 2;
+int launch_gemv_fused(const Problem* problems, const Unit* units, int64_t nunits, int64_t M, int64_t max_K,
+                      hipStream_t stream);
 
 // Sum split-K partials [S][M][N] in slice order and apply the dequant epilogue.
 int launch_splitk_epilogue(const int32_t* partial, int S, int64_t M, const Problem& p,

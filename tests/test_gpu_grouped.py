@@ -41,12 +41,20 @@ def test_grouped_block_matches_oracle(M):
     tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
     table = torch.empty(tb, dtype=torch.uint8, device="cuda")
     plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
-    assert plan.quant_rows == 5 * M          # q/k/v quantized once
+    if M <= 2:   # fused: every workgroup quantizes its own rows, no quantize stage
+        assert plan.quant_rows == 0 and plan.units == sum((p.N + 63) // 64 for p in S.C2_PROJS)
+    else:
+        assert plan.quant_rows == 5 * M      # q/k/v quantized once
     for rep in range(2):                      # a second run gives the same bits
+        for s in specs:
+            s["xq"].fill_(99)
+            s["eta"].fill_(-1.0)
         L.bitlinear_forward_grouped(plan)
         torch.cuda.synchronize()
         for s, (x_np, Wt, g) in zip(specs, refs):
             y_ref, xq_ref, eta_ref, y_int_ref = oracle.forward(x_np, Wt, g, threads=THREADS)
+            assert np.array_equal(s["xq"].cpu().numpy(), xq_ref)
+            assert np.array_equal(s["eta"].cpu().numpy().view(np.uint32), eta_ref.view(np.uint32))
             assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref)
             y = s["y"].cpu().numpy()
             assert_y_close(y, y_ref)
@@ -148,10 +156,14 @@ def test_grouped_split_k_small_plan(M):
     table = torch.empty(tb, dtype=torch.uint8, device="cuda")
     plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
     # split: more work units than row blocks (64 rows per unit for the
-    # dot4 GEMV, 256 otherwise), and the partials in the table
+    # dot4 GEMV, 256 otherwise), and the partials in the table; up to two
+    # tokens the fused kernel takes whole K loops instead
     width = 64 if M <= 4 else 256
-    assert plan.units > sum((N + width - 1) // width for N, _ in shapes)
-    assert tb >= plan.units * M * width * 4
+    if M <= 2:
+        assert plan.units == sum((N + 63) // 64 for N, _ in shapes) and plan.quant_rows == 0
+    else:
+        assert plan.units > sum((N + width - 1) // width for N, _ in shapes)
+        assert tb >= plan.units * M * width * 4
     for rep in range(2):
         L.bitlinear_forward_grouped(plan)
         torch.cuda.synchronize()
@@ -195,3 +207,56 @@ def test_grouped_prefill_tiles(M, shapes):
         y_ref, _, _, y_int_ref = oracle.forward(x_np, Wt, g, threads=THREADS)
         assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref)
         assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+# The fused small-plan decode (M <= 2: quantize, whole-K contraction and
+# dequant in one launch): problems fed from float32 rows and from already
+# quantized ones in one plan, a shared float32 input, ragged N, K with tail
+# blocks, the longest K the fused kernel takes (16384) and the shortest (16),
+# all-zero rows, int8 extremes; x~, eta, y_int and y against the oracle, twice.
+@pytest.mark.parametrize("M", [1, 2])
+def test_grouped_fused_decode(M):
+    torch = torch_cuda()
+    L = bl()
+    shapes = [(300, 4144), (64, 16), (1000, 16384), (257, 2064), (130, 1040), (65, 1040)]
+    xs = {K: S.random_x(400 + K + M, M, K, "t3") for _, K in shapes}
+    xs[2064][0] = 0.0                                     # an all-zero row
+    xs[16][M - 1] = np.float32(3.0e38) * (np.arange(16) % 2 * 2 - 1)   # |x| at the float32 top
+    shared = {K: torch.from_numpy(v).cuda() for K, v in xs.items()}
+    xq_shared = torch.empty((M, 1040), dtype=torch.int8, device="cuda")
+    eta_shared = torch.empty(M, dtype=torch.float32, device="cuda")
+    specs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        say(f"fused decode M={M} problem {i}: N={N} K={K}")
+        Wt = S.random_ternary(500 + i, N, K)
+        g = np.float32(0.017 + 0.003 * i)
+        packed = torch.empty(L.bitlinear_packed_bytes(N, K), dtype=torch.uint8, device="cuda")
+        L.bitlinear_pack_ternary(torch.from_numpy(Wt).cuda(), N, K, packed)
+        x_np = xs[K]
+        xq_ref, eta_ref = oracle.quantize_act(x_np)
+        if i == 3:   # already quantized: x = NULL, x~ and eta given
+            x, xq, eta = None, torch.from_numpy(xq_ref).cuda(), torch.from_numpy(eta_ref).cuda()
+        elif K == 1040:   # two problems share one float32 input and its x~ / eta buffers
+            x, xq, eta = shared[K], xq_shared, eta_shared
+        else:
+            x = shared[K]
+            xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+            eta = torch.empty(M, dtype=torch.float32, device="cuda")
+        specs.append(dict(x=x, xq=xq, eta=eta, packed=packed,
+                          y=torch.empty((M, N), dtype=torch.float32, device="cuda"),
+                          y_int=torch.empty((M, N), dtype=torch.int32, device="cuda"), gamma=g, N=N, K=K))
+        refs.append((x_np, Wt, g, xq_ref, eta_ref))
+    probs = L.make_problems(specs)
+    tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
+    table = torch.empty(tb, dtype=torch.uint8, device="cuda")
+    plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
+    assert plan.quant_rows == 0 and plan.units == sum((N + 63) // 64 for N, _ in shapes)
+    for rep in range(2):
+        L.bitlinear_forward_grouped(plan)
+        torch.cuda.synchronize()
+        for s, (x_np, Wt, g, xq_ref, eta_ref) in zip(specs, refs):
+            y_ref, y_int_ref = oracle.forward_q(xq_ref, eta_ref, Wt, g, threads=THREADS)
+            assert np.array_equal(s["xq"].cpu().numpy(), xq_ref)
+            assert np.array_equal(s["eta"].cpu().numpy().view(np.uint32), eta_ref.view(np.uint32))
+            assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref)
+            assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
