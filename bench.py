@@ -405,6 +405,10 @@ def bench_rmsnorm(torch, L, S, reps: int):
     out = []
     cases = [(f"prefill x K={S.C3_SHAPES[w][0]}", S.c3_inputs(w)[1]) for w in (0, 1)]
     cases += [(f"decode x M={M} K={K}", S.random_x(9000 + M + K, M, K)) for M, K in ((16, 8192), (16, 28672))]
+    # Heavy-tailed rows (a few of them land next to a float32 rounding boundary
+    # of the mean of squares and take the exact path) against normal rows.
+    cases += [(f"student-t x K=11008", S.random_x(9100, 1024, 11008, "t3")),
+              (f"normal x K=11008", S.random_x(9101, 1024, 11008))]
     for name, x in cases:
         M, K = x.shape
         xd = torch.from_numpy(x).cuda()
@@ -626,6 +630,36 @@ def summarize_profile(root: str) -> str:
     return "\n".join(out)
 
 
+def summarize_pmc(root: str) -> str:
+    """Markdown table of the counters of every rocprofv3 --pmc run under
+    root/pmc*/: per contraction kernel of this library (and the int8 MFMA-loop probe), the
+    median of each counter over its dispatches, with the matrix-core busy
+    fraction SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs) where
+    both were collected (GRBM_GUI_ACTIVE sums the XCDs' active cycles)."""
+    import glob
+    import statistics
+    per = {}
+    for path in sorted(glob.glob(os.path.join(root, "pmc*", "**", "*counter_collection.csv"), recursive=True)):
+        for r in _csv_rows(path):
+            name = r["Kernel_Name"]
+            if not any(k in name for k in ("gemm_prefill", "mfma_loop", "skinny_mfma", "gemv_dot4", "gemv_fused")):
+                continue
+            per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not per:
+        return ""
+    out = ["| kernel | counter | median per dispatch | dispatches |", "|---|---|---|---|"]
+    for name, cs in per.items():
+        short = name[:70].replace("|", "/")
+        for c in sorted(cs):
+            out.append(f"| {short} | {c} | {statistics.median(cs[c]):,.0f} | {len(cs[c])} |")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in cs and "GRBM_GUI_ACTIVE" in cs:
+            busy = statistics.median(cs["SQ_VALU_MFMA_BUSY_CYCLES"])
+            active = statistics.median(cs["GRBM_GUI_ACTIVE"]) / 8.0
+            out.append(f"| {short} | matrix cores busy | {busy / (active * 1024):.1%} "
+                       f"(of {active:,.0f} cycles per XCD, 1024 SIMDs) | |")
+    return "\n".join(out)
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_dot4_grouped_decode70b_m1_traffic.json")
 
 
@@ -671,6 +705,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize:
         print(summarize_profile(args.summarize))
+        print(summarize_pmc(args.summarize))
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -765,7 +800,8 @@ def main() -> int:
             extra[key] = bench_block(torch, L, S, max(10, args.steps), which)
             for r in extra[key]["per_M"]:
                 log(f"C{which} block M={r['M']}: grouped {r['grouped_us_cold']} us cold / {r['grouped_us_hot']} "
-                    f"hot, seven single calls {r['single_calls_us_cold']} / {r['single_calls_us_hot']} us "
+                    f"hot (graph replay; eager {r['grouped_us_cold_eager']} / {r['grouped_us_hot_eager']}), seven "
+                    f"single calls {r['single_calls_us_cold_eager']} / {r['single_calls_us_hot_eager']} us eager "
                     f"(floor {r['roofline_floor_us']} us, {r['frac_of_roofline_cold']:.1%} cold)")
 
     if not args.no_prefill:
