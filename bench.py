@@ -433,10 +433,14 @@ def bench_rmsnorm(torch, L, S, reps: int):
 
 
 def bench_lut(torch, L, reps: int):
-    """Decode (M = 1) on the largest 70B-shaped projections: the dot4 path on
-    the 2-bit layout next to the lookup-table path on the 2-bit and on the
-    base-3 layout.  Weight GB/s counts each layout's own bytes; weights/s is
-    the format-independent rate."""
+    """Decode (M = 1) on the largest 70B-shaped projections, one call each way:
+    dot4 on the 2-bit layout (the decode path of bitlinear_forward), the
+    matrix-core path on the base-3 layout (bitlinear_forward3) and the
+    lookup-table path on both layouts.  Device time per call from HIP-graph
+    replays, hot (one weight copy, called repeatedly: it stays in the 256 MB
+    MALL) and cold (copies of more than 1.2 GB in all cycled, one per call).
+    Weight GB/s counts each layout's own bytes; weights/s is the
+    format-independent rate."""
     out = []
     for K, N in ((8192, 28672), (28672, 8192)):
         gen = torch.Generator(device="cuda").manual_seed(K + N)
@@ -449,31 +453,61 @@ def bench_lut(torch, L, reps: int):
         xq = torch.randint(-127, 128, (1, K), generator=gen, device="cuda", dtype=torch.int32).to(torch.int8)
         eta = torch.ones(1, dtype=torch.float32, device="cuda")
         y = torch.empty((1, N), dtype=torch.float32, device="cuda")
-        ws_bytes = max(L.bitlinear_workspace_bytes(1, N, K),
+        ws_bytes = max(L.bitlinear_workspace_bytes(1, N, K), L.bitlinear_forward3_workspace_bytes(1, N, K),
                        L.bitlinear_lut_workspace_bytes(1, N, K, L.BITLINEAR_FORMAT_2BIT),
                        L.bitlinear_lut_workspace_bytes(1, N, K, L.BITLINEAR_FORMAT_BASE3))
         ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
-        st = torch.cuda.current_stream().cuda_stream
-        a = [t.data_ptr() for t in (xq, eta, p2, p3, y, ws)]
+        copies = {}
+        for name, src in (("2bit", p2), ("base3", p3)):
+            n = max(2, -(-COLD_BYTES // src.numel()))
+            copies[name] = [src] + [src.clone() for _ in range(n - 1)]
+        a = [t.data_ptr() for t in (xq, eta, y, ws)]
         runs = {
-            "dot4_2bit": (lambda: L.bitlinear_forward(a[0], a[1], a[2], 0.02, 1, N, K, a[4], None, a[5],
-                                                      ws_bytes, st), p2),
-            "lut_2bit": (lambda: L.bitlinear_forward_lut(a[0], a[1], a[2], L.BITLINEAR_FORMAT_2BIT, 0.02, 1, N,
-                                                         K, a[4], None, a[5], ws_bytes, st), p2),
-            "lut_base3": (lambda: L.bitlinear_forward_lut(a[0], a[1], a[3], L.BITLINEAR_FORMAT_BASE3, 0.02, 1,
-                                                          N, K, a[4], None, a[5], ws_bytes, st), p3),
+            "dot4_2bit": ("2bit", lambda pk, st: L.bitlinear_forward(a[0], a[1], pk, 0.02, 1, N, K, a[2], None,
+                                                                     a[3], ws_bytes, st)),
+            "base3_mfma": ("base3", lambda pk, st: L.bitlinear_forward3(a[0], a[1], pk, 0.02, 1, N, K, a[2], None,
+                                                                        a[3], ws_bytes, st)),
+            "lut_2bit": ("2bit", lambda pk, st: L.bitlinear_forward_lut(a[0], a[1], pk, L.BITLINEAR_FORMAT_2BIT,
+                                                                        0.02, 1, N, K, a[2], None, a[3],
+                                                                        ws_bytes, st)),
+            "lut_base3": ("base3", lambda pk, st: L.bitlinear_forward_lut(a[0], a[1], pk, L.BITLINEAR_FORMAT_BASE3,
+                                                                          0.02, 1, N, K, a[2], None, a[3],
+                                                                          ws_bytes, st)),
         }
-        row = {"gemv": f"M=1 K={K} N={N}"}
-        for name, (fn, packed) in runs.items():
-            for _ in range(3):
-                fn()
-            ms = time_events(torch, fn, reps)
-            row[name] = {"us": round(ms * 1e3, 2),
-                         "weight_gbs": round(packed.numel() / (ms * 1e-3) / 1e9, 1),
-                         "gweights_per_s": round(N * K / (ms * 1e-3) / 1e9, 1)}
+        row = {"gemv": f"M=1 K={K} N={N}",
+               "cold": f"{len(copies['2bit'])} 2-bit / {len(copies['base3'])} base-3 weight copies cycled"}
+        for name, (fmt, fn) in runs.items():
+            cs = copies[fmt]
+            ptrs = [c.data_ptr() for c in cs]
+            hot = time_graph(torch, lambda i, st: fn(ptrs[0], st), 20, max(5, reps // 2))
+            cold = time_graph(torch, lambda i, st: fn(ptrs[i], st), len(ptrs), max(3, reps // 5))
+            nbytes = cs[0].numel()
+            row[name] = {"us_hot": round(hot * 1e3, 2), "us_cold": round(cold * 1e3, 2),
+                         "weight_gbs_cold": round(nbytes / (cold * 1e-3) / 1e9, 1),
+                         "gweights_per_s_cold": round(N * K / (cold * 1e-3) / 1e9, 1)}
+        row["base3_over_dot4"] = {k: round(row["base3_mfma"][k] / row["dot4_2bit"][k], 3)
+                                  for k in ("us_cold", "us_hot")}
+        # the floor of one launch that only reads that many bytes (the stream
+        # probe, cold, same copies)
+        sink = torch.empty(L.bitlinear_measure_sink_bytes() // 4, dtype=torch.int32, device="cuda")
+        for fmt in ("2bit", "base3"):
+            cs = copies[fmt]
+            ms = time_graph(torch, lambda i, st: L.bitlinear_measure_stream_read(cs[i], cs[i].numel(), sink, st),
+                            len(cs), max(3, reps // 5))
+            row[f"read_only_{fmt}_us_cold"] = round(ms * 1e3, 2)
         out.append(row)
-        del p2, p3, xq, eta, y, ws
+        del p2, p3, xq, eta, y, ws, copies
+        torch.cuda.empty_cache()
     return out
+
+
+def lut_line(r) -> str:
+    return f"decode {r['gemv']}: " + "; ".join(
+        f"{k} {v['us_cold']} us cold / {v['us_hot']} hot ({v['weight_gbs_cold']} GB/s, "
+        f"{v['gweights_per_s_cold']} Gw/s cold)"
+        for k, v in r.items() if isinstance(v, dict) and "weight_gbs_cold" in v) + \
+        f"; base-3 / dot4 {r['base3_over_dot4']['us_cold']} cold, {r['base3_over_dot4']['us_hot']} hot" + \
+        f"; read-only launch {r['read_only_2bit_us_cold']} us (2-bit bytes), {r['read_only_base3_us_cold']} us (base-3)"
 
 
 def bench_pack(torch, L, reps: int):
@@ -701,6 +735,9 @@ def main() -> int:
     ap.add_argument("--profile-blocks", action="store_true",
                     help="time only the single-block grouped forwards (3B block at M=1, 8; "
                          "hidden-4096 block at M=32, 64, 128), for a rocprofv3 run")
+    ap.add_argument("--profile-decode3", action="store_true",
+                    help="time only the M=1 decode of the two largest 70B projections in both weight "
+                         "formats (dot4, base-3 matrix cores, lookup tables), for a rocprofv3 run")
     ap.add_argument("--summarize", metavar="DIR", help="summarize rocprofv3 output under DIR")
     args = ap.parse_args()
     if args.summarize:
@@ -728,6 +765,10 @@ def main() -> int:
             for r in bench_block(torch, L, S, max(1, args.steps), which)["per_M"]:
                 log(f"C{which} block M={r['M']}: grouped {r['grouped_us_cold']} us cold / "
                     f"{r['grouped_us_hot']} us hot")
+        return 0
+    if args.profile_decode3:
+        for r in bench_lut(torch, L, max(5, args.steps)):
+            log(lut_line(r))
         return 0
     if args.profile_prefill:
         for r in bench_prefill(torch, L, S, max(1, args.steps))[0]:
@@ -813,9 +854,7 @@ def main() -> int:
     if not args.no_prefill:
         extra["lut_decode"] = bench_lut(torch, L, max(10, args.steps))
         for r in extra["lut_decode"]:
-            log(f"decode {r['gemv']}: " + "; ".join(
-                f"{k} {v['us']} us {v['weight_gbs']} GB/s {v['gweights_per_s']} Gw/s"
-                for k, v in r.items() if k != "gemv"))
+            log(lut_line(r))
 
     if not args.no_prefill:
         extra["pack"] = bench_pack(torch, L, 3)

@@ -270,12 +270,16 @@ int bitlinear_forward_rmsnorm_f32(const float* x, const uint8_t* packed, float g
  * Canonical byte: v = sum_j (w[5b + j] + 1) * 3^j, pads weight 0.
  * Base-3 device layout ("base-3 layout"): rows grouped by 64, K cut into
  * blocks of 80; block (g, b) of 1024 bytes holds 16 bytes per row in order,
- * byte p of row r being the canonical byte of k = 80b + 5p .. 80b + 5p + 4.
- * Rows past N and k past K hold weight 0.  Bytes above 242 never occur.
+ * byte p of row r being the fraction form q = ceil(256 v / 243) of the
+ * canonical byte v of k = 80b + 5p .. 80b + 5p + 4 (v = floor(243 q / 256);
+ * floor(3^s q / 256) is v's top s digits, which the decode uses).  Rows past
+ * N and k past K hold weight 0 (q = 128).  The 13 byte values that are no
+ * fraction form (1, 20, 40, 60, 79, 99, 119, 138, 158, 178, 197, 217, 237)
+ * never occur.
  *   bitlinear_packed3_bytes(N, K) = ceil(N/64) * ceil(K/80) * 1024.
  * pack_weights3, pack_ternary3 and unpack_weights3 mirror the 2-bit calls
- * (same gamma, workspace and `bad` conventions; unpack counts bytes above 242
- * inside [0, N) x [0, K) and decodes them as zero weights).
+ * (same gamma, workspace and `bad` conventions; unpack counts bytes that are
+ * no fraction form inside [0, N) x [0, K) and decodes them as zero weights).
  */
 size_t bitlinear_packed3_bytes(int64_t N, int64_t K);
 int bitlinear_pack_weights3(const float* W, int64_t N, int64_t K, uint8_t* packed3, float* gamma,
@@ -304,6 +308,26 @@ size_t bitlinear_lut_workspace_bytes(int64_t M, int64_t N, int64_t K, int format
 int bitlinear_forward_lut(const int8_t* xq, const float* eta, const uint8_t* packed, int format,
                           float gamma, int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Base-3 forward: the contraction and dequantization of bitlinear_forward,
+ * read straight from the base-3 layout (1.6 bits per weight) on the matrix
+ * cores; results identical to bitlinear_forward's.  [P2] the bandwidth
+ * paragraph before "Scaling Laws and Empirical Benchmarks" (compact ternary
+ * packing) and "3. Additive Integer Accumulation".  Built for decode: each
+ * pass over the weights serves up to 8 tokens, so larger M costs ceil(M/8)
+ * passes.
+ *   xq      [M][K] int8, 16-byte aligned; eta [M] float32
+ *   packed3 base-3 layout of the [N][K] ternary matrix, 16-byte aligned
+ *   y       [M][N] float32; y_int [M][N] int32 or NULL
+ *   ws      workspace of bitlinear_forward3_workspace_bytes(M, N, K) bytes
+ *           (K-split partial sums; 0 bytes needs no workspace), 256-byte aligned
+ * Same errors as bitlinear_forward.
+ */
+size_t bitlinear_forward3_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int bitlinear_forward3(const int8_t* xq, const float* eta, const uint8_t* packed3, float gamma,
+                       int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,
+                       size_t ws_bytes, void* stream);
 
 /*
  * Grouped forward: many independent BitLinear problems of the same token

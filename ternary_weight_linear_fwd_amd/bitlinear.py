@@ -82,6 +82,8 @@ _SIGS = {
     "bitlinear_lut_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], _SZ),
     "bitlinear_forward_lut": ([_P, _P, _P, ctypes.c_int, _F, _I64, _I64, _I64, _P, _P, _P, _SZ,
                                _P], ctypes.c_int),
+    "bitlinear_forward3_workspace_bytes": ([_I64, _I64, _I64], _SZ),
+    "bitlinear_forward3": ([_P, _P, _P, _F, _I64, _I64, _I64, _P, _P, _P, _SZ, _P], ctypes.c_int),
     "bitlinear_grouped_table_bytes": ([ctypes.POINTER(BitLinearProblem), _I32, _I64], _SZ),
     "bitlinear_grouped_plan_init": ([ctypes.POINTER(BitLinearProblem), _I32, _I64, _P, _SZ,
                                      ctypes.POINTER(BitLinearGroupedPlan), _P], ctypes.c_int),
@@ -271,6 +273,16 @@ def bitlinear_forward_lut(xq, eta, packed, fmt: int, gamma: float, M: int, N: in
     _check(_lib.bitlinear_forward_lut(_ptr(xq), _ptr(eta), _ptr(packed), int(fmt), float(gamma),
                                       M, N, K, _ptr(y), _ptr(y_int), _ptr(ws), ws_bytes,
                                       _stream(stream)), "bitlinear_forward_lut")
+
+
+def bitlinear_forward3_workspace_bytes(M: int, N: int, K: int) -> int:
+    return _lib.bitlinear_forward3_workspace_bytes(M, N, K)
+
+
+def bitlinear_forward3(xq, eta, packed3, gamma: float, M: int, N: int, K: int, y, y_int=None,
+                       ws=None, ws_bytes: int = 0, stream=None) -> None:
+    _check(_lib.bitlinear_forward3(_ptr(xq), _ptr(eta), _ptr(packed3), float(gamma), M, N, K, _ptr(y),
+                                   _ptr(y_int), _ptr(ws), ws_bytes, _stream(stream)), "bitlinear_forward3")
 
 
 def make_problems(specs: Sequence[dict]):

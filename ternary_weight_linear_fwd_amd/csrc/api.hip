@@ -560,6 +560,26 @@ int bitlinear_forward_lut(const int8_t* xq, const float* eta, const uint8_t* pac
     return launch_lut(p, M, format, ws, (hipStream_t)stream);
 }
 
+size_t bitlinear_forward3_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (check_sizes(M, N, K) != BITLINEAR_OK) return 0;
+    return align256(base3_ws_bytes(M, N, K));
+}
+
+int bitlinear_forward3(const int8_t* xq, const float* eta, const uint8_t* packed3, float gamma,
+                       int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,
+                       size_t ws_bytes, void* stream) {
+    int rc = check_sizes(M, N, K);
+    if (rc) return rc;
+    if (!xq || !eta || !packed3 || !y) return BITLINEAR_EINVAL;
+    if (!aligned(xq, 16) || !aligned(packed3, 16)) return BITLINEAR_EINVAL;
+    const size_t need = base3_ws_bytes(M, N, K);
+    if (need && (!ws || !aligned(ws, 256) || ws_bytes < need)) return BITLINEAR_EWORKSPACE;
+    if (M == 0) return BITLINEAR_OK;
+    clear_hip_error();
+    Problem p = make_problem(xq, eta, packed3, gamma, N, K, y, y_int);
+    return launch_base3(p, M, ws, (hipStream_t)stream);
+}
+
 int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
                       int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,
                       size_t ws_bytes, void* stream) {

@@ -3,10 +3,13 @@
 // Base-3 format.  [P2] (bandwidth paragraph before "Scaling Laws and
 // Empirical Benchmarks": 1.58 bits per weight under compact ternary packing,
 // 2 bits otherwise) and [P3] "Common Misconceptions" (log2(3) bits of
-// information per weight).  Five weights per byte: digit d = w + 1, byte value
-// sum_j d_j 3^j <= 242, 1.6 bits per weight.  Device layout: 64-row groups x
-// blocks of 80 k; a block is 1024 bytes, 16 per row, and byte p of a row holds
-// k = 80b + 5p + j at 3^j (rows past N and k past K hold digit 1).
+// information per weight).  Five weights per byte: digit d = w + 1, canonical
+// value v = sum_j d_j 3^j <= 242, 1.6 bits per weight.  Device layout: 64-row
+// groups x blocks of 80 k; a block is 1024 bytes, 16 per row, and byte p of a
+// row holds k = 80b + 5p + j at 3^j (rows past N and k past K hold digit 1).
+// The stored byte is the fraction form q = ceil(256 v / 243), a bijection of
+// 0..242 onto 243 of the 256 byte values with v = floor(243 q / 256), from
+// which the matrix-core decode takes digits by multiplying by 3 (base3.hip).
 //
 // Lookup-table contraction.  [P3] "What Most People Miss" (precompute every
 // possible outcome of a small block of int8 activations against ternary
@@ -45,14 +48,15 @@ __device__ inline Pos3 pos3(int64_t i, int64_t Kb3) {
     return {g * 64 + r, b * kBase3BlockK + q * 20};
 }
 
-// Four base-3 bytes from 20 digits (byte c holds digits 5c .. 5c + 4).
+// Four base-3 bytes from 20 digits (byte c holds digits 5c .. 5c + 4), each
+// in the fraction form.
 __device__ inline uint32_t pack3_dword(const uint32_t (&d)[20]) {
     uint32_t word = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const uint32_t v = d[5 * c] + 3 * d[5 * c + 1] + 9 * d[5 * c + 2] + 27 * d[5 * c + 3] +
                            81 * d[5 * c + 4];
-        word |= v << (8 * c);
+        word |= base3_fraction_byte(v) << (8 * c);
     }
     return word;
 }
@@ -111,10 +115,11 @@ __global__ __launch_bounds__(256) void unpack3_kernel(const uint32_t* __restrict
     int nbad = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        uint32_t v = (word >> (8 * c)) & 0xffu;
+        const uint32_t q = (word >> (8 * c)) & 0xffu;
+        uint32_t v = base3_canonical_byte(q);
         const int64_t kc = p.k0 + 5 * c;
         if (kc >= K) break;
-        const bool ok = v < 243u;
+        const bool ok = base3_fraction_byte(v) == q;   // 13 byte values are no fraction form
         nbad += !ok;
         if (!ok) v = 121u;   // decoded as zero weights
 #pragma unroll
@@ -182,7 +187,7 @@ template <>
 struct LutFmt<kFormatBase3> {
     static constexpr int BK = 80;
     static constexpr int RUN = 9;     // entries per run: the two low digits
-    static constexpr int RUNS = 27;   // runs per table (243 entries; 243..255 stay 0)
+    static constexpr int RUNS = 27;   // runs per table (243 entries at their stored bytes; 13 stay 0)
     __device__ static int k_of(int p, int j) { return 5 * p + j; }
 };
 
@@ -207,20 +212,23 @@ __device__ inline void build_tables(int16_t (*tab)[16][256], const int (*xs)[80]
         const int p = rest / F::RUNS, u = rest - p * F::RUNS;
         const int x0 = xs[mm][F::k_of(p, 0)], x1 = xs[mm][F::k_of(p, 1)];
         const int x2 = xs[mm][F::k_of(p, 2)], x3 = xs[mm][F::k_of(p, 3)];
-        int16_t* t = &tab[mm][p][u * F::RUN];
         if constexpr (FMT == kFormatBase3) {
             const int x4 = xs[mm][F::k_of(p, 4)];
-            // entry 9u + 3 d1 + d0: high digits from u, low digits counting up
+            // canonical value 9u + 3 d1 + d0: high digits from u, low digits
+            // counting up; the entry sits at its stored (fraction-form) byte
             const int d2 = u % 3, d3 = (u / 3) % 3, d4 = u / 9;
             const int base = (d2 - 1) * x2 + (d3 - 1) * x3 + (d4 - 1) * x4 - x0 - x1;
+            int16_t* tb = &tab[mm][p][0];
 #pragma unroll
             for (int d1 = 0; d1 < 3; ++d1)
 #pragma unroll
-                for (int d0 = 0; d0 < 3; ++d0) t[3 * d1 + d0] = (int16_t)(base + d1 * x1 + d0 * x0);
+                for (int d0 = 0; d0 < 3; ++d0)
+                    tb[base3_fraction_byte(9u * u + 3u * d1 + d0)] = (int16_t)(base + d1 * x1 + d0 * x0);
         } else {
             // entry 16u + 4 f1 + f0: fields 2 and 3 from u; field 3 (never
             // produced) only needs a bounded value
             const int f2 = u & 3, f3 = u >> 2;
+            int16_t* t = &tab[mm][p][u * F::RUN];
             const int base = (f2 - 1) * x2 + (f3 - 1) * x3 - x0 - x1;
 #pragma unroll
             for (int f1 = 0; f1 < 4; ++f1)
@@ -244,11 +252,12 @@ __global__ __launch_bounds__(256) void lut_gemv_kernel(LutArgs a) {
     if (kb1 > a.Kb) kb1 = a.Kb;
     const uint4* packed = p.packed;
 
-    // Entries past 242 of a base-3 table are never written by the builder.
+    // The 13 entries of a base-3 table at bytes that are no fraction form
+    // are never written by the builder.
     if constexpr (FMT == kFormatBase3)
-        for (int i = t; i < MC * 16 * 13; i += 256) {
-            const int mm = i / (16 * 13), r = i - mm * 16 * 13;
-            tab[mm][r / 13][243 + r % 13] = 0;
+        for (int i = t; i < MC * 16 * 256; i += 256) {
+            const uint32_t q = (uint32_t)i & 255u;
+            if (base3_fraction_byte(base3_canonical_byte(q)) != q) tab[i >> 12][(i >> 8) & 15][q] = 0;
         }
 
     int64_t g_of[RW];

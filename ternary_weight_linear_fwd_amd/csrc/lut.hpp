@@ -1,5 +1,6 @@
 // lut.hpp -- compact base-3 weight format and the lookup-table decode
-// contraction (lut.hip).
+// contraction (lut.hip); the matrix-core decode of the base-3 layout
+// (base3.hip).
 #pragma once
 #include "kernels.hpp"
 
@@ -10,8 +11,11 @@ constexpr int kFormat2Bit = 0;   // the 2-bit device layout
 constexpr int kFormatBase3 = 1;  // the base-3 device layout
 
 // Base-3 device layout: 64-row groups x blocks of 80 k, 1024 bytes per block
-// (16 bytes per row; byte p holds k = 80b + 5p + j as the base-3 digit of 3^j).
+// (16 bytes per row; byte p holds k = 80b + 5p + j as the base-3 digit of 3^j
+// of v, stored in the fraction form q = ceil(256 v / 243)).
 constexpr int kBase3BlockK = 80;
+__host__ __device__ inline uint32_t base3_fraction_byte(uint32_t v) { return (256u * v + 242u) / 243u; }
+__host__ __device__ inline uint32_t base3_canonical_byte(uint32_t q) { return (243u * q) >> 8; }
 size_t packed3_bytes(int64_t N, int64_t K);
 
 int launch_pack_weights3(const float* W, int64_t N, int64_t K, uint8_t* packed3, float* gamma_dev,
@@ -25,5 +29,12 @@ int launch_unpack3(const uint8_t* packed3, int64_t N, int64_t K, int8_t* Wt, int
 size_t lut_ws_bytes(int64_t M, int64_t N, int64_t K, int format);
 // p.packed points at the format's device layout; p.Kb is ignored.
 int launch_lut(const Problem& p, int64_t M, int format, void* ws, hipStream_t stream);
+
+// Matrix-core contraction of the base-3 layout (base3.hip): up to
+// kBase3MaxTokens tokens per pass over the weights; split-K partial sums in
+// the workspace.
+constexpr int kBase3MaxTokens = 8;
+size_t base3_ws_bytes(int64_t M, int64_t N, int64_t K);
+int launch_base3(const Problem& p, int64_t M, void* ws, hipStream_t stream);
 
 }  // namespace bl

@@ -198,6 +198,30 @@ def test_noalloc_validation():
     assert _rc("bitlinear_forward_f32_noalloc", FAKE, FAKE, f1, 0, 64, 64, FAKE, None) == L.BITLINEAR_OK
 
 
+def test_forward3_validation_and_workspace():
+    """The base-3 forward checks its arguments before any device work; its
+    workspace holds the K-split partial sums ([S][M][N] int32) or nothing."""
+    L = bl
+    f1 = ctypes.c_float(1.0)
+    assert _rc("bitlinear_forward3", FAKE, FAKE, FAKE, f1, 1, 64, 64, None, None, None, 0, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward3", FAKE + 4, FAKE, FAKE, f1, 1, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward3", FAKE, FAKE, FAKE + 8, f1, 1, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
+    assert _rc("bitlinear_forward3", FAKE, FAKE, FAKE, f1, 1, 64, 40, FAKE, None, None, 0, None) == L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_forward3", FAKE, FAKE, FAKE, f1, 1, 64, L.BITLINEAR_MAX_K + 16, FAKE, None, None, 0,
+               None) == L.BITLINEAR_EUNSUPPORTED
+    assert _rc("bitlinear_forward3", FAKE, FAKE, FAKE, f1, 0, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_OK
+    for M, N, K in ((1, 28672, 8192), (1, 8192, 28672), (8, 8192, 28672), (20, 3200, 8640)):
+        need = L.bitlinear_forward3_workspace_bytes(M, N, K)
+        assert need % 256 == 0 and need >= 2 * 4 * M * N          # at least two K-slices
+        assert _rc("bitlinear_forward3", FAKE, FAKE, FAKE, f1, M, N, K, FAKE, None, FAKE, need - 256,
+                   None) == L.BITLINEAR_EWORKSPACE
+        assert _rc("bitlinear_forward3", FAKE, FAKE, FAKE, f1, M, N, K, FAKE, None, FAKE + 16, need,
+                   None) == L.BITLINEAR_EWORKSPACE
+    # one slice (no workspace) when K is short and N alone fills the chip
+    assert L.bitlinear_forward3_workspace_bytes(1, 131072, 160) == 0
+    assert L.bitlinear_forward3_workspace_bytes(1, 64, 40) == 0      # invalid sizes: 0
+
+
 def test_grouped_planner_validation():
     def probs(n, **over):
         specs = []

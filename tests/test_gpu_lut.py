@@ -1,6 +1,6 @@
 """GPU parity: the compact base-3 weight format (device layout, packing,
-unpacking) and the lookup-table contraction over both weight formats,
-bit-exact against the oracle."""
+unpacking), the lookup-table contraction over both weight formats and the
+matrix-core contraction of the base-3 layout, bit-exact against the oracle."""
 import numpy as np
 import pytest
 
@@ -11,14 +11,20 @@ from ternary_weight_linear_fwd_amd import synthetic as S
 pytestmark = pytest.mark.gpu
 
 
+def fraction_form(v):
+    """The stored form of a canonical base-3 byte v: ceil(256 v / 243)."""
+    return ((256 * np.asarray(v, np.int64) + 242) // 243).astype(np.uint8)
+
+
 def device_layout3(canon: np.ndarray, N: int, K: int) -> np.ndarray:
     """The documented base-3 device layout, built on the host from the oracle's
     canonical bytes: block (g, b) holds 16 bytes per row, byte p of row r being
-    canonical byte 16b + p of row 64g + r; everything else is weight 0."""
+    the fraction form of canonical byte 16b + p of row 64g + r; everything
+    else is weight 0 (canonical 121)."""
     G, Kb3 = -(-N // 64), -(-K // 80)
     out = np.full((G * 64, Kb3 * 16), 121, np.uint8)
     out[:N, :canon.shape[1]] = canon
-    return out.reshape(G, 64, Kb3, 16).transpose(0, 2, 1, 3).ravel()
+    return fraction_form(out.reshape(G, 64, Kb3, 16).transpose(0, 2, 1, 3).ravel())
 
 
 def pack3_ternary(Wt: np.ndarray):
@@ -68,13 +74,18 @@ def test_base3_bad_inputs():
     fixed[69, 159] = 0
     back, bad = unpack3(packed, N, K)
     assert bad == 0 and np.array_equal(back, fixed)
-    # an out-of-range byte inside the matrix decodes as zero weights and is counted
+    # a byte that is no fraction form inside the matrix decodes as zero
+    # weights and is counted; every other byte value decodes
     raw = packed.cpu().numpy()
-    raw[16 * 5 + 2] = 250          # row 5, block 0, byte 2: k = 10..14
+    raw[16 * 5 + 2] = 237          # row 5, block 0, byte 2: k = 10..14
+    raw[16 * 6 + 3] = 1            # row 6, block 0, byte 3: k = 15..19
     back, bad = unpack3(to_dev(raw), N, K)
-    assert bad == 1
+    assert bad == 2
     fixed[5, 10:15] = 0
+    fixed[6, 15:20] = 0
     assert np.array_equal(back, fixed)
+    valid = set(fraction_form(np.arange(243)).tolist())
+    assert sorted(set(range(256)) - valid) == [1, 20, 40, 60, 79, 99, 119, 138, 158, 178, 197, 217, 237]
 
 
 def test_pack_weights3_latent():
@@ -154,3 +165,79 @@ def test_lut_extreme_activations():
                         (L.BITLINEAR_FORMAT_BASE3, pack3_ternary(Wt)[0])):
         y, yi = forward_lut(xq, eta, packed, fmt, np.float32(0.5), N)
         assert np.array_equal(yi, yi_ref) and np.array_equal(y, y_ref)
+
+
+# ---------------------------------------------------------------- base-3 forward
+def forward3(xq, eta, packed3, gamma, N):
+    torch = torch_cuda()
+    L = bl()
+    M, K = xq.shape
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    y_int = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    ws_bytes = L.bitlinear_forward3_workspace_bytes(M, N, K)
+    ws = empty(ws_bytes)
+    L.bitlinear_forward3(to_dev(xq), to_dev(eta), packed3, float(gamma), M, N, K, y, y_int, ws, ws_bytes)
+    y_only = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    L.bitlinear_forward3(to_dev(xq), to_dev(eta), packed3, float(gamma), M, N, K, y_only, None, ws, ws_bytes)
+    torch.cuda.synchronize()
+    y, y_only = y.cpu().numpy(), y_only.cpu().numpy()
+    assert np.array_equal(y.view(np.uint32), y_only.view(np.uint32))
+    return y, y_int.cpu().numpy()
+
+
+def check_forward3(M, N, K, seed, dist="normal", xq=None, eta=None, Wt=None):
+    if xq is None:
+        xq, eta = oracle.quantize_act(S.random_x(seed, M, K, dist))
+    if Wt is None:
+        Wt = S.random_ternary(seed + 1, N, K)
+    gamma = np.float32(0.0173)
+    say(f"forward3 M={M} N={N} K={K} seed={seed}")
+    y_ref, yi_ref = oracle.forward_q(xq, eta, Wt, gamma, threads=8)
+    p3, bad = pack3_ternary(Wt)
+    assert bad == 0
+    y, yi = forward3(xq, eta, p3, gamma, N)
+    assert np.array_equal(yi, yi_ref), np.argwhere(yi != yi_ref)[:5]
+    assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 9, 17])
+def test_forward3_token_counts(M):
+    # up to 8 tokens per pass over the weights; 9 and 17 take two and three
+    check_forward3(M, 300, 1040, seed=1300 + M)
+
+
+@pytest.mark.parametrize("N,K", [(1, 16), (63, 80), (64, 96), (65, 160), (255, 320), (257, 1040),
+                                 (1000, 4160), (2049, 336), (4100, 8208), (300, 30000)])
+def test_forward3_shapes(N, K):
+    check_forward3(1, N, K, seed=1500 + N + K)
+
+
+def test_forward3_config_shapes():
+    # decode projections of the 3B and 70B shapes at one token (heavy-tailed
+    # activations), and the 70B pair at 8 tokens
+    for K, N in ((3200, 8640), (8640, 3200), (8192, 28672), (28672, 8192)):
+        check_forward3(1, N, K, seed=K + N, dist="t3")
+    for K, N in ((8192, 28672), (28672, 8192)):
+        check_forward3(8, N, K, seed=abs(K - N))
+
+
+def test_forward3_extremes():
+    # int8 extremes including -128 against all-(+1), all-(-1) and mixed rows:
+    # the T_5 - 128 byte, the modular combination and the X5 correction at
+    # their limits
+    M, N, K = 8, 192, 2000
+    rng = np.random.default_rng(9)
+    xq = rng.choice(np.array([-128, -127, 127, 0], np.int8), size=(M, K))
+    xq[0] = -128
+    xq[1] = 127
+    eta = np.linspace(0.5, 4.0, M).astype(np.float32)
+    Wt = S.random_ternary(10, N, K)
+    Wt[0] = 1
+    Wt[1] = -1
+    Wt[2] = 0
+    check_forward3(M, N, K, seed=0, xq=xq, eta=eta, Wt=Wt)
+
+
+def test_forward3_long_k():
+    # K far past the workloads: several K-slices of the maximum slice length
+    check_forward3(2, 70, 200000, seed=77)
