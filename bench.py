@@ -109,7 +109,7 @@ def time_graph(torch, call, count: int, replays: int = 10) -> float:
     return ms
 
 
-def contraction_only_plan(sw, M):
+def contraction_only_plan(sw, M, fmt="2bit"):
     """A plan over the same problems whose activations are already quantized
     (x = NULL): forward then launches the contraction kernel alone."""
     L, torch = sw.L, sw.torch
@@ -118,13 +118,44 @@ def contraction_only_plan(sw, M):
         for p in sw.projs:
             key = (layer, p.name, M)
             specs.append(dict(x=None, xq=sw.xq[key], eta=sw.eta[key],
-                              packed=sw.packed[(layer, p.name)], y=sw.y[key],
-                              gamma=sw.gamma[(layer, p.name)], N=p.N, K=p.K))
+                              packed=sw.packed[(fmt, layer, p.name)], y=sw.y[key],
+                              gamma=sw.gamma[(layer, p.name)], N=p.N, K=p.K,
+                              format=L.BITLINEAR_FORMAT_2BIT if fmt == "2bit" else L.BITLINEAR_FORMAT_BASE3))
     probs = L.make_problems(specs)
     tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
     table = torch.empty(tb, dtype=torch.uint8, device="cuda")
     plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
     return plan, table
+
+
+def bench_decode_base3(torch, sw, steps: int):
+    """The 70B-shaped decode step (one grouped forward over all 560
+    projections) with the weights in the base-3 layout (13.7 GB, 1.6 bits per
+    weight) next to the same step in the 2-bit layout (17.1 GB), at each
+    token count both are planned for; the contraction kernel alone too."""
+    out = []
+    for M in sw.Ms["base3"]:
+        row = {"M": M}
+        for fmt in ("2bit", "base3"):
+            if (fmt, M) not in sw.plans:
+                continue
+            for _ in range(2):
+                sw.step(M, fmt=fmt)
+            ms = time_events(torch, lambda: sw.step(M, fmt=fmt), max(5, steps // 2))
+            plan_c, _table = contraction_only_plan(sw, M, fmt)
+            sw.L.bitlinear_forward_grouped(plan_c)
+            kern = time_events(torch, lambda: sw.L.bitlinear_forward_grouped(plan_c), max(5, steps // 2))
+            del plan_c, _table
+            gbs = sw.algorithmic_bytes(M, fmt) / (ms * 1e-3) / 1e9
+            kgbs = sw.contraction_bytes(M, fmt) / (kern * 1e-3) / 1e9
+            row[fmt] = {"ms_per_step": round(ms, 4), "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "contraction_ms": round(kern, 4), "contraction_gbs": round(kgbs, 1),
+                        "contraction_frac": round(kgbs / HBM_PEAK_GBS, 4),
+                        "weight_bytes": sw.weight_bytes(fmt)}
+        if "2bit" in row and "base3" in row:
+            row["base3_over_2bit"] = round(row["base3"]["ms_per_step"] / row["2bit"]["ms_per_step"], 3)
+        out.append(row)
+    return out
 
 
 def bench_prefill(torch, L, S, reps: int):
@@ -725,6 +756,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-m16", action="store_true")
+    ap.add_argument("--no-base3", action="store_true", help="skip the base-3 layout of the 70B sweep")
     ap.add_argument("--profile-m", type=int, default=1, choices=(1, 16),
                     help="token count of the --profile-run sweep")
     ap.add_argument("--profile-run", action="store_true",
@@ -788,8 +820,12 @@ def main() -> int:
         for r in prefill:
             log(f"prefill {r['gemm']}: {r['us']} us, {r['tops']} TOP/s ({r['frac']:.1%}); "
                 f"own row sums {r['us_own_row_sums']} us; quantize {r['quantize_us']} us")
-    sw = DecodeSweep(layers=args.layers, Ms=Ms, progress=log)
-    log(f"packed weights resident: {sw.weight_bytes() / 1e9:.3f} GB")
+    formats = ("2bit",) if args.profile_run or args.no_base3 else ("2bit", "base3")
+    base3_Ms = (1, 8) if not args.profile_run else ()
+    if not args.profile_run and not args.no_base3:
+        Ms = tuple(sorted(set(Ms) | {8}))   # the 2-bit step at 8 tokens, beside base-3's
+    sw = DecodeSweep(layers=args.layers, Ms=Ms, progress=log, formats=formats, base3_Ms=base3_Ms)
+    log(f"packed weights resident: {sum(sw.weight_bytes(f) for f in formats) / 1e9:.3f} GB ({', '.join(formats)})")
     if args.profile_run:
         return profile_run(torch, L, sw, args)
 
@@ -828,6 +864,14 @@ def main() -> int:
                                "unit": "GB/s", "frac": round(gbs16 / HBM_PEAK_GBS, 4),
                                "tops": round(sw.ops(16) / (ms16 * 1e-3) / 1e12, 1)}
         log(f"M=16 step: {ms16:.3f} ms, {gbs16:.1f} GB/s")
+
+    if "base3" in sw.formats:
+        extra["decode_base3"] = bench_decode_base3(torch, sw, args.steps)
+        for r in extra["decode_base3"]:
+            log(f"70B decode step M={r['M']}: " + "; ".join(
+                f"{f} {r[f]['ms_per_step']} ms ({r[f]['gbs']} GB/s, {r[f]['frac']:.1%}; contraction "
+                f"{r[f]['contraction_ms']} ms, {r[f]['contraction_frac']:.1%})" for f in ("2bit", "base3") if f in r)
+                + (f"; base-3 / 2-bit {r['base3_over_2bit']}" if "base3_over_2bit" in r else ""))
 
     if prefill is not None:
         extra["prefill"] = prefill

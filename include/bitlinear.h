@@ -339,18 +339,23 @@ int bitlinear_forward3(const int8_t* xq, const float* eta, const uint8_t* packed
  * to two tokens too small to fill the chip (one transformer block, say), with
  * every K at most 16384, queues one kernel that quantizes, contracts and
  * dequantizes; it writes xq and eta of problems with x != NULL all the same.
+ * A plan of base-3 problems (format BITLINEAR_FORMAT_BASE3, up to 8 tokens)
+ * contracts on the base-3 matrix-core kernel of bitlinear_forward3, with the
+ * same results.
  */
 typedef struct bitlinear_problem {
     const float* x;        /* [M][K] float32, or NULL: xq/eta already hold the quantized rows */
     int8_t* xq;            /* [M][K] int8: written by the quantize stage when x != NULL */
     float* eta;            /* [M] float32: likewise */
-    const uint8_t* packed; /* device layout of the [N][K] ternary matrix */
+    const uint8_t* packed; /* the [N][K] ternary matrix in the layout `format` names */
     float* y;              /* [M][N] float32 output */
     int32_t* y_int;        /* [M][N] int32 output or NULL */
     float gamma;           /* the matrix's scale */
     int32_t N;
     int32_t K;
-    int32_t reserved;      /* must be 0 */
+    int32_t format;        /* layout of packed: BITLINEAR_FORMAT_2BIT (0, the device layout) or
+                              BITLINEAR_FORMAT_BASE3 (1, the base-3 layout, up to 8 tokens);
+                              one format for every problem of a plan */
 } bitlinear_problem;
 
 /* Host-side handle of a plan; plain data owned by the caller. */
@@ -369,7 +374,8 @@ typedef struct bitlinear_grouped_plan {
  * whose work units would leave CUs idle (a single transformer block, say) may
  * split their K loops, and the table then also holds the int32 partial sums:
  * M x 64 x 4 bytes per work unit of the dot4 decode path (up to 4 tokens),
- * M x 256 x 4 bytes per unit past 4 tokens. */
+ * M x 256 x 4 bytes per unit past 4 tokens and of base-3 plans (whose K
+ * loops also split where one would not fit the kernel's LDS). */
 size_t bitlinear_grouped_table_bytes(const bitlinear_problem* problems_host, int32_t count,
                                      int64_t M);
 

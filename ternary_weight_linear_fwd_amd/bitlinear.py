@@ -47,7 +47,7 @@ _F = ctypes.c_float
 class BitLinearProblem(ctypes.Structure):
     """Mirror of ``bitlinear_problem``."""
     _fields_ = [("x", _P), ("xq", _P), ("eta", _P), ("packed", _P), ("y", _P), ("y_int", _P),
-                ("gamma", _F), ("N", _I32), ("K", _I32), ("reserved", _I32)]
+                ("gamma", _F), ("N", _I32), ("K", _I32), ("format", _I32)]
 
 
 class BitLinearGroupedPlan(ctypes.Structure):
@@ -298,7 +298,7 @@ def make_problems(specs: Sequence[dict]):
         arr[i].gamma = float(s["gamma"])
         arr[i].N = int(s["N"])
         arr[i].K = int(s["K"])
-        arr[i].reserved = 0
+        arr[i].format = int(s.get("format", BITLINEAR_FORMAT_2BIT))
     return arr
 
 

@@ -127,9 +127,11 @@ F32Ws f32_ws(int64_t M, int64_t N, int64_t K) {
 // (64 x 256 tiles) with K split (split plans: partials in the table, then an
 // epilogue), 5 prefill MFMA (64 x 256 tiles), 6 dot4 GEMV with K split,
 // 7 fused dot4 GEMV (quantize + contract + dequant in one launch, whole K
-// per workgroup; no quantize stage).
+// per workgroup; no quantize stage), 8 base-3 matrix-core decode over
+// 256-row blocks, 9 the same with K split.
 constexpr int32_t kPlanGemv = 0, kPlanGemm = 1, kPlanSkinny = 2, kPlanSkinnySplit = 3, kPlanGemmSplit = 4,
-                  kPlanGemmSmall = 5, kPlanGemvSplit = 6, kPlanGemvFused = 7, kPlanLast = 7;
+                  kPlanGemmSmall = 5, kPlanGemvSplit = 6, kPlanGemvFused = 7, kPlanBase3 = 8,
+                  kPlanBase3Split = 9, kPlanLast = 9;
 
 struct TableLayout {
     size_t problems_off, units_off, rows_off, part_off, bytes;
@@ -144,7 +146,9 @@ TableLayout table_layout(int64_t count, int64_t nunits, int64_t nrows, int32_t k
     t.rows_off = t.units_off + align256((size_t)nunits * sizeof(Unit));
     t.part_off = t.rows_off + align256((size_t)nrows * sizeof(QuantRow));
     const size_t width = kernel == kPlanGemvSplit ? 64   // output rows per work unit
-                         : (kernel == kPlanSkinnySplit || kernel == kPlanGemmSplit) ? kSkinnyRows : 0;
+                         : (kernel == kPlanSkinnySplit || kernel == kPlanGemmSplit || kernel == kPlanBase3Split)
+                             ? kSkinnyRows
+                             : 0;
     const size_t part = (size_t)nunits * (size_t)M * width * sizeof(int32_t);
     t.bytes = t.part_off + align256(part);
     return t;
@@ -154,7 +158,7 @@ TableLayout table_layout(int64_t count, int64_t nunits, int64_t nrows, int32_t k
 int64_t problem_units(int32_t kernel, int64_t M, int64_t N) {
     if (kernel == kPlanGemv || kernel == kPlanGemvFused) return ceil_div(N, 64);   // per 64-row group
     if (kernel == kPlanGemm) return ceil_div(N, gemm_tile_n(M));
-    return ceil_div(N, kSkinnyRows);                   // one workgroup per 256 rows
+    return ceil_div(N, kSkinnyRows);                   // one workgroup per 256 rows (skinny, base-3)
 }
 
 int32_t plan_kernel(int64_t M) {
@@ -270,6 +274,38 @@ bool choose_gemv_slices(std::vector<Problem>& problems) {
     return any;
 }
 
+// K-slices for a grouped base-3 plan.  Every slice fits the kernel's LDS
+// arrangement (base3_max_slice_kb); plans whose 256-row blocks number fewer
+// than kBase3GroupedUnits (one transformer block, say) are cut further into
+// slices of about equal length aiming at that many work units, at least
+// kBase3SplitMinKb blocks of 80 k each.
+constexpr int64_t kBase3GroupedUnits = 768;
+constexpr int64_t kBase3SplitMinKb = 8;
+
+bool choose_base3_slices(std::vector<Problem>& problems, int64_t M) {
+    const int64_t mc = M < 1 ? 1 : (M > kBase3MaxTokens ? kBase3MaxTokens : M);
+    const int64_t max_kb = base3_max_slice_kb(mc);
+    int64_t blocks = 0, work = 0;   // work: 256-row blocks x 80-k blocks
+    for (const Problem& p : problems) {
+        blocks += ceil_div(p.N, kSkinnyRows);
+        work += ceil_div(p.N, kSkinnyRows) * p.Kb;
+    }
+    int64_t len = max_kb;
+    if (blocks < kBase3GroupedUnits) {
+        len = ceil_div(work, kBase3GroupedUnits);
+        if (len < kBase3SplitMinKb) len = kBase3SplitMinKb;
+        if (len > max_kb) len = max_kb;
+    }
+    bool any = false;
+    for (Problem& p : problems) {
+        int64_t S = ceil_div(p.Kb, len);
+        while (S > 1 && (S - 1) * ceil_div(p.Kb, S) >= p.Kb) --S;   // no empty slice
+        p.slices = (int32_t)(S < 1 ? 1 : S);
+        any = any || p.slices > 1;
+    }
+    return any;
+}
+
 struct PlanHost {
     std::vector<Problem> problems;
     std::vector<Unit> units;
@@ -282,7 +318,8 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
     std::map<const int8_t*, const float*> xq_source;  // xq buffer -> its x
     for (int32_t i = 0; i < count; ++i) {
         const bitlinear_problem& q = pr[i];
-        if (q.reserved != 0) return BITLINEAR_EINVAL;
+        if (q.format != kFormat2Bit && q.format != kFormatBase3) return BITLINEAR_EINVAL;
+        if (q.format != pr[0].format) return BITLINEAR_EINVAL;   // one layout per plan
         int rc = check_sizes(M, q.N, q.K);
         if (rc) return rc;
         if (!q.packed || !q.y || !q.xq || !q.eta) return BITLINEAR_EINVAL;
@@ -306,7 +343,13 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
         }
         out.problems.push_back(make_problem(q.xq, q.eta, q.packed, q.gamma, q.N, q.K, q.y, q.y_int, q.x));
     }
-    out.kernel = plan_kernel(M);
+    if (pr[0].format == kFormatBase3) {
+        if (M > kBase3MaxTokens) return BITLINEAR_EUNSUPPORTED;
+        for (Problem& p : out.problems) p.Kb = (int32_t)ceil_div(p.K, kBase3BlockK);
+        out.kernel = choose_base3_slices(out.problems, M) ? kPlanBase3Split : kPlanBase3;
+    } else {
+        out.kernel = plan_kernel(M);
+    }
     if (out.kernel == kPlanGemv && fused_gemv_plan(out.problems, M)) {
         out.kernel = kPlanGemvFused;
         out.rows.clear();   // each workgroup quantizes its problem's rows itself
@@ -340,6 +383,7 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
         const int32_t k = out.kernel == kPlanSkinnySplit ? kPlanSkinny
                           : (out.kernel == kPlanGemmSplit || out.kernel == kPlanGemmSmall) ? kPlanGemm
                           : out.kernel == kPlanGemvSplit                                  ? kPlanGemv
+                          : out.kernel == kPlanBase3Split                                 ? kPlanBase3
                                                                                           : out.kernel;
         const int64_t nu = problem_units(k, M, p.N);
         for (int64_t g = 0; g < nu; ++g)
@@ -726,6 +770,17 @@ int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) 
             return launch_gemm_grouped(problems, units, plan->units, plan->M, true,
                                        reinterpret_cast<int32_t*>(static_cast<char*>(plan->table) + L.part_off), s);
         case kPlanGemmSmall: return launch_gemm_grouped(problems, units, plan->units, plan->M, true, nullptr, s);
+        case kPlanBase3:
+        case kPlanBase3Split: {
+            // no slice is longer than the longest K or than the LDS arrangement allows
+            int64_t max_kb = base3_max_slice_kb(plan->M);
+            if (ceil_div(plan->max_K, kBase3BlockK) < max_kb) max_kb = ceil_div(plan->max_K, kBase3BlockK);
+            return launch_base3_grouped(problems, units, plan->units, plan->M, max_kb,
+                                        plan->kernel == kPlanBase3Split
+                                            ? reinterpret_cast<int32_t*>(static_cast<char*>(plan->table) + L.part_off)
+                                            : nullptr,
+                                        s);
+        }
         default: return launch_gemm_grouped(problems, units, plan->units, plan->M, false, nullptr, s);
     }
 }

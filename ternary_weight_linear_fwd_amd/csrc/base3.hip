@@ -58,8 +58,11 @@ constexpr int kB3Depth = 2;                    // K-steps of weights in flight p
 constexpr int kB3XLoads = 4;                   // 16-byte activation loads per thread: 16 KB per slice
 
 struct B3Args {
-    Problem p;          // p.packed: base-3 layout; p.xq, p.eta: all tokens
-    int32_t* partial;   // [S][M][N] int32 when S > 1
+    Problem p;          // single problem: p.packed: base-3 layout; p.xq, p.eta: all tokens
+    int32_t* partial;   // single problem: [S][M][N] int32 when S > 1
+    const Problem* problems;   // grouped: p.Kb = 80-k blocks, p.slices K-slices per 256-row block
+    const Unit* units;         // grouped: (problem, 256-row block), K-slices adjacent
+    int32_t* gpart;            // grouped, K split: [unit][M][256] int32 partial sums
     int64_t M;          // all tokens
     int32_t m0, mc;     // this pass: tokens m0 .. m0 + mc - 1 (mc <= kBase3MaxTokens)
     int32_t Kb3;        // 80-k blocks along K
@@ -143,21 +146,43 @@ __device__ __forceinline__ void b3_load(uint4 (&w)[4], const uint8_t* wrow, int6
     for (int t = 0; t < 4; ++t) w[t] = ldnt_u4(src + t * 256);
 }
 
-template <int D>
+template <int D, bool GROUPED>
 __global__ __launch_bounds__(256, 2) void base3_mfma_kernel(B3Args a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int lane = t & 63, nl = lane & 15, lg = lane >> 4;
-    const Problem& p = a.p;
-    // Each XCD runs a contiguous run of the workgroups: neighbouring row
-    // blocks of one K-slice, which share its activations in L2.
+    // Each XCD runs a contiguous run of the workgroups: single problem,
+    // neighbouring row blocks of one K-slice, which share its activations in
+    // L2; grouped, neighbouring units of the table.
     const uint32_t wg = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int64_t rb = wg % (uint32_t)a.row_wgs, slice = wg / (uint32_t)a.row_wgs;
+    Problem p;
+    int64_t rb, slice, b0, b1, Kb3;
+    int nblk4;
+    uint32_t xmagic;
+    if constexpr (GROUPED) {
+        const Unit un = a.units[wg];
+        p = a.problems[un.problem];
+        rb = un.group;
+        slice = (int64_t)wg - p.unit_begin - rb * p.slices;
+        Kb3 = p.Kb;
+        const int64_t kbs = ceil_div(Kb3, p.slices);
+        b0 = slice * kbs;
+        b1 = b0 + kbs < Kb3 ? b0 + kbs : Kb3;
+        nblk4 = (int)ceil_div(kbs, 4) * 4;
+        xmagic = ((1u << 24) + (uint32_t)(nblk4 * 5) - 1u) / (uint32_t)(nblk4 * 5);
+    } else {
+        p = a.p;
+        rb = wg % (uint32_t)a.row_wgs;
+        slice = wg / (uint32_t)a.row_wgs;
+        Kb3 = a.Kb3;
+        b0 = slice * a.kb_per_slice;
+        b1 = b0 + a.kb_per_slice < Kb3 ? b0 + a.kb_per_slice : Kb3;
+        nblk4 = a.nblk4;
+        xmagic = a.xmagic;
+    }
     const int64_t N = p.N, K = p.K, G = ceil_div(N, 64);
-    const int64_t b0 = slice * a.kb_per_slice;
-    const int64_t b1 = b0 + a.kb_per_slice < a.Kb3 ? b0 + a.kb_per_slice : a.Kb3;
-    const int nblk = (int)(b1 - b0), nstep = (nblk + 3) / 4, nblk4 = a.nblk4;
+    const int nblk = (int)(b1 - b0), nstep = (nblk + 3) / 4;
     const int mc = a.mc;
 
     // LDS: A arrangement [mc][nblk4][6][2][16], zero area, sums [2][8] (X, X5), raw x [mc][nblk4 * 80].
@@ -178,13 +203,13 @@ __global__ __launch_bounds__(256, 2) void base3_mfma_kernel(B3Args a) {
 #pragma unroll
     for (int r = 0; r < kB3XLoads; ++r) {
         const int c = t + 256 * r;
-        const int m = (int)(((uint32_t)c * a.xmagic) >> 24), o = (c - m * (nblk4 * 5)) * 16;
+        const int m = (int)(((uint32_t)c * xmagic) >> 24), o = (c - m * (nblk4 * 5)) * 16;
         xin[r] = c < xch && o < nblk * kB3BlockX && b0 * kB3BlockX + o < K;
         xv[r] = ldnt_u4(p.xq + (xin[r] ? (int64_t)(a.m0 + m) * K + b0 * kB3BlockX + o : 0));
     }
     const int64_t g = rb * kB3Waves + wave;
     const bool group_ok = g < G;
-    const uint8_t* wrow = reinterpret_cast<const uint8_t*>(p.packed) + (group_ok ? g : G - 1) * a.Kb3 * 1024 + nl * 16;
+    const uint8_t* wrow = reinterpret_cast<const uint8_t*>(p.packed) + (group_ok ? g : G - 1) * Kb3 * 1024 + nl * 16;
     uint4 wb[D][4];
 #pragma unroll
     for (int i = 0; i < D; ++i) b3_load(wb[i], wrow, b0, b1, i, lg);
@@ -267,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void base3_mfma_kernel(B3Args a) {
 
     // Element r of tile t is A row 4 lg + r, column (output row) 16t + nl:
     // token 2 lg + r / 2, C0 for even r, C1 for odd r.
-    const bool split = a.S > 1;
+    const bool split = GROUPED ? p.slices > 1 : a.S > 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int m = 2 * lg + h;
@@ -281,7 +306,9 @@ __global__ __launch_bounds__(256, 2) void base3_mfma_kernel(B3Args a) {
             if (n >= N) continue;
             // modulo 2^32: the parts may exceed int32, the result does not
             const int v = (int)((uint32_t)acc[tt][2 * h] - 3u * (uint32_t)acc[tt][2 * h + 1] + 128u * X5 - X);
-            if (split) {
+            if (GROUPED && split) {
+                a.gpart[((int64_t)wg * a.M + mg) * kB3Rows + (n - rb * kB3Rows)] = v;
+            } else if (split) {
                 a.partial[(slice * a.M + mg) * N + n] = v;
             } else {
                 p.y[mg * N + n] = dequant(v, sc);
@@ -297,16 +324,25 @@ struct B3Plan {
     size_t lds;
 };
 
+int64_t base3_max_slice_kb(int64_t mc) {
+    const int64_t per_blk = mc * (kB3BlockLds + kB3BlockX);
+    int64_t max_kb = (kB3LdsBudget - kB3ZeroLds - 64) / per_blk / 4 * 4;
+    const int64_t max_kb_x = (int64_t)kB3XLoads * 256 * 16 / (mc * kB3BlockX) / 4 * 4;
+    if (max_kb > max_kb_x) max_kb = max_kb_x;   // the activation loads cover the slice
+    if (max_kb > 2048) max_kb = 2048;   // keeps every MFMA accumulator inside int32
+    return max_kb;
+}
+
+static size_t base3_lds_bytes(int64_t mc, int64_t nblk4) {
+    return (size_t)(mc * nblk4 * (kB3BlockLds + kB3BlockX) + kB3ZeroLds + 64);
+}
+
 static B3Plan base3_plan(int64_t M, int64_t N, int64_t K) {
     B3Plan pl;
     pl.Kb3 = (int32_t)ceil_div(K, kBase3BlockK);
     pl.row_wgs = ceil_div(N, kB3Rows);
     pl.mc = (int32_t)(M < kBase3MaxTokens ? (M > 0 ? M : 1) : kBase3MaxTokens);
-    const int64_t per_blk = (int64_t)pl.mc * (kB3BlockLds + kB3BlockX);
-    int64_t max_kb = (kB3LdsBudget - kB3ZeroLds - 64) / per_blk / 4 * 4;
-    const int64_t max_kb_x = (int64_t)kB3XLoads * 256 * 16 / (pl.mc * kB3BlockX) / 4 * 4;
-    if (max_kb > max_kb_x) max_kb = max_kb_x;   // the activation loads cover the slice
-    if (max_kb > 2048) max_kb = 2048;   // keeps every MFMA accumulator inside int32
+    const int64_t max_kb = base3_max_slice_kb(pl.mc);
     int64_t S = ceil_div(kB3TargetWgs, pl.row_wgs);
     const int64_t min_s = ceil_div(pl.Kb3, max_kb);
     const int64_t max_s = ceil_div(pl.Kb3, 8);   // at least two K-steps per slice
@@ -316,7 +352,7 @@ static B3Plan base3_plan(int64_t M, int64_t N, int64_t K) {
     pl.kb_per_slice = (int32_t)ceil_div(pl.Kb3, S);
     pl.S = (int32_t)ceil_div(pl.Kb3, pl.kb_per_slice);
     pl.nblk4 = (int32_t)(ceil_div(pl.kb_per_slice, 4) * 4);
-    pl.lds = (size_t)pl.mc * pl.nblk4 * (kB3BlockLds + kB3BlockX) + kB3ZeroLds + 64;
+    pl.lds = base3_lds_bytes(pl.mc, pl.nblk4);
     return pl;
 }
 
@@ -342,11 +378,28 @@ int launch_base3(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
     for (int64_t m0 = 0; m0 < M; m0 += kBase3MaxTokens) {
         a.m0 = (int32_t)m0;
         a.mc = (int32_t)(M - m0 < kBase3MaxTokens ? M - m0 : kBase3MaxTokens);
-        hipLaunchKernelGGL(base3_mfma_kernel<kB3Depth>, dim3((unsigned)blocks), dim3(256), pl.lds, stream, a);
+        hipLaunchKernelGGL((base3_mfma_kernel<kB3Depth, false>), dim3((unsigned)blocks), dim3(256), pl.lds, stream, a);
         BL_LAUNCH_CHECK();
     }
     if (pl.S > 1) return launch_splitk_epilogue(a.partial, pl.S, M, p, stream);
     return BITLINEAR_OK;
+}
+
+int launch_base3_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
+                         int64_t max_slice_kb, int32_t* partial, hipStream_t stream) {
+    if (M < 1 || M > kBase3MaxTokens) return BITLINEAR_EUNSUPPORTED;
+    B3Args a{};
+    a.problems = problems;
+    a.units = units;
+    a.gpart = partial;
+    a.M = M;
+    a.m0 = 0;
+    a.mc = (int32_t)M;
+    const size_t lds = base3_lds_bytes(M, ceil_div(max_slice_kb, 4) * 4);
+    hipLaunchKernelGGL((base3_mfma_kernel<kB3Depth, true>), dim3((unsigned)nunits), dim3(256), lds, stream, a);
+    BL_LAUNCH_CHECK();
+    return partial ? launch_grouped_splitk_epilogue(problems, units, nunits, M, kB3Rows, partial, stream)
+                   : BITLINEAR_OK;
 }
 
 }  // namespace bl

@@ -36,5 +36,14 @@ int launch_lut(const Problem& p, int64_t M, int format, void* ws, hipStream_t st
 constexpr int kBase3MaxTokens = 8;
 size_t base3_ws_bytes(int64_t M, int64_t N, int64_t K);
 int launch_base3(const Problem& p, int64_t M, void* ws, hipStream_t stream);
+// Longest K-slice (80-k blocks) one workgroup arranges in LDS for mc tokens.
+int64_t base3_max_slice_kb(int64_t mc);
+// Grouped (M <= kBase3MaxTokens): problem p's units are its 256-row blocks,
+// each cut into p.slices K-slices (consecutive units; p.Kb holds the 80-k
+// block count); max_slice_kb bounds every slice's length.  With any slices >
+// 1, partial holds nunits * M * 256 int32 and a second launch adds the
+// slices and dequantizes.
+int launch_base3_grouped(const Problem* problems, const Unit* units, int64_t nunits, int64_t M,
+                         int64_t max_slice_kb, int32_t* partial, hipStream_t stream);
 
 }  // namespace bl

@@ -292,11 +292,11 @@ int launch_skinny(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
 
 // Grouped split-K epilogue (shared with the grouped prefill tiles, whose
 // column tiles are 256 wide too), grid (units, row chunks): the workgroups
-// of a block's first slice add the block's slices in order for kEpiRows token rows
+// of a block's first slice add the block's slices for kEpiRows token rows
 // (thread = output row n of the block) and apply the dequant; every other
-// unit, and blocks of unsplit problems, exit.  The slice loop is unrolled to
-// its maximum, so that a thread's loads are all in flight at once rather
-// than one memory round trip per slice.
+// unit, and blocks of unsplit problems, exit.  The slice loop is unrolled in
+// rounds of kSkinnyMaxSlices, so that a thread's loads of a round are all in
+// flight at once rather than one memory round trip per slice.
 constexpr int kEpiRows = 4;
 
 template <int W>   // unit width: output rows of a unit = threads of a workgroup
@@ -313,21 +313,27 @@ __global__ __launch_bounds__(W) void grouped_splitk_epilogue_kernel(const Proble
     const int rows = M - m0 < kEpiRows ? (int)(M - m0) : kEpiRows;
     const int S = p.slices;
     const int32_t* __restrict__ src = gpart + (u * M + m0) * W + threadIdx.x;
-    int part[kSkinnyMaxSlices][kEpiRows];
+    int v[kEpiRows] = {};
+    // kSkinnyMaxSlices slices' loads in flight at a time (more slices: more
+    // rounds); the int32 sum is exact in any order
+    for (int s0 = 0; s0 < S; s0 += kSkinnyMaxSlices) {
+        int part[kSkinnyMaxSlices][kEpiRows];
 #pragma unroll
-    for (int s = 0; s < kSkinnyMaxSlices; ++s)
+        for (int s = 0; s < kSkinnyMaxSlices; ++s)
+#pragma unroll
+            for (int r = 0; r < kEpiRows; ++r)
+                part[s][r] = s0 + s < S && r < rows ? src[((int64_t)(s0 + s) * M + r) * W] : 0;
 #pragma unroll
         for (int r = 0; r < kEpiRows; ++r)
-            part[s][r] = s < S && r < rows ? src[((int64_t)s * M + r) * W] : 0;
+#pragma unroll
+            for (int s = 0; s < kSkinnyMaxSlices; ++s) v[r] += part[s][r];
+    }
 #pragma unroll
     for (int r = 0; r < kEpiRows; ++r) {
         if (r >= rows) break;
-        int v = 0;
-#pragma unroll
-        for (int s = 0; s < kSkinnyMaxSlices; ++s) v += part[s][r];   // slice order
         const int64_t m = m0 + r;
-        p.y[m * p.N + n] = dequant(v, dequant_scale(p.eta[m], p.gamma));
-        if (p.y_int) p.y_int[m * p.N + n] = v;
+        p.y[m * p.N + n] = dequant(v[r], dequant_scale(p.eta[m], p.gamma));
+        if (p.y_int) p.y_int[m * p.N + n] = v[r];
     }
 }
 

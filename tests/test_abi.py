@@ -237,8 +237,14 @@ def test_grouped_planner_validation():
     assert bl.bitlinear_grouped_table_bytes(ok, 0, 1) == 0
     assert bl.bitlinear_grouped_table_bytes(probs(2, K=40), 2, 1) == 0
     bad = probs(2)
-    bad[1].reserved = 1
+    bad[1].format = 2                                    # no such layout
     assert bl.bitlinear_grouped_table_bytes(bad, 2, 1) == 0
+    mixed = probs(2)
+    mixed[1].format = bl.BITLINEAR_FORMAT_BASE3          # one layout per plan
+    assert bl.bitlinear_grouped_table_bytes(mixed, 2, 1) == 0
+    b3 = probs(2, format=bl.BITLINEAR_FORMAT_BASE3)
+    assert bl.bitlinear_grouped_table_bytes(b3, 2, 8) > 0
+    assert bl.bitlinear_grouped_table_bytes(b3, 2, 9) == 0   # base-3 plans: up to 8 tokens
     # one xq buffer fed from two different float32 sources
     clash = bl.make_problems([dict(x=FAKE, xq=FAKE, eta=FAKE, packed=FAKE, y=FAKE, gamma=1, N=64, K=64),
                               dict(x=FAKE + 4096, xq=FAKE, eta=FAKE, packed=FAKE, y=FAKE, gamma=1, N=64, K=64)])

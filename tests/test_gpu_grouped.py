@@ -93,6 +93,34 @@ def test_c4_sweep_full_size_sampled():
             assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
 
 
+@pytest.mark.timeout(900)
+def test_c4_sweep_base3_full_size_sampled():
+    # the same 70B-shaped sweep with every matrix in the base-3 layout, at one
+    # and eight tokens, as bench.py times it
+    torch = torch_cuda()
+    from ternary_weight_linear_fwd_amd.sweep import DecodeSweep
+    sw = DecodeSweep(Ms=(), formats=("base3",), base3_Ms=(1, 8), keep_int=SAMPLES, progress=say)
+    assert sw.weight_bytes("base3") == 13_754_695_680
+    for M in (1, 8):
+        sw.step(M, fmt="base3")
+    torch.cuda.synchronize()
+    projs = {p.name: p for p in S.C4_PROJS}
+    for layer, name in SAMPLES:
+        p = projs[name]
+        say(f"C4 base-3 check layer={layer} {name} ({p.K}->{p.N})")
+        W = S.c4_weight_device(layer, p).cpu().numpy()
+        Wt, g = oracle.quantize_weights(W)
+        del W
+        assert np.float32(sw.gamma[(layer, name)]) == g
+        for M in (1, 8):
+            key = (layer, name, M)
+            x = sw.x[key].cpu().numpy()
+            y_ref, xq_ref, eta_ref, y_int_ref = oracle.forward(x, Wt, g, threads=THREADS)
+            assert np.array_equal(sw.xq[key].cpu().numpy(), xq_ref)
+            assert np.array_equal(sw.y_int[key].cpu().numpy(), y_int_ref)
+            assert np.array_equal(sw.y[key].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
 # Rows of very different lengths in one plan: K past the quantizer's register
 # budget (32768 floats: read twice), tiny K, and ordinary K; x̃ and eta from the
 # grouped quantizer and the integer sums bit-exact.

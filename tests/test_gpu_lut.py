@@ -241,3 +241,127 @@ def test_forward3_extremes():
 def test_forward3_long_k():
     # K far past the workloads: several K-slices of the maximum slice length
     check_forward3(2, 70, 200000, seed=77)
+
+
+# ---------------------------------------------------------------- grouped base-3
+def pack3_latent(W: np.ndarray):
+    """Latent float32 weights -> base-3 layout on the GPU (absmean gamma)."""
+    import ctypes
+    L = bl()
+    N, K = W.shape
+    packed = empty(L.bitlinear_packed3_bytes(N, K))
+    ws_bytes = L.bitlinear_workspace_bytes(0, N, K)
+    ws = empty(ws_bytes)
+    g = ctypes.c_float()
+    L.bitlinear_pack_weights3(to_dev(W), N, K, packed, None, g, ws, ws_bytes)
+    return packed, np.float32(g.value)
+
+
+def run_grouped3(specs, M):
+    torch = torch_cuda()
+    L = bl()
+    for s in specs:
+        s["format"] = L.BITLINEAR_FORMAT_BASE3
+    probs = L.make_problems(specs)
+    tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
+    assert tb > 0
+    table = empty(tb)
+    plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
+    L.bitlinear_forward_grouped(plan)
+    torch.cuda.synchronize()
+    return plan
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+def test_grouped_base3_block(M):
+    # the 3B-shaped block in base-3 weights, q/k/v sharing one input: a plan
+    # too small to fill the chip, so every K loop is cut into slices
+    torch = torch_cuda()
+    specs, refs = [], []
+    shared_x = torch.from_numpy(S.c2_x(S.C2_PROJS[0], M)).cuda()
+    shared_xq = torch.empty((M, 3200), dtype=torch.int8, device="cuda")
+    shared_eta = torch.empty(M, dtype=torch.float32, device="cuda")
+    for p in S.C2_PROJS:
+        W = S.c2_weight(p)
+        packed, g = pack3_latent(W)
+        Wt, g_ref = oracle.quantize_weights(W)
+        assert g == g_ref
+        if p.name in ("q", "k", "v"):
+            x_np, x, xq, eta = S.c2_x(S.C2_PROJS[0], M), shared_x, shared_xq, shared_eta
+        else:
+            x_np = S.c2_x(p, M)
+            x = torch.from_numpy(x_np).cuda()
+            xq = torch.empty((M, p.K), dtype=torch.int8, device="cuda")
+            eta = torch.empty(M, dtype=torch.float32, device="cuda")
+        y = torch.empty((M, p.N), dtype=torch.float32, device="cuda")
+        y_int = torch.empty((M, p.N), dtype=torch.int32, device="cuda")
+        specs.append(dict(x=x, xq=xq, eta=eta, packed=packed, y=y, y_int=y_int, gamma=g, N=p.N, K=p.K))
+        refs.append((x_np, Wt, g, packed))
+    say(f"grouped base-3 block M={M}")
+    plan = run_grouped3(specs, M)
+    assert plan.quant_rows == 5 * M and plan.kernel == 9    # K split: the block alone is a small plan
+    for s, (x_np, Wt, g, packed) in zip(specs, refs):
+        y_ref, xq_ref, eta_ref, y_int_ref = oracle.forward(x_np, Wt, g, threads=8)
+        assert np.array_equal(s["xq"].cpu().numpy(), xq_ref)
+        assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref)
+        y = s["y"].cpu().numpy()
+        assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
+        # the single-problem base-3 forward gives the same bits
+        y1, _ = forward3(xq_ref, eta_ref, packed, g, s["N"])
+        assert np.array_equal(y1.view(np.uint32), y.view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_grouped_base3_shapes(M):
+    # ragged N and K, a problem whose activations are already quantized
+    # (x = NULL), and 65 x 28672, whose K needs more than 16 slices at 8 tokens
+    # (the slice length is bounded by the kernel's LDS arrangement)
+    torch = torch_cuda()
+    shapes = [(300, 4144), (64, 16), (1000, 16384), (257, 2064), (130, 1040), (65, 28672)]
+    specs, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        Wt = S.random_ternary(40 + i, N, K)
+        packed, bad = pack3_ternary(Wt)
+        assert bad == 0
+        x_np = S.random_x(50 + i, M, K, "t3" if i % 2 else "normal")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        y_int = torch.empty((M, N), dtype=torch.int32, device="cuda")
+        g = np.float32(0.01 * (i + 1))
+        if i == 1:
+            xq_np, eta_np = oracle.quantize_act(x_np)
+            spec = dict(x=None, xq=to_dev(xq_np), eta=to_dev(eta_np), packed=packed, y=y, y_int=y_int,
+                        gamma=g, N=N, K=K)
+        else:
+            spec = dict(x=to_dev(x_np), xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                        eta=torch.empty(M, dtype=torch.float32, device="cuda"), packed=packed, y=y,
+                        y_int=y_int, gamma=g, N=N, K=K)
+        specs.append(spec)
+        refs.append((x_np, Wt, g))
+    say(f"grouped base-3 shapes M={M}")
+    run_grouped3(specs, M)
+    for s, (x_np, Wt, g) in zip(specs, refs):
+        y_ref, _, _, y_int_ref = oracle.forward(x_np, Wt, g, threads=8)
+        assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref), (s["N"], s["K"])
+        assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+def test_grouped_base3_large_plan():
+    # enough 256-row blocks to fill the chip: whole K loops, no partial sums
+    torch = torch_cuda()
+    M, N, K = 1, 17000, 1040
+    specs, refs = [], []
+    for i in range(12):
+        Wt = S.random_ternary(70 + i, N, K)
+        packed, _ = pack3_ternary(Wt)
+        x_np = S.random_x(80 + i, M, K)
+        specs.append(dict(x=to_dev(x_np), xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                          eta=torch.empty(M, dtype=torch.float32, device="cuda"), packed=packed,
+                          y=torch.empty((M, N), dtype=torch.float32, device="cuda"), y_int=None,
+                          gamma=np.float32(0.02), N=N, K=K))
+        refs.append((x_np, Wt))
+    say("grouped base-3 large plan")
+    plan = run_grouped3(specs, M)
+    assert plan.kernel == 8 and plan.units == 12 * -(-N // 256)   # base-3, one unit per 256-row block
+    for s, (x_np, Wt) in zip(specs, refs):
+        y_ref, *_ = oracle.forward(x_np, Wt, np.float32(0.02), threads=8)
+        assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
