@@ -632,10 +632,10 @@ COPY_BYTES = 1 << 30
 
 def profile_run(torch, L, sw, args) -> int:
     """Kernels for rocprofv3: full steps, contraction-only launches, a calibration copy."""
-    M = args.profile_m
+    M, fmt = args.profile_m, args.profile_fmt
     for _ in range(max(1, args.steps)):
-        sw.step(M)
-    plan_c, _table = contraction_only_plan(sw, M)
+        sw.step(M, fmt=fmt)
+    plan_c, _table = contraction_only_plan(sw, M, fmt)
     for _ in range(max(1, args.steps)):
         L.bitlinear_forward_grouped(plan_c)
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -643,7 +643,7 @@ def profile_run(torch, L, sw, args) -> int:
     for _ in range(3):
         dst.copy_(src)   # reads and writes exactly COPY_BYTES each
     torch.cuda.synchronize()
-    log(f"profile run done: M={M}, contraction bytes per launch {sw.contraction_bytes(M)}")
+    log(f"profile run done: {fmt} M={M}, contraction bytes per launch {sw.contraction_bytes(M, fmt)}")
     return 0
 
 
@@ -679,7 +679,8 @@ def summarize_profile(root: str) -> str:
         for r in rows:
             key = "copy" if "copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower() \
                 else ("contraction" if any(k in r["Kernel_Name"] for k in
-                                           ("gemv_dot4_kernel", "skinny_mfma_kernel", "gemm_prefill_kernel"))
+                                           ("gemv_dot4_kernel", "skinny_mfma_kernel", "gemm_prefill_kernel",
+                                            "base3_mfma_kernel"))
                       else None)
             if key:
                 per.setdefault(key, []).append(float(r["Counter_Value"]))
@@ -759,6 +760,8 @@ def main() -> int:
     ap.add_argument("--no-base3", action="store_true", help="skip the base-3 layout of the 70B sweep")
     ap.add_argument("--profile-m", type=int, default=1, choices=(1, 16),
                     help="token count of the --profile-run sweep")
+    ap.add_argument("--profile-fmt", default="2bit", choices=("2bit", "base3"),
+                    help="weight layout of the --profile-run sweep (base-3: M=1 only)")
     ap.add_argument("--profile-run", action="store_true",
                     help="short run for rocprofv3: the M=1 sweep, the contraction kernel alone and a "
                          "1 GiB copy whose counters calibrate FETCH_SIZE/WRITE_SIZE")
@@ -820,10 +823,12 @@ def main() -> int:
         for r in prefill:
             log(f"prefill {r['gemm']}: {r['us']} us, {r['tops']} TOP/s ({r['frac']:.1%}); "
                 f"own row sums {r['us_own_row_sums']} us; quantize {r['quantize_us']} us")
-    formats = ("2bit",) if args.profile_run or args.no_base3 else ("2bit", "base3")
-    base3_Ms = (1, 8) if not args.profile_run else ()
-    if not args.profile_run and not args.no_base3:
-        Ms = tuple(sorted(set(Ms) | {8}))   # the 2-bit step at 8 tokens, beside base-3's
+    if args.profile_run:
+        formats = (args.profile_fmt,)
+        base3_Ms = Ms
+    else:
+        formats = ("2bit",) if args.no_base3 else ("2bit", "base3")
+        base3_Ms = (1,)
     sw = DecodeSweep(layers=args.layers, Ms=Ms, progress=log, formats=formats, base3_Ms=base3_Ms)
     log(f"packed weights resident: {sum(sw.weight_bytes(f) for f in formats) / 1e9:.3f} GB ({', '.join(formats)})")
     if args.profile_run:

@@ -281,6 +281,10 @@ bool choose_gemv_slices(std::vector<Problem>& problems) {
 // kBase3SplitMinKb blocks of 80 k each.
 constexpr int64_t kBase3GroupedUnits = 768;
 constexpr int64_t kBase3SplitMinKb = 8;
+// Problems whose K loop is not split run base3_unit_blocks(M) consecutive
+// 256-row blocks per work unit: one arrangement of the activations in LDS and
+// one unbroken weight stream serve them all (split problems: one block per
+// unit, the layout of the split partials).
 
 bool choose_base3_slices(std::vector<Problem>& problems, int64_t M) {
     const int64_t mc = M < 1 ? 1 : (M > kBase3MaxTokens ? kBase3MaxTokens : M);
@@ -301,6 +305,7 @@ bool choose_base3_slices(std::vector<Problem>& problems, int64_t M) {
         int64_t S = ceil_div(p.Kb, len);
         while (S > 1 && (S - 1) * ceil_div(p.Kb, S) >= p.Kb) --S;   // no empty slice
         p.slices = (int32_t)(S < 1 ? 1 : S);
+        p.blocks_per_unit = p.slices > 1 ? 1 : base3_unit_blocks(mc);
         any = any || p.slices > 1;
     }
     return any;
@@ -385,7 +390,8 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
                           : out.kernel == kPlanGemvSplit                                  ? kPlanGemv
                           : out.kernel == kPlanBase3Split                                 ? kPlanBase3
                                                                                           : out.kernel;
-        const int64_t nu = problem_units(k, M, p.N);
+        const int64_t nu = k == kPlanBase3 ? ceil_div(ceil_div(p.N, kSkinnyRows), p.blocks_per_unit)
+                                           : problem_units(k, M, p.N);
         for (int64_t g = 0; g < nu; ++g)
             for (int32_t s = 0; s < p.slices; ++s) out.units.push_back(Unit{i, (int32_t)g});
         if (out.units.size() >= (size_t)kMaxDim) return BITLINEAR_EUNSUPPORTED;

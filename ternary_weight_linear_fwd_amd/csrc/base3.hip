@@ -28,15 +28,19 @@
 // work is 12 operations per 20 weights (two byte splits and ten multiplies),
 // against 9 per 16 weights for the 2-bit codes on v_dot4.
 //
-// Work unit: a workgroup of four wavefronts owns 256 output rows (a wavefront
-// one 64-row group of the layout, four 16-column MFMA tiles) and a K-slice.
-// It first arranges the slice's activations of up to 8 tokens in LDS
-// (per 80-k block and token, five digit steps x 32 bytes plus a zero step);
-// per K-step of four blocks every lane then loads its four 16-byte row chunks
-// (row n of each tile, block kb + lane / 16: four 256-byte runs per wave
-// load, D steps in flight), splits and multiplies them, and issues 40 MFMAs
-// against 10 A fragments read from LDS.  Lanes whose A row has no token read
-// a zero area.  K-slices leave int32 partial sums for the split-K epilogue.
+// Work unit: a workgroup of four wavefronts owns a K-slice of one or more
+// consecutive 256-row blocks (a wavefront one 64-row group of the layout per
+// block, four 16-column MFMA tiles).  It first arranges the slice's
+// activations of up to 8 tokens in LDS (per 80-k block and token, five digit
+// steps x 32 bytes plus a zero step); per K-step of four blocks every lane
+// then loads its four 16-byte row chunks (row n of each tile, block
+// kb + lane / 16: four 256-byte runs per wave load, D steps in flight, the
+// stream running on from one row block into the next), splits and
+// multiplies them, and issues 40 MFMAs against 10 A fragments read from LDS.
+// Lanes whose A row has no token read a zero area.  A finished row block's
+// sums go to an LDS stage; the unit writes its outputs at the end as runs of
+// consecutive rows.  K-slices leave int32 partial sums for a split-K
+// epilogue.
 #include "lut.hpp"
 #include "xcd.hpp"
 
@@ -68,7 +72,7 @@ struct B3Args {
     int32_t Kb3;        // 80-k blocks along K
     int32_t S, kb_per_slice;
     int32_t row_wgs;    // workgroups along N
-    int32_t nblk4;      // LDS blocks per token: kb_per_slice rounded up to whole steps
+    int32_t nblk4;      // LDS blocks per token: kb_per_slice rounded up to whole rings of K-steps
     uint32_t xmagic;    // ceil(2^24 / (nblk4 * 5)): c / (nblk4 * 5) = (c * xmagic) >> 24 for c < 1024
 };
 
@@ -137,13 +141,24 @@ __device__ __forceinline__ void b3_step(const uint4 (&w)[4], const uint8_t* alds
 // The lane's chunks of K-step st (blocks past the slice re-read its last
 // block: their activations are zero, and the address stays inside the
 // layout).
+// Non-temporal 16-byte load through a pointer the compiler knows to be
+// global: a generic (flat) load counts against both the memory and the LDS
+// counters and may return out of order, so the compiler then waits for every
+// load in flight before any use.
+typedef const __attribute__((address_space(1))) nv_u32x4 b3_gvec;
+
+__device__ __forceinline__ uint4 b3_ldg(const void* p) {
+    const nv_u32x4 v = __builtin_nontemporal_load((b3_gvec*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ void b3_load(uint4 (&w)[4], const uint8_t* wrow, int64_t b0, int64_t b1, int st,
                                         int lg) {
     int64_t b = b0 + 4 * st + lg;
     if (b >= b1) b = b1 - 1;
     const uint8_t* src = wrow + b * 1024;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) w[t] = ldnt_u4(src + t * 256);
+    for (int t = 0; t < 4; ++t) w[t] = b3_ldg(src + t * 256);
 }
 
 template <int D, bool GROUPED>
@@ -157,23 +172,25 @@ __global__ __launch_bounds__(256, 2) void base3_mfma_kernel(B3Args a) {
     // L2; grouped, neighbouring units of the table.
     const uint32_t wg = xcd_contiguous(blockIdx.x, gridDim.x);
     Problem p;
-    int64_t rb, slice, b0, b1, Kb3;
-    int nblk4;
+    int64_t rb0, slice, b0, b1, Kb3;
+    int nblk4, nrb = 1;   // the unit's 256-row blocks rb0 .. rb0 + nrb - 1
     uint32_t xmagic;
     if constexpr (GROUPED) {
         const Unit un = a.units[wg];
         p = a.problems[un.problem];
-        rb = un.group;
-        slice = (int64_t)wg - p.unit_begin - rb * p.slices;
+        slice = (int64_t)wg - p.unit_begin - (int64_t)un.group * p.slices;
+        rb0 = (int64_t)un.group * p.blocks_per_unit;
+        const int64_t left = ceil_div((int64_t)p.N, kB3Rows) - rb0;
+        nrb = left < p.blocks_per_unit ? (int)left : p.blocks_per_unit;
         Kb3 = p.Kb;
         const int64_t kbs = ceil_div(Kb3, p.slices);
         b0 = slice * kbs;
         b1 = b0 + kbs < Kb3 ? b0 + kbs : Kb3;
-        nblk4 = (int)ceil_div(kbs, 4) * 4;
+        nblk4 = (int)ceil_div(kbs, 4 * D) * (4 * D);   // whole rings of K-steps
         xmagic = ((1u << 24) + (uint32_t)(nblk4 * 5) - 1u) / (uint32_t)(nblk4 * 5);
     } else {
         p = a.p;
-        rb = wg % (uint32_t)a.row_wgs;
+        rb0 = wg % (uint32_t)a.row_wgs;
         slice = wg / (uint32_t)a.row_wgs;
         Kb3 = a.Kb3;
         b0 = slice * a.kb_per_slice;
@@ -182,15 +199,18 @@ __global__ __launch_bounds__(256, 2) void base3_mfma_kernel(B3Args a) {
         xmagic = a.xmagic;
     }
     const int64_t N = p.N, K = p.K, G = ceil_div(N, 64);
-    const int nblk = (int)(b1 - b0), nstep = (nblk + 3) / 4;
+    const int nblk = (int)(b1 - b0);
+    const int nstep_d = ((nblk + 3) / 4 + D - 1) / D * D;   // K-steps per block, padded to whole rings
     const int mc = a.mc;
 
-    // LDS: A arrangement [mc][nblk4][6][2][16], zero area, sums [2][8] (X, X5), raw x [mc][nblk4 * 80].
+    // LDS: A arrangement [mc][nblk4][6][2][16], zero area, sums [2][8] (X, X5),
+    // raw x [mc][nblk4 * 80], output stage [nrb][mc][256] int32.
     uint8_t* F = lds;
     const uint32_t zero_off = (uint32_t)(mc * nblk4 * kB3BlockLds);
     int* sums = reinterpret_cast<int*>(lds + zero_off + kB3ZeroLds);
     uint32_t* xr = reinterpret_cast<uint32_t*>(lds + zero_off + kB3ZeroLds + 64);
     const int xdw = nblk4 * (kB3BlockX / 4);   // raw dwords per token
+    int* ystage = reinterpret_cast<int*>(xr + mc * xdw);
 
     // The slice's raw activations (up to 16 KB: 4 x 16 bytes per thread) are
     // loaded first, then the first D steps of weights, both as fixed,
@@ -205,14 +225,26 @@ __global__ __launch_bounds__(256, 2) void base3_mfma_kernel(B3Args a) {
         const int c = t + 256 * r;
         const int m = (int)(((uint32_t)c * xmagic) >> 24), o = (c - m * (nblk4 * 5)) * 16;
         xin[r] = c < xch && o < nblk * kB3BlockX && b0 * kB3BlockX + o < K;
-        xv[r] = ldnt_u4(p.xq + (xin[r] ? (int64_t)(a.m0 + m) * K + b0 * kB3BlockX + o : 0));
+        xv[r] = b3_ldg(p.xq + (xin[r] ? (int64_t)(a.m0 + m) * K + b0 * kB3BlockX + o : 0));
     }
-    const int64_t g = rb * kB3Waves + wave;
-    const bool group_ok = g < G;
-    const uint8_t* wrow = reinterpret_cast<const uint8_t*>(p.packed) + (group_ok ? g : G - 1) * Kb3 * 1024 + nl * 16;
+    // The weight stream runs over the unit's blocks one after the other: step
+    // (r, st) is K-step st of block r; past the last step it re-reads that
+    // step's chunks (in range, and never used).
+    const uint8_t* wbase = reinterpret_cast<const uint8_t*>(p.packed) + nl * 16;
+    int lr = 0, ls = 0;   // the next (block, step) to load
+    auto load_next = [&](uint4 (&w)[4]) {
+        const bool past = lr >= nrb;
+        int64_t g = (rb0 + (past ? nrb - 1 : lr)) * kB3Waves + wave;
+        if (g >= G) g = G - 1;   // rows past N (a ragged last block): any rows in range
+        b3_load(w, wbase + g * Kb3 * 1024, b0, b1, past ? nstep_d - 1 : ls, lg);
+        if (!past && ++ls == nstep_d) {
+            ls = 0;
+            ++lr;
+        }
+    };
     uint4 wb[D][4];
 #pragma unroll
-    for (int i = 0; i < D; ++i) b3_load(wb[i], wrow, b0, b1, i, lg);
+    for (int i = 0; i < D; ++i) load_next(wb[i]);
     if (t < kB3ZeroLds / 4) reinterpret_cast<uint32_t*>(lds + zero_off)[t] = 0u;
     if (t < 16) sums[t] = 0;
 #pragma unroll
@@ -262,7 +294,6 @@ __global__ __launch_bounds__(256, 2) void base3_mfma_kernel(B3Args a) {
         }
     }
     lds_barrier();
-    if (!group_ok) return;
 
     // Lane (nl, lg): A row nl is token nl / 2, C0 (even) or C1 (odd, one step later).
     const int mt = nl >> 1;
@@ -270,50 +301,69 @@ __global__ __launch_bounds__(256, 2) void base3_mfma_kernel(B3Args a) {
     const uint32_t a_base = a_on ? (uint32_t)((mt * nblk4 + lg) * kB3BlockLds + (nl & 1) * kB3StepLds) : zero_off;
     const uint32_t a_step = a_on ? 4 * kB3BlockLds : 0;
 
+    const bool split = GROUPED ? p.slices > 1 : a.S > 1;
+    // This lane's tokens 2 lg + h (h = 0, 1): their sums.
+    uint32_t Xh[2], X5h[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int m = 2 * lg + h < mc ? 2 * lg + h : 0;
+        Xh[h] = (uint32_t)sums[m];
+        X5h[h] = (uint32_t)sums[8 + m];
+    }
+
     v4i acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = v4i{0, 0, 0, 0};
-    // A ring of D register stages, refilled unconditionally (steps past the
-    // slice re-read its last block), so that the loop body is straight-line
-    // code and the compiler waits for each stage alone while the later ones
-    // stay in flight.
-    int st0 = 0;
-    for (; st0 + D <= nstep; st0 += D) {
+    // A ring of D register stages, refilled unconditionally, so that the loop
+    // body is straight-line code and the compiler waits for each stage alone
+    // while the later ones stay in flight; the stream runs on from one block
+    // into the next (nstep_d, a multiple of D, steps per block: the padding
+    // steps meet zero activations).  A finished block's sums go to the LDS
+    // output stage, which leaves the loads' count of outstanding operations
+    // alone (a global store here would make the next wait drain the stream).
+    for (int r = 0; r < nrb; ++r) {
+        for (int st0 = 0; st0 < nstep_d; st0 += D) {
 #pragma unroll
-        for (int i = 0; i < D; ++i) {
-            b3_step(wb[i], lds + a_base + (st0 + i) * a_step, acc);
-            b3_load(wb[i], wrow, b0, b1, st0 + i + D, lg);
-            __builtin_amdgcn_sched_barrier(0);   // the refill leaves here, not at the end of the body
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < D - 1; ++i)
-        if (st0 + i < nstep) b3_step(wb[i], lds + a_base + (st0 + i) * a_step, acc);
-
-    // Element r of tile t is A row 4 lg + r, column (output row) 16t + nl:
-    // token 2 lg + r / 2, C0 for even r, C1 for odd r.
-    const bool split = GROUPED ? p.slices > 1 : a.S > 1;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int m = 2 * lg + h;
-        if (m >= mc) continue;
-        const uint32_t X = (uint32_t)sums[m], X5 = (uint32_t)sums[8 + m];
-        const int64_t mg = a.m0 + m;
-        const float sc = split ? 0.0f : dequant_scale(p.eta[mg], p.gamma);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int64_t n = g * 64 + tt * 16 + nl;
-            if (n >= N) continue;
-            // modulo 2^32: the parts may exceed int32, the result does not
-            const int v = (int)((uint32_t)acc[tt][2 * h] - 3u * (uint32_t)acc[tt][2 * h + 1] + 128u * X5 - X);
-            if (GROUPED && split) {
-                a.gpart[((int64_t)wg * a.M + mg) * kB3Rows + (n - rb * kB3Rows)] = v;
-            } else if (split) {
-                a.partial[(slice * a.M + mg) * N + n] = v;
-            } else {
-                p.y[mg * N + n] = dequant(v, sc);
-                if (p.y_int) p.y_int[mg * N + n] = v;
+            for (int i = 0; i < D; ++i) {
+                b3_step(wb[i], lds + a_base + (st0 + i) * a_step, acc);
+                load_next(wb[i]);
+                __builtin_amdgcn_sched_barrier(0);   // the refill leaves here, not at the end of the body
             }
+        }
+        // Element q of tile t is A row 4 lg + q, column (output row) 16t + nl:
+        // token 2 lg + q / 2, C0 for even q, C1 for odd q.
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int m = 2 * lg + h;
+            if (m >= mc) continue;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                // modulo 2^32: the parts may exceed int32, the result does not
+                const int v = (int)((uint32_t)acc[tt][2 * h] - 3u * (uint32_t)acc[tt][2 * h + 1] + 128u * X5h[h] -
+                                    Xh[h]);
+                ystage[(r * mc + m) * kB3Rows + wave * 64 + tt * 16 + nl] = v;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = v4i{0, 0, 0, 0};
+    }
+    lds_barrier();
+
+    // The unit's outputs, row runs of consecutive n (rows past N are not
+    // stored): dequantized into y (and y_int), or the split partials.
+    for (int idx = t; idx < nrb * mc * kB3Rows; idx += 256) {
+        const int r = idx / (mc * kB3Rows), rest = idx - r * (mc * kB3Rows);
+        const int m = rest / kB3Rows, nloc = rest - m * kB3Rows;
+        const int64_t rb = rb0 + r, n = rb * kB3Rows + nloc, mg = a.m0 + m;
+        if (n >= N) continue;
+        const int v = ystage[idx];
+        if (GROUPED && split) {   // split units hold one block
+            a.gpart[((int64_t)wg * a.M + mg) * kB3Rows + nloc] = v;
+        } else if (split) {
+            a.partial[(slice * a.M + mg) * N + n] = v;
+        } else {
+            p.y[mg * N + n] = dequant(v, dequant_scale(p.eta[mg], p.gamma));
+            if (p.y_int) p.y_int[mg * N + n] = v;
         }
     }
 }
@@ -324,17 +374,22 @@ struct B3Plan {
     size_t lds;
 };
 
+// Slice lengths are multiples of one ring of K-steps (4 * kB3Depth blocks),
+// which is also how far the LDS arrangement of a slice is padded.
+constexpr int kB3RingKb = 4 * kB3Depth;
+
 int64_t base3_max_slice_kb(int64_t mc) {
     const int64_t per_blk = mc * (kB3BlockLds + kB3BlockX);
-    int64_t max_kb = (kB3LdsBudget - kB3ZeroLds - 64) / per_blk / 4 * 4;
-    const int64_t max_kb_x = (int64_t)kB3XLoads * 256 * 16 / (mc * kB3BlockX) / 4 * 4;
+    const int64_t stage = (int64_t)base3_unit_blocks(mc) * mc * kB3Rows * 4;   // the output stage
+    int64_t max_kb = (kB3LdsBudget - kB3ZeroLds - 64 - stage) / per_blk / kB3RingKb * kB3RingKb;
+    const int64_t max_kb_x = (int64_t)kB3XLoads * 256 * 16 / (mc * kB3BlockX) / kB3RingKb * kB3RingKb;
     if (max_kb > max_kb_x) max_kb = max_kb_x;   // the activation loads cover the slice
     if (max_kb > 2048) max_kb = 2048;   // keeps every MFMA accumulator inside int32
-    return max_kb;
+    return max_kb < kB3RingKb ? kB3RingKb : max_kb;
 }
 
-static size_t base3_lds_bytes(int64_t mc, int64_t nblk4) {
-    return (size_t)(mc * nblk4 * (kB3BlockLds + kB3BlockX) + kB3ZeroLds + 64);
+static size_t base3_lds_bytes(int64_t mc, int64_t nblk4, int64_t nrb) {
+    return (size_t)(mc * nblk4 * (kB3BlockLds + kB3BlockX) + kB3ZeroLds + 64 + nrb * mc * kB3Rows * 4);
 }
 
 static B3Plan base3_plan(int64_t M, int64_t N, int64_t K) {
@@ -351,8 +406,8 @@ static B3Plan base3_plan(int64_t M, int64_t N, int64_t K) {
     if (S < 1) S = 1;
     pl.kb_per_slice = (int32_t)ceil_div(pl.Kb3, S);
     pl.S = (int32_t)ceil_div(pl.Kb3, pl.kb_per_slice);
-    pl.nblk4 = (int32_t)(ceil_div(pl.kb_per_slice, 4) * 4);
-    pl.lds = base3_lds_bytes(pl.mc, pl.nblk4);
+    pl.nblk4 = (int32_t)(ceil_div(pl.kb_per_slice, kB3RingKb) * kB3RingKb);
+    pl.lds = base3_lds_bytes(pl.mc, pl.nblk4, 1);
     return pl;
 }
 
@@ -395,7 +450,7 @@ int launch_base3_grouped(const Problem* problems, const Unit* units, int64_t nun
     a.M = M;
     a.m0 = 0;
     a.mc = (int32_t)M;
-    const size_t lds = base3_lds_bytes(M, ceil_div(max_slice_kb, 4) * 4);
+    const size_t lds = base3_lds_bytes(M, ceil_div(max_slice_kb, kB3RingKb) * kB3RingKb, base3_unit_blocks(M));
     hipLaunchKernelGGL((base3_mfma_kernel<kB3Depth, true>), dim3((unsigned)nunits), dim3(256), lds, stream, a);
     BL_LAUNCH_CHECK();
     return partial ? launch_grouped_splitk_epilogue(problems, units, nunits, M, kB3Rows, partial, stream)

@@ -376,9 +376,10 @@ int launch_gemv_fused(const Problem* problems, const Unit* units, int64_t nunits
 
 // Sum the split-K partials and apply the dequant epilogue.  One output per
 // lane in 64-lane workgroups (a 28672-wide row is 448 of them), each lane
-// with eight partial loads in flight at a time: the sum is exact in int32, so
-// its order does not matter.
-constexpr int kEpiLoads = 8;
+// with up to 32 partial loads in flight at once (one memory round trip for
+// the slice counts the planners choose): the sum is exact in int32, so its
+// order does not matter.
+constexpr int kEpiLoads = 32;
 
 __global__ __launch_bounds__(64) void splitk_epilogue_kernel(const int32_t* __restrict__ partial,
                                                              int S, int64_t M, int64_t N,

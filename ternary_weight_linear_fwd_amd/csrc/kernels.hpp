@@ -28,7 +28,8 @@ struct Problem {
     int32_t unit_begin;     // first work unit of this problem in a grouped table
     int32_t slices;         // grouped skinny plans: K-slices per 256-row block (1: whole K)
     const float* x;         // [M][K] float32 activations (fused grouped decode), or null
-    int32_t pad[2];
+    int32_t blocks_per_unit;  // grouped base-3 plans: 256-row blocks per work unit
+    int32_t pad;
 };
 static_assert(sizeof(Problem) == 80, "Problem descriptor: 80 bytes");
 

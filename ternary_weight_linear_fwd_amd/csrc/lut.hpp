@@ -34,6 +34,9 @@ int launch_lut(const Problem& p, int64_t M, int format, void* ws, hipStream_t st
 // kBase3MaxTokens tokens per pass over the weights; split-K partial sums in
 // the workspace.
 constexpr int kBase3MaxTokens = 8;
+// 256-row blocks one grouped work unit runs (unsplit problems): fewer for
+// more tokens, whose per-block outputs the unit stages in LDS (at most 8 KB).
+constexpr int base3_unit_blocks(int64_t M) { return M <= 2 ? 4 : (M <= 4 ? 2 : 1); }
 size_t base3_ws_bytes(int64_t M, int64_t N, int64_t K);
 int launch_base3(const Problem& p, int64_t M, void* ws, hipStream_t stream);
 // Longest K-slice (80-k blocks) one workgroup arranges in LDS for mc tokens.

@@ -345,10 +345,13 @@ def test_grouped_base3_shapes(M):
         assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
 
 
-def test_grouped_base3_large_plan():
-    # enough 256-row blocks to fill the chip: whole K loops, no partial sums
+@pytest.mark.parametrize("M", [1, 3])
+def test_grouped_base3_large_plan(M):
+    # enough 256-row blocks to fill the chip: whole K loops, no partial sums;
+    # a work unit runs 4 (one or two tokens) or 2 (up to four) consecutive
+    # blocks, the last unit of each problem fewer, the last block ragged
     torch = torch_cuda()
-    M, N, K = 1, 17000, 1040
+    N, K = 17000, 1040
     specs, refs = [], []
     for i in range(12):
         Wt = S.random_ternary(70 + i, N, K)
@@ -359,9 +362,10 @@ def test_grouped_base3_large_plan():
                           y=torch.empty((M, N), dtype=torch.float32, device="cuda"), y_int=None,
                           gamma=np.float32(0.02), N=N, K=K))
         refs.append((x_np, Wt))
-    say("grouped base-3 large plan")
+    say(f"grouped base-3 large plan M={M}")
     plan = run_grouped3(specs, M)
-    assert plan.kernel == 8 and plan.units == 12 * -(-N // 256)   # base-3, one unit per 256-row block
+    per_unit = 4 if M <= 2 else 2
+    assert plan.kernel == 8 and plan.units == 12 * -(-(-(-N // 256)) // per_unit)
     for s, (x_np, Wt) in zip(specs, refs):
         y_ref, *_ = oracle.forward(x_np, Wt, np.float32(0.02), threads=8)
         assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
