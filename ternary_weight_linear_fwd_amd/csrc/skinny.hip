@@ -314,19 +314,33 @@ __global__ __launch_bounds__(W) void grouped_splitk_epilogue_kernel(const Proble
     const int S = p.slices;
     const int32_t* __restrict__ src = gpart + (u * M + m0) * W + threadIdx.x;
     int v[kEpiRows] = {};
-    // kSkinnyMaxSlices slices' loads in flight at a time (more slices: more
-    // rounds); the int32 sum is exact in any order
-    for (int s0 = 0; s0 < S; s0 += kSkinnyMaxSlices) {
+    if (S <= kSkinnyMaxSlices) {
+        // every slice's loads in flight at once (straight-line code)
         int part[kSkinnyMaxSlices][kEpiRows];
 #pragma unroll
         for (int s = 0; s < kSkinnyMaxSlices; ++s)
 #pragma unroll
             for (int r = 0; r < kEpiRows; ++r)
-                part[s][r] = s0 + s < S && r < rows ? src[((int64_t)(s0 + s) * M + r) * W] : 0;
+                part[s][r] = s < S && r < rows ? src[((int64_t)s * M + r) * W] : 0;
 #pragma unroll
         for (int r = 0; r < kEpiRows; ++r)
 #pragma unroll
             for (int s = 0; s < kSkinnyMaxSlices; ++s) v[r] += part[s][r];
+    } else {
+        // more slices (base-3 plans of many tokens): rounds of
+        // kSkinnyMaxSlices; the int32 sum is exact in any order
+        for (int s0 = 0; s0 < S; s0 += kSkinnyMaxSlices) {
+            int part[kSkinnyMaxSlices][kEpiRows];
+#pragma unroll
+            for (int s = 0; s < kSkinnyMaxSlices; ++s)
+#pragma unroll
+                for (int r = 0; r < kEpiRows; ++r)
+                    part[s][r] = s0 + s < S && r < rows ? src[((int64_t)(s0 + s) * M + r) * W] : 0;
+#pragma unroll
+            for (int r = 0; r < kEpiRows; ++r)
+#pragma unroll
+                for (int s = 0; s < kSkinnyMaxSlices; ++s) v[r] += part[s][r];
+        }
     }
 #pragma unroll
     for (int r = 0; r < kEpiRows; ++r) {
