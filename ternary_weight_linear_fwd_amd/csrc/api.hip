@@ -4,6 +4,7 @@
 // carving, kernel choice by token count and the grouped planner.  All the
 // arithmetic of the forward pass runs in the kernels of quant.hip, pack.hip,
 // gemv.hip and gemm.hip.  Nothing here allocates device memory.
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <cstring>
@@ -318,6 +319,41 @@ struct PlanHost {
     int32_t kernel = kPlanGemv;
 };
 
+// Work-unit order of unsplit plans.  A grouped grid holds far more
+// workgroups than the chip runs at once, and each XCD works through its
+// contiguous run of the grid (xcd_contiguous) in order; units whose K loops
+// start late decide when the launch ends.  Within each XCD's run the units
+// therefore go longest first (stable: a problem's units stay adjacent), so
+// the run ends on short units.  Plans whose kernel takes units[blockIdx.x]
+// (round-robin over the XCDs) are ordered as one run.  Measured on the
+// 70B-shaped decode sweep: 2% at one token, 3% at 16 tokens.  Split plans
+// keep their order: a block's K-slices are found from the unit index.
+void order_longest_first(PlanHost& h, int64_t units_per_wg, bool xcd_runs) {
+    const int64_t n = (int64_t)h.units.size();
+    auto length = [&h](const Unit& u) {
+        const Problem& p = h.problems[u.problem];
+        int64_t rows = 1;   // 256-row blocks of a base-3 unit
+        if (p.blocks_per_unit > 1) {
+            const int64_t left = ceil_div(p.N, kSkinnyRows) - (int64_t)u.group * p.blocks_per_unit;
+            rows = left < p.blocks_per_unit ? left : p.blocks_per_unit;
+        }
+        return (int64_t)p.Kb * rows;
+    };
+    auto longer = [&length](const Unit& a, const Unit& b) { return length(a) > length(b); };
+    if (!xcd_runs) {
+        std::stable_sort(h.units.begin(), h.units.end(), longer);
+        return;
+    }
+    // The XCD runs as xcd_contiguous cuts a grid of T workgroups.
+    constexpr int64_t X = 8;
+    const int64_t T = ceil_div(n, units_per_wg), q = T / X, r = T % X;
+    for (int64_t x = 0; x < X; ++x) {
+        const int64_t b0 = x * q + (x < r ? x : r), b1 = b0 + q + (x < r ? 1 : 0);
+        const int64_t u0 = b0 * units_per_wg, u1 = b1 * units_per_wg < n ? b1 * units_per_wg : n;
+        if (u0 < u1) std::stable_sort(h.units.begin() + u0, h.units.begin() + u1, longer);
+    }
+}
+
 int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& out) {
     if (!pr || count <= 0 || M < 0 || M > kMaxDim) return BITLINEAR_EINVAL;
     std::map<const int8_t*, const float*> xq_source;  // xq buffer -> its x
@@ -396,6 +432,11 @@ int build_plan(const bitlinear_problem* pr, int32_t count, int64_t M, PlanHost& 
             for (int32_t s = 0; s < p.slices; ++s) out.units.push_back(Unit{i, (int32_t)g});
         if (out.units.size() >= (size_t)kMaxDim) return BITLINEAR_EUNSUPPORTED;
     }
+    if (out.kernel == kPlanGemv) order_longest_first(out, kGemvWaves, true);
+    if (out.kernel == kPlanSkinny || out.kernel == kPlanBase3) order_longest_first(out, 1, true);
+    if (out.kernel == kPlanGemvFused) order_longest_first(out, 1, false);
+    // Quantizer rows, one workgroup each in grid order: longest first too.
+    std::stable_sort(out.rows.begin(), out.rows.end(), [](const QuantRow& a, const QuantRow& b) { return a.K > b.K; });
     return BITLINEAR_OK;
 }
 

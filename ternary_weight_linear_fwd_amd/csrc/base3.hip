@@ -178,7 +178,10 @@ __global__ __launch_bounds__(256, 2) void base3_mfma_kernel(B3Args a) {
     if constexpr (GROUPED) {
         const Unit un = a.units[wg];
         p = a.problems[un.problem];
-        slice = (int64_t)wg - p.unit_begin - (int64_t)un.group * p.slices;
+        // Split problems: a block's slices are consecutive units from
+        // unit_begin on.  Unsplit problems' units may be reordered (the
+        // planner runs long K loops first), so their slice is 0 by fiat.
+        slice = p.slices > 1 ? (int64_t)wg - p.unit_begin - (int64_t)un.group * p.slices : 0;
         rb0 = (int64_t)un.group * p.blocks_per_unit;
         const int64_t left = ceil_div((int64_t)p.N, kB3Rows) - rb0;
         nrb = left < p.blocks_per_unit ? (int)left : p.blocks_per_unit;

@@ -22,7 +22,6 @@
 
 namespace bl {
 
-constexpr int kGemvWaves = 4;  // wavefronts (work units) per workgroup
 
 template <int M>
 struct Acc {
@@ -238,9 +237,9 @@ __global__ __launch_bounds__(kFusedThreads, 6) void gemv_fused_kernel(const Prob
     const int t = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int lane = t & 63;
-    // Units in table order, which the dispatcher deals round-robin to the
-    // XCDs: problems of different K (the long down projection) spread evenly
-    // over the XCDs' shares of memory bandwidth.
+    // Units in table order (longest K first), which the dispatcher deals
+    // round-robin to the XCDs: problems of different K (the long down
+    // projection) spread evenly over the XCDs' shares of memory bandwidth.
     const Unit un = units[blockIdx.x];
     const Problem p = problems[un.problem];
     const int64_t K = p.K, N = p.N, Kb = p.Kb, g = un.group;

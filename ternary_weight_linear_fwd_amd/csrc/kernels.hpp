@@ -64,6 +64,7 @@ int launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
 // ---- decode contraction, dot4 path for M <= 4 (gemv.hip)
 constexpr int kGemvMaxM = 4;
+constexpr int kGemvWaves = 4;  // wavefronts (work units) per workgroup
 int gemv_split_slices(int64_t M, int64_t N, int64_t K);
 size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K);
 int launch_gemv(const Problem& p, int64_t M, void* ws, hipStream_t stream);
