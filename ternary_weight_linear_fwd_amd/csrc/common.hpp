@@ -50,6 +50,23 @@ __device__ __forceinline__ float4 ldnt_f4(const void* p) {
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// The same loads through pointers the compiler knows to be global, for
+// pointers it cannot trace to a kernel argument (read from a descriptor in
+// memory): a generic (flat) load also counts against the LDS counter, so
+// every LDS access after it would wait for it.
+typedef const __attribute__((address_space(1))) nv_u32x4 gnv_u32x4;
+typedef const __attribute__((address_space(1))) nv_f32x4 gnv_f32x4;
+
+__device__ __forceinline__ uint4 ldgnt_u4(const void* p) {
+    const nv_u32x4 v = __builtin_nontemporal_load((gnv_u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float4 ldg_f4(const void* p) {
+    const nv_f32x4 v = *(gnv_f32x4*)p;
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // Dequantization scale of one token row: s = (eta * gamma) / 127, two float32
 // roundings in that order ([P1] BitLinear158.forward step 5; [P5]
 // bitlinear_forward listing).

@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kFusedThreads, 6) void gemv_fused_kernel(const Prob
 #pragma unroll
             for (int r = 0; r < kFusedChunks; ++r) {
                 const int64_t i = t + (int64_t)r * kFusedThreads;
-                v[r] = i < n4 ? x4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                v[r] = i < n4 ? ldg_f4(x4 + i) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[r].x), fabsf(v[r].y)), fmaxf(fabsf(v[r].z), fabsf(v[r].w))));
             }
             amax = wave_max(amax);
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kFusedThreads, 6) void gemv_fused_kernel(const Prob
     uint4 wq[kFusedBatch];
 #pragma unroll
     for (int i = 0; i < kFusedBatch; ++i)
-        if (kb0 + i < kb1) wq[i] = ldnt_u4(wp + (kb0 + i) * 64);
+        if (kb0 + i < kb1) wq[i] = ldgnt_u4(wp + (kb0 + i) * 64);
 
     // Row group 0 hands x~ and eta on, as the quantize stage does.
     if (g == 0 && p.x) {
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kFusedThreads, 6) void gemv_fused_kernel(const Prob
     for (int64_t kb = kb0 + kFusedBatch; kb < kb1; kb += kFusedBatch) {
 #pragma unroll
         for (int i = 0; i < kFusedBatch; ++i)
-            if (kb + i < kb1) wq[i] = ldnt_u4(wp + (kb + i) * 64);
+            if (kb + i < kb1) wq[i] = ldgnt_u4(wp + (kb + i) * 64);
 #pragma unroll
         for (int i = 0; i < kFusedBatch; ++i)
             if (kb + i < kb1) dot_block_lds<M>(acc, wq[i], xs, kpad, kb + i);

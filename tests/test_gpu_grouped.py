@@ -288,3 +288,80 @@ def test_grouped_fused_decode(M):
             assert np.array_equal(s["eta"].cpu().numpy().view(np.uint32), eta_ref.view(np.uint32))
             assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref)
             assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+# The planner's unit order (no forward runs): unsplit plans run each XCD's
+# run of the grid longest K loop first, stably (a problem's units stay in
+# order), plans whose kernel takes units in grid order (the fused decode) are
+# one such run, and split plans keep problem, block, slice order.  The table
+# is read back and checked against these rules and against the full set of
+# (problem, unit) pairs.
+def _plan_units(L, torch, shapes, M, fmt):
+    dummy = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    base = dummy.data_ptr()
+    specs = [dict(x=None, xq=base, eta=base, packed=base, y=base, gamma=1.0, N=N, K=K, format=fmt)
+             for N, K in shapes]
+    probs = L.make_problems(specs)
+    tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
+    table = torch.empty(tb, dtype=torch.uint8, device="cuda")
+    plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
+    torch.cuda.synchronize()
+    off = -(-len(specs) * 80 // 256) * 256           # units follow the 80-byte problem descriptors
+    raw = table.cpu().numpy()[off:off + 8 * plan.units].view(np.int32).reshape(-1, 2)
+    return plan, [tuple(int(v) for v in u) for u in raw]
+
+
+def _xcd_runs(n, per):
+    T = -(-n // per)
+    q, r = divmod(T, 8)
+    runs = []
+    for x in range(8):
+        b0 = x * q + min(x, r)
+        b1 = b0 + q + (1 if x < r else 0)
+        runs.append((b0 * per, min(b1 * per, n)))
+    return runs
+
+
+@pytest.mark.parametrize("case", ["gemv", "fused", "skinny", "base3", "split"])
+def test_plan_unit_order(case):
+    torch = torch_cuda()
+    L = bl()
+    big = [(28672, 2048), (8192, 8192), (1024, 4096), (8192, 8192)] * 12   # 8640 64-row groups
+    small = [(3200, 3200), (3200, 8640), (1024, 3200), (8640, 3200)]
+    fmt2, fmt3 = L.BITLINEAR_FORMAT_2BIT, L.BITLINEAR_FORMAT_BASE3
+    shapes, M, fmt, kernel = {"gemv": (big, 1, fmt2, 0), "fused": (small, 1, fmt2, 7),
+                              "skinny": (big, 16, fmt2, 2), "base3": (big, 1, fmt3, 8),
+                              "split": (small, 3, fmt2, 6)}[case]
+    plan, units = _plan_units(L, torch, shapes, M, fmt)
+    assert plan.kernel == kernel
+    if fmt == fmt3:
+        per_unit = 4                                            # 256-row blocks per unit at one token
+        nu = [-(-(-(-N // 256)) // per_unit) for N, _ in shapes]
+
+        def length(u):
+            N, K = shapes[u[0]]
+            blocks = min(per_unit, -(-N // 256) - u[1] * per_unit)
+            return -(-K // 80) * blocks
+    else:
+        rows = 256 if kernel == 2 else 64
+        nu = [-(-N // rows) for N, _ in shapes]
+
+        def length(u):
+            return -(-shapes[u[0]][1] // 64)
+    if case == "split":
+        # problem-major, blocks in order, a block's slices adjacent
+        seen = [(p, g) for p, g in units]
+        assert seen == sorted(seen)
+        assert sorted(set(seen)) == [(p, g) for p in range(len(shapes)) for g in range(nu[p])]
+        assert len(units) > sum(nu)
+        return
+    assert sorted(units) == [(p, g) for p in range(len(shapes)) for g in range(nu[p])]
+    runs = [(0, len(units))] if case == "fused" else _xcd_runs(len(units), 4 if case == "gemv" else 1)
+    for u0, u1 in runs:
+        run = units[u0:u1]
+        lens = [length(u) for u in run]
+        assert lens == sorted(lens, reverse=True)
+        # stable: equal lengths keep the table's problem, unit order
+        for a, b in zip(run, run[1:]):
+            if length(a) == length(b):
+                assert a < b
