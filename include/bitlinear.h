@@ -197,9 +197,12 @@ int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t
  *          aligned: split-K partial sums (decode kernels, and the tiled
  *          kernel when its 32 x 128 tiles leave CUs idle over a long K), or
  *          room for the activation row sums of the tiled kernel
- * Kernel by size: M <= 4 the dot4 GEMV; 4 < M <= 16 the streaming MFMA
- * kernel; M > 16 the tiled int8-MFMA kernel (its K loop split over several
- * workgroups per tile when few tiles would leave CUs idle).
+ * Kernel by size: M <= 4 the dot4 GEMV (M <= 2 with a short K loop per
+ * 64-row group: one workgroup per group whose wavefronts split K and add
+ * their sums in LDS; otherwise K split over workgroups, with partial sums
+ * in ws and a second launch); 4 < M <= 16 the streaming MFMA kernel; M > 16
+ * the tiled int8-MFMA kernel (its K loop split over several workgroups per
+ * tile when few tiles would leave CUs idle).
  */
 int bitlinear_forward(const int8_t* xq, const float* eta, const uint8_t* packed, float gamma,
                       int64_t M, int64_t N, int64_t K, float* y, int32_t* y_int, void* ws,
@@ -227,7 +230,10 @@ int bitlinear_forward_xsum(const int8_t* xq, const float* eta, const int32_t* xs
 /*
  * Fused forward from float32 activations: quantize (into the workspace, with
  * the row sums for bitlinear_forward_xsum), contract, dequantize.  Same
- * arguments as above; ws is required.
+ * arguments as above; ws is required.  At one or two tokens, on the shapes
+ * where bitlinear_forward takes the one-workgroup-per-row-group dot4 kernel
+ * (and K <= 16384), that kernel quantizes the rows itself in one launch; x~
+ * and eta still land in the workspace, the row sums do not.
  * [P1] BitLinear158.forward steps 2, 4 and 5.
  */
 int bitlinear_forward_f32(const float* x, const uint8_t* packed, float gamma, int64_t M,

@@ -713,6 +713,11 @@ static int forward_f32_common(const float* x, const uint8_t* packed, float gamma
     void* rest = (char*)ws + w.xq + w.eta + w.xsum;
     hipStream_t s = (hipStream_t)stream;
     clear_hip_error();
+    // One or two tokens on a shape the fused decode kernel takes: each
+    // workgroup quantizes the rows itself, one launch (x~ and eta still land
+    // in the workspace; no row sums, which no decode kernel reads).
+    if (!rmsnorm && K <= kFusedMaxK && forward_path(M, N) == Path::Gemv && gemv_fused_single(M, N, K))
+        return launch_gemv_fused_single(make_problem(xq, eta, packed, gamma, N, K, y, nullptr, x), M, s);
     // The quantizer writes the row sums alongside xq, so the contraction
     // need not sum the activation tiles again.
     rc = rmsnorm ? launch_rmsnorm_quantize(x, M, K, xq, eta, xsum, nullptr, s)

@@ -224,9 +224,12 @@ __device__ __forceinline__ void dot_block_lds(Acc<M>& acc, const uint4 w, const 
     }
 }
 
-template <int M>
+// SINGLE: one problem given by value (x = NULL: x~ and eta given), row group
+// = blockIdx.x; otherwise (problem, row group) from the grouped table.
+template <int M, bool SINGLE>
 __global__ __launch_bounds__(kFusedThreads, 6) void gemv_fused_kernel(const Problem* __restrict__ problems,
-                                                                   const Unit* __restrict__ units, int64_t nunits) {
+                                                                   const Unit* __restrict__ units, int64_t nunits,
+                                                                   Problem single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // [M][Kb * 64] x~, zero at k >= K
     __shared__ float red_max[M][kFusedWaves];
     __shared__ int red_sum[M][kFusedWaves];
@@ -240,9 +243,8 @@ __global__ __launch_bounds__(kFusedThreads, 6) void gemv_fused_kernel(const Prob
     // Units in table order (longest K first), which the dispatcher deals
     // round-robin to the XCDs: problems of different K (the long down
     // projection) spread evenly over the XCDs' shares of memory bandwidth.
-    const Unit un = units[blockIdx.x];
-    const Problem p = problems[un.problem];
-    const int64_t K = p.K, N = p.N, Kb = p.Kb, g = un.group;
+    const Problem p = SINGLE ? single : problems[units[blockIdx.x].problem];
+    const int64_t K = p.K, N = p.N, Kb = p.Kb, g = SINGLE ? (int64_t)blockIdx.x : (int64_t)units[blockIdx.x].group;
     const int64_t kpad = Kb * 64;
 
     // This wavefront's contiguous run of k-blocks.
@@ -364,11 +366,46 @@ int launch_gemv_fused(const Problem* problems, const Unit* units, int64_t nunits
     if (max_K > kFusedMaxK) return BITLINEAR_EUNSUPPORTED;
     const size_t lds = (size_t)M * (size_t)(ceil_div(max_K, 64) * 64);
     const dim3 grid((unsigned)nunits), block(kFusedThreads);
+    const Problem none{};
     switch (M) {
-        case 1: hipLaunchKernelGGL(gemv_fused_kernel<1>, grid, block, lds, stream, problems, units, nunits); break;
-        case 2: hipLaunchKernelGGL(gemv_fused_kernel<2>, grid, block, lds, stream, problems, units, nunits); break;
+        case 1:
+            hipLaunchKernelGGL((gemv_fused_kernel<1, false>), grid, block, lds, stream, problems, units, nunits, none);
+            break;
+        case 2:
+            hipLaunchKernelGGL((gemv_fused_kernel<2, false>), grid, block, lds, stream, problems, units, nunits, none);
+            break;
         default: return BITLINEAR_EUNSUPPORTED;
     }
+    BL_LAUNCH_CHECK();
+    return BITLINEAR_OK;
+}
+
+// A single problem of at most kFusedMaxM tokens runs the fused kernel -- one
+// workgroup per 64-row group whose wavefronts split the K loop and meet in
+// LDS, no split-K partials and no second launch -- where each wavefront's
+// run of k-blocks is one batch of loads, or two on a grid of at least
+// kFusedSingleGroups groups, and the x~ rows fit the LDS.  Measured on
+// MI355X against the split GEMV and its epilogue (graph replay, weights
+// cycled): 2048 x 2048 at one token 5.5 -> 4.0 us, 8640 x 3200 7.0 -> 5.1,
+// 28672 x 8192 16.4 -> 14.2; the long-K runs it leaves to the split GEMV
+// (8192 x 28672 16.2 against 19.4 fused; 1024 x 8192 6.3 against 6.9).
+constexpr int64_t kFusedSingleGroups = 32;
+constexpr int64_t kFusedSingleMaxLds = 32 * 1024;
+
+bool gemv_fused_single(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > kFusedMaxM || M * ceil_div(K, 64) * 64 > kFusedSingleMaxLds) return false;
+    const int64_t run = ceil_div(ceil_div(K, 64), kFusedWaves);   // k-blocks per wavefront
+    return run <= 8 || (run <= 16 && ceil_div(N, 64) >= kFusedSingleGroups);
+}
+
+int launch_gemv_fused_single(const Problem& p, int64_t M, hipStream_t stream) {
+    if (p.x && p.K > kFusedMaxK) return BITLINEAR_EUNSUPPORTED;
+    const size_t lds = (size_t)M * (size_t)(p.Kb * 64);
+    const dim3 grid((unsigned)ceil_div(p.N, 64)), block(kFusedThreads);
+    if (M == 1)
+        hipLaunchKernelGGL((gemv_fused_kernel<1, true>), grid, block, lds, stream, nullptr, nullptr, 0, p);
+    else
+        hipLaunchKernelGGL((gemv_fused_kernel<2, true>), grid, block, lds, stream, nullptr, nullptr, 0, p);
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
 }
@@ -424,6 +461,7 @@ int gemv_split_slices(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
+    if (gemv_fused_single(M, N, K)) return 0;
     const int S = gemv_split_slices(M, N, K);
     return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
 }
@@ -435,6 +473,7 @@ static void launch_single(const GemvArgs& a, int64_t blocks, hipStream_t stream)
 }
 
 int launch_gemv(const Problem& p, int64_t M, void* ws, hipStream_t stream) {
+    if (!p.x && gemv_fused_single(M, p.N, p.K)) return launch_gemv_fused_single(p, M, stream);
     GemvArgs a{};
     a.p = p;
     const int S = gemv_split_slices(M, p.N, p.K);

@@ -82,6 +82,11 @@ constexpr int kFusedMaxK = 16384;
 constexpr int kFusedMaxM = 2;
 int launch_gemv_fused(const Problem* problems, const Unit* units, int64_t nunits, int64_t M, int64_t max_K,
                       hipStream_t stream);
+// The same kernel on one problem (row group = workgroup), where
+// gemv_fused_single(M, N, K) holds: from x~ (p.x = NULL), or quantizing p.x
+// itself (K <= kFusedMaxK; x~ and eta also written to p.xq / p.eta).
+bool gemv_fused_single(int64_t M, int64_t N, int64_t K);
+int launch_gemv_fused_single(const Problem& p, int64_t M, hipStream_t stream);
 
 // Sum split-K partials [S][M][N] in slice order and apply the dequant epilogue.
 int launch_splitk_epilogue(const int32_t* partial, int S, int64_t M, const Problem& p,

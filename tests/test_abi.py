@@ -116,9 +116,9 @@ def test_validation_before_any_device_work():
     # forward: null output, bad K, split-K workspace missing
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 64, 64, None, None, None, 0, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 64, 48 + 1, FAKE, None, None, 0, None) == L.BITLINEAR_EUNSUPPORTED
-    need = L.bitlinear_workspace_bytes(1, 8192, 8192)
+    need = L.bitlinear_workspace_bytes(1, 8192, 28672)   # a long K loop: split over workgroups
     assert need > 0
-    assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 28672, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
     # prefill sizes: the row sums need the workspace
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward", FAKE, FAKE, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, FAKE, 256, None) == L.BITLINEAR_EWORKSPACE
@@ -134,7 +134,7 @@ def test_validation_before_any_device_work():
     assert _rc("bitlinear_forward_xsum", FAKE, FAKE, None, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_forward_xsum", FAKE, FAKE, FAKE + 2, FAKE, ctypes.c_float(1.0), 128, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_forward_xsum", FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), 128, 64, 40, FAKE, None, None, 0, None) == L.BITLINEAR_EUNSUPPORTED
-    assert _rc("bitlinear_forward_xsum", FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_forward_xsum", FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), 1, 8192, 28672, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_forward_f32", FAKE, FAKE, ctypes.c_float(1.0), 4, 64, 64, FAKE, FAKE + 8, 1 << 20, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_pack_weights_absmedian", FAKE, 64, 64, FAKE, None, None, FAKE, 4096, None) == L.BITLINEAR_EWORKSPACE
@@ -147,7 +147,7 @@ def test_validation_before_any_device_work():
     assert _rc("bitlinear_forward_lut", FAKE, FAKE, FAKE, 2, ctypes.c_float(1.0), 1, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_forward_lut", FAKE, FAKE, FAKE, 1, ctypes.c_float(1.0), 1, 64, 72, FAKE, None, None, 0, None) == L.BITLINEAR_EUNSUPPORTED
     assert _rc("bitlinear_forward_lut", FAKE, None, FAKE, 0, ctypes.c_float(1.0), 1, 64, 64, FAKE, None, None, 0, None) == L.BITLINEAR_EINVAL
-    assert _rc("bitlinear_forward_lut", FAKE, FAKE, FAKE, 1, ctypes.c_float(1.0), 1, 8192, 8192, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
+    assert _rc("bitlinear_forward_lut", FAKE, FAKE, FAKE, 1, ctypes.c_float(1.0), 1, 8192, 28672, FAKE, None, None, 0, None) == L.BITLINEAR_EWORKSPACE
     assert _rc("bitlinear_rmsnorm_quantize_act", None, 1, 64, FAKE, FAKE, None, None, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_rmsnorm_quantize_act", FAKE, 1, 64, FAKE, None, None, None, None) == L.BITLINEAR_EINVAL
     assert _rc("bitlinear_rmsnorm_quantize_act", FAKE, 1, 40, FAKE, FAKE, None, None, None) == L.BITLINEAR_EUNSUPPORTED
