@@ -56,6 +56,16 @@ def test_ragged_shapes(M, N, K):
     run_case(M, N, K, seed=M * 131 + N * 7 + K)
 
 
+# One or two tokens: the fused kernel (one workgroup per 64-row group, K split
+# among its wavefronts) where each wavefront's run is short, the split GEMV
+# and its epilogue where it is long; ragged N, K with a tail block, both
+# paths from int8 and from float32.
+@pytest.mark.parametrize("M,N,K", [(1, 2065, 4160), (2, 2065, 4160), (1, 2100, 4144), (2, 100, 1040),
+                                   (2, 300, 8208), (1, 4096, 16400)])
+def test_fused_and_split_decode(M, N, K):
+    run_case(M, N, K, seed=7 * M + N + K)
+
+
 def test_heavy_tails_and_direct_ternary():
     run_case(64, 512, 1024, seed=5, dist="t3")
     run_case(3, 777, 528, seed=6, latent=False)
