@@ -197,7 +197,7 @@ int bitlinear_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t
  *          aligned: split-K partial sums (decode kernels, and the tiled
  *          kernel when its 32 x 128 tiles leave CUs idle over a long K), or
  *          room for the activation row sums of the tiled kernel
- * Kernel by size: M <= 4 the dot4 GEMV (M <= 2 with a short K loop per
+ * Kernel by size: M <= 4 the dot4 GEMV (with a short K loop per
  * 64-row group: one workgroup per group whose wavefronts split K and add
  * their sums in LDS; otherwise K split over workgroups, with partial sums
  * in ws and a second launch); 4 < M <= 16 the streaming MFMA kernel; M > 16
@@ -230,7 +230,7 @@ int bitlinear_forward_xsum(const int8_t* xq, const float* eta, const int32_t* xs
 /*
  * Fused forward from float32 activations: quantize (into the workspace, with
  * the row sums for bitlinear_forward_xsum), contract, dequantize.  Same
- * arguments as above; ws is required.  At one or two tokens, on the shapes
+ * arguments as above; ws is required.  At up to four tokens, on the shapes
  * where bitlinear_forward takes the one-workgroup-per-row-group dot4 kernel
  * (and K <= 16384), that kernel quantizes the rows itself in one launch; x~
  * and eta still land in the workspace, the row sums do not.
@@ -342,7 +342,7 @@ int bitlinear_forward3(const int8_t* xq, const float* eta, const uint8_t* packed
  * each forward then queues at most three kernels: quantize all, contract all,
  * and -- for a plan too small to fill the chip, whose long K loops the
  * planner splits -- add the split partial sums and dequantize.  A plan of up
- * to two tokens too small to fill the chip (one transformer block, say), with
+ * to four tokens too small to fill the chip (one transformer block, say), with
  * every K at most 16384, queues one kernel that quantizes, contracts and
  * dequantizes; it writes xq and eta of problems with x != NULL all the same.
  * A plan of base-3 problems (format BITLINEAR_FORMAT_BASE3, up to 8 tokens)

@@ -249,7 +249,7 @@ bool fused_gemv_plan(const std::vector<Problem>& problems, int64_t M) {
     if (M <= 0 || M > kFusedMaxM) return false;
     int64_t groups = 0;
     for (const Problem& p : problems) {
-        if (p.K > kFusedMaxK) return false;
+        if (p.K > kFusedMaxK || M * ceil_div(p.K, 64) * 64 > kFusedMaxLds) return false;
         groups += ceil_div(p.N, 64);
     }
     return groups < kGemvSmallWaves;
@@ -713,7 +713,7 @@ static int forward_f32_common(const float* x, const uint8_t* packed, float gamma
     void* rest = (char*)ws + w.xq + w.eta + w.xsum;
     hipStream_t s = (hipStream_t)stream;
     clear_hip_error();
-    // One or two tokens on a shape the fused decode kernel takes: each
+    // Up to four tokens on a shape the fused decode kernel takes: each
     // workgroup quantizes the rows itself, one launch (x~ and eta still land
     // in the workspace; no row sums, which no decode kernel reads).
     if (!rmsnorm && K <= kFusedMaxK && forward_path(M, N) == Path::Gemv && gemv_fused_single(M, N, K))

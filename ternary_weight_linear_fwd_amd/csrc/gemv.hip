@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs a) {
     }
 }
 
-// ---- fused grouped decode (M <= 2, small plans)
+// ---- fused decode (M <= 4: small grouped plans, short single calls)
 //
 // A plan too small to fill the chip (one transformer block at a few tokens:
 // 520 row groups for hidden 3200 / FFN 8640) gives each (problem, 64-row
@@ -194,8 +194,9 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs a) {
 // would.  No second launch, no partial sums in memory.
 constexpr int kFusedWaves = 8;
 constexpr int kFusedThreads = 64 * kFusedWaves;
-// k-blocks in flight per wavefront (registers: six wavefronts per SIMD, so
-// that three 8-wave workgroups fit on a CU)
+// k-blocks in flight per wavefront (registers: up to two tokens six
+// wavefronts per SIMD, so that three 8-wave workgroups fit on a CU; three
+// and four tokens four, two workgroups)
 template <int M>
 constexpr int fused_batch() { return M == 1 ? 12 : 8; }
 constexpr int kFusedChunks = kFusedMaxK / 4 / kFusedThreads;   // float4 of a row per thread
@@ -227,7 +228,7 @@ __device__ __forceinline__ void dot_block_lds(Acc<M>& acc, const uint4 w, const 
 // SINGLE: one problem given by value (x = NULL: x~ and eta given), row group
 // = blockIdx.x; otherwise (problem, row group) from the grouped table.
 template <int M, bool SINGLE>
-__global__ __launch_bounds__(kFusedThreads, 6) void gemv_fused_kernel(const Problem* __restrict__ problems,
+__global__ __launch_bounds__(kFusedThreads, M <= 2 ? 6 : 4) void gemv_fused_kernel(const Problem* __restrict__ problems,
                                                                    const Unit* __restrict__ units, int64_t nunits,
                                                                    Problem single) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // [M][Kb * 64] x~, zero at k >= K
@@ -374,6 +375,12 @@ int launch_gemv_fused(const Problem* problems, const Unit* units, int64_t nunits
         case 2:
             hipLaunchKernelGGL((gemv_fused_kernel<2, false>), grid, block, lds, stream, problems, units, nunits, none);
             break;
+        case 3:
+            hipLaunchKernelGGL((gemv_fused_kernel<3, false>), grid, block, lds, stream, problems, units, nunits, none);
+            break;
+        case 4:
+            hipLaunchKernelGGL((gemv_fused_kernel<4, false>), grid, block, lds, stream, problems, units, nunits, none);
+            break;
         default: return BITLINEAR_EUNSUPPORTED;
     }
     BL_LAUNCH_CHECK();
@@ -387,8 +394,9 @@ int launch_gemv_fused(const Problem* problems, const Unit* units, int64_t nunits
 // kFusedSingleGroups groups, and the x~ rows fit the LDS.  Measured on
 // MI355X against the split GEMV and its epilogue (graph replay, weights
 // cycled): 2048 x 2048 at one token 5.5 -> 4.0 us, 8640 x 3200 7.0 -> 5.1,
-// 28672 x 8192 16.4 -> 14.2; the long-K runs it leaves to the split GEMV
-// (8192 x 28672 16.2 against 19.4 fused; 1024 x 8192 6.3 against 6.9).
+// 28672 x 8192 16.4 -> 14.2, at four tokens 31.6 -> 20.7; the long-K runs
+// it leaves to the split GEMV (8192 x 28672 16.2 against 19.4 fused;
+// 1024 x 8192 6.3 against 6.9).
 constexpr int64_t kFusedSingleGroups = 32;
 constexpr int64_t kFusedSingleMaxLds = 32 * 1024;
 
@@ -402,10 +410,13 @@ int launch_gemv_fused_single(const Problem& p, int64_t M, hipStream_t stream) {
     if (p.x && p.K > kFusedMaxK) return BITLINEAR_EUNSUPPORTED;
     const size_t lds = (size_t)M * (size_t)(p.Kb * 64);
     const dim3 grid((unsigned)ceil_div(p.N, 64)), block(kFusedThreads);
-    if (M == 1)
-        hipLaunchKernelGGL((gemv_fused_kernel<1, true>), grid, block, lds, stream, nullptr, nullptr, 0, p);
-    else
-        hipLaunchKernelGGL((gemv_fused_kernel<2, true>), grid, block, lds, stream, nullptr, nullptr, 0, p);
+    switch (M) {
+        case 1: hipLaunchKernelGGL((gemv_fused_kernel<1, true>), grid, block, lds, stream, nullptr, nullptr, 0, p); break;
+        case 2: hipLaunchKernelGGL((gemv_fused_kernel<2, true>), grid, block, lds, stream, nullptr, nullptr, 0, p); break;
+        case 3: hipLaunchKernelGGL((gemv_fused_kernel<3, true>), grid, block, lds, stream, nullptr, nullptr, 0, p); break;
+        case 4: hipLaunchKernelGGL((gemv_fused_kernel<4, true>), grid, block, lds, stream, nullptr, nullptr, 0, p); break;
+        default: return BITLINEAR_EUNSUPPORTED;
+    }
     BL_LAUNCH_CHECK();
     return BITLINEAR_OK;
 }

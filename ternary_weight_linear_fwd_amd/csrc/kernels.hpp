@@ -79,7 +79,10 @@ int launch_gemv_grouped(const Problem* problems, const Unit* units, int64_t nuni
 // loop across its wavefronts and dequantizes -- one launch, no partial sums
 // in memory.  Problems' K at most kFusedMaxK; max_K the longest of them.
 constexpr int kFusedMaxK = 16384;
-constexpr int kFusedMaxM = 2;
+constexpr int kFusedMaxM = 4;
+// x~ rows of a fused workgroup in LDS (M * ceil(K / 64) * 64 bytes), at most:
+// with the kernel's 8 KB of partial sums a workgroup stays within 64 KB.
+constexpr int64_t kFusedMaxLds = 56 * 1024;
 int launch_gemv_fused(const Problem* problems, const Unit* units, int64_t nunits, int64_t M, int64_t max_K,
                       hipStream_t stream);
 // The same kernel on one problem (row group = workgroup), where

@@ -294,15 +294,15 @@ def test_grouped_planner_splits_only_small_plans():
              (8192, 28672)]
     groups64 = sum((N + 63) // 64 for N, _ in block)
     blocks256 = sum((N + 255) // 256 for N, _ in block)
-    # fused dot4 GEMV (M <= 2): one unit per 64-row group, no partial sums
+    # fused dot4 GEMV (M <= 4): one unit per 64-row group, no partial sums
     assert plan_bytes(block, 2) == plan_bytes(block, 1)
-    # dot4 GEMV with split K (M = 3, 4): 64-row units, partial sums per token
-    assert plan_bytes(block, 4) - plan_bytes(block, 3) >= groups64 * 64 * 4
+    assert plan_bytes(block, 4) == plan_bytes(block, 3) == plan_bytes(block, 1)
     assert plan_bytes(model, 2, copies=80) == plan_bytes(model, 1, copies=80)
     assert plan_bytes(model, 4, copies=80) == plan_bytes(model, 3, copies=80)
-    # K past the fused kernel's LDS (16384): M = 2 splits K instead
+    # K past the fused kernel's limit (16384): the dot4 GEMV splits K instead,
+    # 64-row units with partial sums per token
     long_k = [(256, 20480), (128, 4096)]
-    assert plan_bytes(long_k, 2) - plan_bytes(long_k, 1) >= 0
+    assert plan_bytes(long_k, 4) - plan_bytes(long_k, 3) >= (256 // 64 + 128 // 64) * 64 * 4
     # streaming MFMA kernel (5 .. 16 tokens): 256-row units
     assert plan_bytes(block, 9) - plan_bytes(block, 8) >= blocks256 * 256 * 4
     assert plan_bytes(model, 9, copies=80) == plan_bytes(model, 8, copies=80)

@@ -56,12 +56,13 @@ def test_ragged_shapes(M, N, K):
     run_case(M, N, K, seed=M * 131 + N * 7 + K)
 
 
-# One or two tokens: the fused kernel (one workgroup per 64-row group, K split
+# Up to four tokens: the fused kernel (one workgroup per 64-row group, K split
 # among its wavefronts) where each wavefront's run is short, the split GEMV
 # and its epilogue where it is long; ragged N, K with a tail block, both
 # paths from int8 and from float32.
 @pytest.mark.parametrize("M,N,K", [(1, 2065, 4160), (2, 2065, 4160), (1, 2100, 4144), (2, 100, 1040),
-                                   (2, 300, 8208), (1, 4096, 16400)])
+                                   (2, 300, 8208), (1, 4096, 16400), (3, 2065, 4160), (4, 2100, 4144),
+                                   (4, 28672, 8192), (4, 300, 8208), (3, 1000, 1040)])
 def test_fused_and_split_decode(M, N, K):
     run_case(M, N, K, seed=7 * M + N + K)
 

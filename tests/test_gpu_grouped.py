@@ -41,7 +41,7 @@ def test_grouped_block_matches_oracle(M):
     tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
     table = torch.empty(tb, dtype=torch.uint8, device="cuda")
     plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
-    if M <= 2:   # fused: every workgroup quantizes its own rows, no quantize stage
+    if M <= 4:   # fused: every workgroup quantizes its own rows, no quantize stage
         assert plan.quant_rows == 0 and plan.units == sum((p.N + 63) // 64 for p in S.C2_PROJS)
     else:
         assert plan.quant_rows == 5 * M      # q/k/v quantized once
@@ -158,14 +158,16 @@ def test_grouped_mixed_row_lengths(M):
 
 
 # A small grouped plan (too few row blocks to fill the chip) splits long K
-# loops: in the dot4 GEMV up to 4 tokens, the streaming MFMA kernel up to 16,
-# 64 x 256 prefill tiles above.  Problems whose K gives one to many slices (a 16-k problem stays
-# whole), ragged M, N and K, run twice on the same table.
-@pytest.mark.parametrize("M", [2, 4, 12, 24, 64, 65, 128, 200])
-def test_grouped_split_k_small_plan(M):
+# loops: in the dot4 GEMV up to 4 tokens (where some K is past the fused
+# kernel's 16384), the streaming MFMA kernel up to 16, 64 x 256 prefill
+# tiles above.  Problems whose K gives one to many slices (a 16-k problem
+# stays whole), ragged M, N and K, run twice on the same table.
+@pytest.mark.parametrize("M,long_k", [(2, False), (4, False), (3, True), (4, True), (12, False), (24, False),
+                                      (64, False), (65, False), (128, False), (200, False)])
+def test_grouped_split_k_small_plan(M, long_k):
     torch = torch_cuda()
     L = bl()
-    shapes = [(300, 4160), (64, 16), (1000, 11008), (257, 2064)]
+    shapes = [(300, 4160), (64, 16), (1000, 11008), (257, 2064)] + ([(200, 20480)] if long_k else [])
     specs, refs = [], []
     for i, (N, K) in enumerate(shapes):
         say(f"grouped split plan M={M} problem {i}: N={N} K={K}")
@@ -184,10 +186,10 @@ def test_grouped_split_k_small_plan(M):
     table = torch.empty(tb, dtype=torch.uint8, device="cuda")
     plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
     # split: more work units than row blocks (64 rows per unit for the
-    # dot4 GEMV, 256 otherwise), and the partials in the table; up to two
-    # tokens the fused kernel takes whole K loops instead
+    # dot4 GEMV, 256 otherwise), and the partials in the table; up to four
+    # tokens with every K at most 16384 the fused kernel takes whole K loops
     width = 64 if M <= 4 else 256
-    if M <= 2:
+    if M <= 4 and not long_k:
         assert plan.units == sum((N + 63) // 64 for N, _ in shapes) and plan.quant_rows == 0
     else:
         assert plan.units > sum((N + width - 1) // width for N, _ in shapes)
@@ -237,16 +239,17 @@ def test_grouped_prefill_tiles(M, shapes):
         assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
 
 
-# The fused small-plan decode (M <= 2: quantize, whole-K contraction and
+# The fused small-plan decode (M <= 4: quantize, whole-K contraction and
 # dequant in one launch): problems fed from float32 rows and from already
 # quantized ones in one plan, a shared float32 input, ragged N, K with tail
 # blocks, the longest K the fused kernel takes (16384) and the shortest (16),
 # all-zero rows, int8 extremes; x~, eta, y_int and y against the oracle, twice.
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 def test_grouped_fused_decode(M):
     torch = torch_cuda()
     L = bl()
-    shapes = [(300, 4144), (64, 16), (1000, 16384), (257, 2064), (130, 1040), (65, 1040)]
+    # the longest K the fused kernel takes: 16384, or what its 56 KB of x~ rows allow
+    shapes = [(300, 4144), (64, 16), (1000, 16384 if M <= 3 else 14336), (257, 2064), (130, 1040), (65, 1040)]
     xs = {K: S.random_x(400 + K + M, M, K, "t3") for _, K in shapes}
     xs[2064][0] = 0.0                                     # an all-zero row
     xs[16][M - 1] = np.float32(3.0e38) * (np.arange(16) % 2 * 2 - 1)   # |x| at the float32 top
@@ -331,7 +334,7 @@ def test_plan_unit_order(case):
     fmt2, fmt3 = L.BITLINEAR_FORMAT_2BIT, L.BITLINEAR_FORMAT_BASE3
     shapes, M, fmt, kernel = {"gemv": (big, 1, fmt2, 0), "fused": (small, 1, fmt2, 7),
                               "skinny": (big, 16, fmt2, 2), "base3": (big, 1, fmt3, 8),
-                              "split": (small, 3, fmt2, 6)}[case]
+                              "split": (small + [(256, 20480)], 3, fmt2, 6)}[case]
     plan, units = _plan_units(L, torch, shapes, M, fmt)
     assert plan.kernel == kernel
     if fmt == fmt3:
