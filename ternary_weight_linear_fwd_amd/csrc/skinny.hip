@@ -43,6 +43,11 @@ struct SkinnyArgs {
     int32_t M;
 };
 
+// Buffer descriptor word 3 of a raw (untyped, 32-bit element) buffer, and
+// the cache-policy bits of a store written through the L2 at device scope.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kStoreDeviceScope = 16;
+
 // One 16-byte-per-lane direct global->LDS load (the wave's 64 lanes fill 1 KB).
 __device__ __forceinline__ void skinny_dma16(const void* src, void* lds_dst) {
     __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
@@ -196,12 +201,18 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
             __syncthreads();
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const int idx = t + 256 * q;
-                const int row = idx >> 6, c4 = idx & 63;
+                // A wavefront stores one token row's 1 KB run (row is the
+                // same on all its lanes), through a buffer descriptor on that
+                // run so that the store can carry the device-scope policy:
+                // written through the XCD's L2 at once (1% faster over the
+                // 70B-shaped sweep at 16 tokens than non-temporal stores, 3%
+                // than plain write-back ones).
+                const int row = __builtin_amdgcn_readfirstlane((t >> 6) + 4 * q), c4 = t & 63;
                 const int64_t m = 8 * h + row, n = n0 + c4 * 4;
                 if (m >= M || n >= N) continue;   // N % 4 == 0: a float4 is wholly inside or outside
-                const nv_f32x4 v = *reinterpret_cast<const nv_f32x4*>(stage + row * 256 + c4 * 4);
-                __builtin_nontemporal_store(v, reinterpret_cast<nv_f32x4*>(p.y + m * N + n));
+                const nv_u32x4 v = *reinterpret_cast<const nv_u32x4*>(stage + row * 256 + c4 * 4);
+                __amdgpu_buffer_rsrc_t run = __builtin_amdgcn_make_buffer_rsrc(p.y + m * N + n0, 0, 1024, kBufferRsrcWord3);
+                __builtin_amdgcn_raw_buffer_store_b128(v, run, c4 * 16, 0, kStoreDeviceScope);
             }
         }
         return;
