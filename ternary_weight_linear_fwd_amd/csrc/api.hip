@@ -806,7 +806,9 @@ int bitlinear_forward_grouped(const bitlinear_grouped_plan* plan, void* stream) 
     hipStream_t s = (hipStream_t)stream;
     clear_hip_error();
     int rc = BITLINEAR_OK;
-    if (plan->quant_rows) rc = launch_quantize_grouped(rows, plan->quant_rows, s);
+    if (plan->quant_rows)
+        rc = launch_quantize_grouped(rows, plan->quant_rows,
+                                     plan->kernel != kPlanGemv && plan->kernel != kPlanGemvSplit, s);
     if (rc) return rc;
     switch (plan->kernel) {
         case kPlanGemv: return launch_gemv_grouped(problems, units, plan->units, plan->M, nullptr, s);

@@ -49,7 +49,9 @@ struct SplitK {
 // ---- activation quantization (quant.hip)
 int launch_quantize(const float* x, int64_t M, int64_t K, int8_t* xq, float* eta, int32_t* xsum,
                     hipStream_t stream);
-int launch_quantize_grouped(const QuantRow* rows, int64_t nrows, hipStream_t stream);
+// nontemporal: x~ stored non-temporally (for contraction kernels that stage
+// it through LDS rather than read it through the scalar cache).
+int launch_quantize_grouped(const QuantRow* rows, int64_t nrows, bool nontemporal, hipStream_t stream);
 
 // ---- weight quantization and packing (pack.hip)
 constexpr int kGammaBins = 256;  // bins[t] collects significands of 2^(t-149) units

@@ -432,10 +432,10 @@ __device__ void rmsnorm_quant_row(const float* __restrict__ x, int64_t K, int8_t
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int64_t i = t + (int64_t)r * THREADS;
-            if (i < n4) q4[i] = quant4(mul4(cache[r], norm), eta, sum);
+            if (i < n4) __builtin_nontemporal_store(quant4(mul4(cache[r], norm), eta, sum), q4 + i);
         }
     } else {
-        for (int64_t i = t; i < n4; i += THREADS) q4[i] = quant4(mul4(x4[i], norm), eta, sum);
+        for (int64_t i = t; i < n4; i += THREADS) __builtin_nontemporal_store(quant4(mul4(x4[i], norm), eta, sum), q4 + i);
     }
     if (t == 0) {
         eta_out[0] = eta;
