@@ -57,6 +57,22 @@ __device__ __forceinline__ float4 ldnt_f4(const void* p) {
 typedef const __attribute__((address_space(1))) nv_u32x4 gnv_u32x4;
 typedef const __attribute__((address_space(1))) nv_f32x4 gnv_f32x4;
 
+// Buffer descriptor word 3 of a raw (untyped, 32-bit element) buffer, and
+// cache-policy bits of buffer accesses: a store written through the L2 at
+// device scope (sc1), a non-temporal load (nt).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kStoreDeviceScope = 16;
+constexpr int kLoadNonTemporal = 2;
+
+// A pointer that is the same in every lane of the wavefront, moved to scalar
+// registers (only for values that are wave-uniform by construction).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ uint4 ldgnt_u4(const void* p) {
     const nv_u32x4 v = __builtin_nontemporal_load((gnv_u32x4*)p);
     return make_uint4(v.x, v.y, v.z, v.w);

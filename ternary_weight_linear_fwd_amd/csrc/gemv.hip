@@ -252,7 +252,6 @@ __global__ __launch_bounds__(kFusedThreads, M <= 2 ? 6 : 4) void gemv_fused_kern
     const int64_t nbw = (Kb + kFusedWaves - 1) / kFusedWaves;
     const int64_t kb0 = (int64_t)wave * nbw;
     const int64_t kb1 = kb0 + nbw < Kb ? kb0 + nbw : Kb;
-    const uint4* wp = p.packed + (g * Kb) * 64 + lane;
 
     // x~ rows into LDS, with eta and sum x~ per row (the float32 chunks and the
     // weight words below are never live together: registers for occupancy).
@@ -312,37 +311,59 @@ __global__ __launch_bounds__(kFusedThreads, M <= 2 ? 6 : 4) void gemv_fused_kern
 
     __syncthreads();   // x~, eta and the row sums are in LDS (a full barrier: no loads in flight here)
 
-    // The run's k-blocks, up to kFusedBatch in flight.
+    // The run's k-blocks, up to kFusedBatch in flight, through a buffer
+    // descriptor on exactly the run: the run bounds and the group's weight
+    // rows are the same for every lane (scalar registers), and a load past
+    // the run returns zeros without touching memory.  So every load is
+    // issued unconditionally and the compiler counts the loads in flight
+    // exactly, waiting for one block at a time.
     constexpr int kFusedBatch = fused_batch<M>();
+    const int rb0 = __builtin_amdgcn_readfirstlane((int)kb0);
+    const int run = __builtin_amdgcn_readfirstlane((int)(kb1 > kb0 ? kb1 - kb0 : 0));
+    const uint8_t* wrun = uniform_ptr(reinterpret_cast<const uint8_t*>(p.packed + (g * Kb + rb0) * 64));
+    const __amdgpu_buffer_rsrc_t wres =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wrun), 0, run * 1024, kBufferRsrcWord3);
+    const int wl = lane * 16;
+    auto wload = [&](int j) {   // block rb0 + j of the run (zeros past its end)
+        // The whole offset in the vector operand: the range check covers the
+        // vector and instruction offsets, not the scalar one.
+        const nv_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wres, wl + j * 1024, 0, kLoadNonTemporal);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    };
+    // Nothing is in flight here (the barrier above follows the last
+    // activation load); saying so keeps the compiler from carrying a load it
+    // cannot see completed on some path (one thread's eta read) into the
+    // weight loads, where it would wait for all of them.
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
     uint4 wq[kFusedBatch];
 #pragma unroll
-    for (int i = 0; i < kFusedBatch; ++i)
-        if (kb0 + i < kb1) wq[i] = ldgnt_u4(wp + (kb0 + i) * 64);
-
-    // Row group 0 hands x~ and eta on, as the quantize stage does.
-    if (g == 0 && p.x) {
-        for (int m = 0; m < M; ++m) {
-            const uint4* src = reinterpret_cast<const uint4*>(xs + m * kpad);
-            uint4* dst = reinterpret_cast<uint4*>(const_cast<int8_t*>(p.xq) + m * K);
-            for (int64_t i = t; i < K / 16; i += kFusedThreads) dst[i] = src[i];
-            if (t == 0) const_cast<float*>(p.eta)[m] = eta_sh[m];
-        }
-    }
+    for (int i = 0; i < kFusedBatch; ++i) wq[i] = wload(i);
 
     Acc<M> acc;
 #pragma unroll
     for (int m = 0; m < M; ++m) acc.a0[m] = acc.a1[m] = acc.a2[m] = 0;
+    // The registers form a ring: as soon as slot i's block has been used the
+    // slot is refilled with the block kFusedBatch further on, so a run longer
+    // than one batch keeps kFusedBatch loads in flight instead of waiting a
+    // second memory round trip for its tail.  Every block of a round before
+    // the last lies inside the run.
+    const int rounds = (run + kFusedBatch - 1) / kFusedBatch;
+    for (int r = 0; r + 1 < rounds; ++r) {
 #pragma unroll
-    for (int i = 0; i < kFusedBatch; ++i)
-        if (kb0 + i < kb1) dot_block_lds<M>(acc, wq[i], xs, kpad, kb0 + i);
-    // Runs longer than one batch.
-    for (int64_t kb = kb0 + kFusedBatch; kb < kb1; kb += kFusedBatch) {
+        for (int i = 0; i < kFusedBatch; ++i) {
+            dot_block_lds<M>(acc, wq[i], xs, kpad, rb0 + r * kFusedBatch + i);
+            wq[i] = wload((r + 1) * kFusedBatch + i);
+            // Keep each refill right after its slot's use: left to itself the
+            // scheduler gathers the refills at the end of the round, which
+            // turns the ring back into batches.
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (rounds > 0) {
+        const int last = (rounds - 1) * kFusedBatch;
 #pragma unroll
         for (int i = 0; i < kFusedBatch; ++i)
-            if (kb + i < kb1) wq[i] = ldgnt_u4(wp + (kb + i) * 64);
-#pragma unroll
-        for (int i = 0; i < kFusedBatch; ++i)
-            if (kb + i < kb1) dot_block_lds<M>(acc, wq[i], xs, kpad, kb + i);
+            if (last + i < run) dot_block_lds<M>(acc, wq[i], xs, kpad, rb0 + last + i);
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) part[wave][m][lane] = acc.a0[m] + (acc.a1[m] >> 2) + (acc.a2[m] >> 4);
@@ -358,6 +379,16 @@ __global__ __launch_bounds__(kFusedThreads, M <= 2 ? 6 : 4) void gemv_fused_kern
         if (row < N) {
             p.y[m * N + row] = dequant(v, dequant_scale(eta_sh[m], p.gamma));
             if (p.y_int) p.y_int[m * N + row] = v;
+        }
+    }
+
+    // Row group 0 hands x~ and eta on, as the quantize stage does.
+    if (g == 0 && p.x) {
+        for (int m = 0; m < M; ++m) {
+            const uint4* src = reinterpret_cast<const uint4*>(xs + m * kpad);
+            uint4* dst = reinterpret_cast<uint4*>(const_cast<int8_t*>(p.xq) + m * K);
+            for (int64_t i = t; i < K / 16; i += kFusedThreads) dst[i] = src[i];
+            if (t == 0) const_cast<float*>(p.eta)[m] = eta_sh[m];
         }
     }
 }

@@ -43,10 +43,6 @@ struct SkinnyArgs {
     int32_t M;
 };
 
-// Buffer descriptor word 3 of a raw (untyped, 32-bit element) buffer, and
-// the cache-policy bits of a store written through the L2 at device scope.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-constexpr int kStoreDeviceScope = 16;
 
 // One 16-byte-per-lane direct global->LDS load (the wave's 64 lanes fill 1 KB).
 __device__ __forceinline__ void skinny_dma16(const void* src, void* lds_dst) {
