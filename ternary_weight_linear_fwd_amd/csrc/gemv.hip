@@ -120,29 +120,47 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs a) {
 #pragma unroll
     for (int m = 0; m < M; ++m) acc.a0[m] = acc.a1[m] = acc.a2[m] = 0;
 
-    // Main loop: batches of U complete k-blocks, the next batch in flight
-    // while the current one is consumed.
-    int64_t kb = kb0;
-    if (kb + U <= kend) {
-        uint4 cur[U];
+    // Main loop over the complete k-blocks of the range: a ring of U
+    // registers, each refilled with the block U further on right after its
+    // use, so U loads stay in flight all along.  The loads go through a
+    // buffer descriptor on exactly those blocks (wave-uniform, in scalar
+    // registers): one past the end returns zeros without touching memory, so
+    // every load is issued unconditionally and the compiler waits for one
+    // block at a time.
+    const int rk0 = __builtin_amdgcn_readfirstlane((int)kb0);
+    const int run = __builtin_amdgcn_readfirstlane((int)(kend > kb0 ? kend - kb0 : 0));
+    {
+        const uint8_t* wrun = uniform_ptr(reinterpret_cast<const uint8_t*>(p.packed + (g * p.Kb + rk0) * 64));
+        const __amdgpu_buffer_rsrc_t wres =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wrun), 0, run * 1024, kBufferRsrcWord3);
+        const int wl = lane * 16;
+        auto wload = [&](int j) {   // block rk0 + j (zeros past the range)
+            // The whole offset in the vector operand: the range check covers
+            // the vector and instruction offsets, not the scalar one.
+            const nv_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wres, wl + j * 1024, 0, kLoadNonTemporal);
+            return make_uint4(v.x, v.y, v.z, v.w);
+        };
+        uint4 wq[U];
 #pragma unroll
-        for (int i = 0; i < U; ++i) cur[i] = ldnt_u4(wp + (kb + i) * 64);
-        for (; kb + U <= kend; kb += U) {
-            uint4 nxt[U];
-            const bool more = kb + 2 * U <= kend;
-            if (more) {
+        for (int i = 0; i < U; ++i) wq[i] = wload(i);
+        const int rounds = (run + U - 1) / U;
+        for (int r = 0; r + 1 < rounds; ++r) {   // every block of these rounds is inside the range
 #pragma unroll
-                for (int i = 0; i < U; ++i) nxt[i] = ldnt_u4(wp + (kb + U + i) * 64);
-            }
-#pragma unroll
-            for (int i = 0; i < U; ++i) dot_block<M>(acc, cur[i], xs, xstride, kb + i, 4);
-            if (more) {
-#pragma unroll
-                for (int i = 0; i < U; ++i) cur[i] = nxt[i];
+            for (int i = 0; i < U; ++i) {
+                dot_block<M>(acc, wq[i], xs, xstride, rk0 + r * U + i, 4);
+                wq[i] = wload((r + 1) * U + i);
+                // Each refill right after its slot's use (the scheduler would
+                // gather them at the end of the round).
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        if (rounds > 0) {
+            const int last = (rounds - 1) * U;
+#pragma unroll
+            for (int i = 0; i < U; ++i)
+                if (last + i < run) dot_block<M>(acc, wq[i], xs, xstride, rk0 + last + i, 4);
+        }
     }
-    for (; kb < kend; ++kb) dot_block<M>(acc, ldnt_u4(wp + kb * 64), xs, xstride, kb, 4);
     // Partial last block (K % 64 in {16, 32, 48}): only its valid words.
     if (kb1 > kfull && kb0 <= kfull && (K & 63)) {
         dot_block<M>(acc, ldnt_u4(wp + kfull * 64), xs, xstride, kfull,
