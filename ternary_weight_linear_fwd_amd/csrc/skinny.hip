@@ -180,6 +180,14 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
         float* stage = reinterpret_cast<float*>(lds);   // [8][256]
         const int t = threadIdx.x;
         const int64_t n0 = blk * kSkinnyRows;
+        // The scales of this lane's four token rows, their loads issued
+        // together (rows past M read row 0 and are never stored).
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = lg * 4 + r;
+            sc[r] = dequant_scale(p.eta[m < M ? m : 0], p.gamma);
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             __syncthreads();   // the last K step's reads (or the previous half's stores) are done
@@ -188,10 +196,9 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int m = lg * 4 + r;
                     if ((m >> 3) != h || m >= M) continue;
-                    const float sc = dequant_scale(p.eta[m], p.gamma);
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt)
-                        stage[(m & 7) * 256 + wave * 64 + tt * 16 + nl] = dequant(acc[0][tt][r] - accs[0][r], sc);
+                        stage[(m & 7) * 256 + wave * 64 + tt * 16 + nl] = dequant(acc[0][tt][r] - accs[0][r], sc[r]);
                 }
             }
             __syncthreads();
@@ -215,13 +222,22 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(SkinnyArgs a) {
     }
     // Epilogue: element r of tile (i, t) is row 16i + 4lg + r, column 16t + nl.
     if (!group_ok) return;
+    // The scales of this lane's rows, their loads issued together.
+    float sc[MT][4];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t m = i * 16 + lg * 4 + r;
+            sc[i][r] = split ? 0.0f : dequant_scale(p.eta[m < M ? m : 0], p.gamma);
+        }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t m = i * 16 + lg * 4 + r;
             if (m >= M) continue;
-            const float s = split ? 0.0f : dequant_scale(p.eta[m], p.gamma);
+            const float s = sc[i][r];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int64_t n = g * 64 + t * 16 + nl;
