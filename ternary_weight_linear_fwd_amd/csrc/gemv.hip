@@ -486,6 +486,7 @@ __global__ __launch_bounds__(64) void splitk_epilogue_kernel(const int32_t* __re
     const int64_t MN = M * N;
     if (i >= MN) return;
     const int64_t m = i / N;
+    const float sc = dequant_scale(eta[m], gamma);   // its load goes out before the partials'
     int acc = 0;
     for (int s0 = 0; s0 < S; s0 += kEpiLoads) {
         int v[kEpiLoads];
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(64) void splitk_epilogue_kernel(const int32_t* __re
 #pragma unroll
         for (int j = 0; j < kEpiLoads; ++j) acc += v[j];
     }
-    y[i] = dequant(acc, dequant_scale(eta[m], gamma));
+    y[i] = dequant(acc, sc);
     if (y_int) y_int[i] = acc;
 }
 

@@ -336,6 +336,11 @@ __global__ __launch_bounds__(W) void grouped_splitk_epilogue_kernel(const Proble
     const int rows = M - m0 < kEpiRows ? (int)(M - m0) : kEpiRows;
     const int S = p.slices;
     const int32_t* __restrict__ src = gpart + (u * M + m0) * W + threadIdx.x;
+    // The rows' scales, loaded together with the partial sums (rows past M
+    // read row m0 and are never stored).
+    float sc[kEpiRows];
+#pragma unroll
+    for (int r = 0; r < kEpiRows; ++r) sc[r] = dequant_scale(p.eta[m0 + (r < rows ? r : 0)], p.gamma);
     int v[kEpiRows] = {};
     if (S <= kSkinnyMaxSlices) {
         // every slice's loads in flight at once (straight-line code)
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(W) void grouped_splitk_epilogue_kernel(const Proble
     for (int r = 0; r < kEpiRows; ++r) {
         if (r >= rows) break;
         const int64_t m = m0 + r;
-        p.y[m * p.N + n] = dequant(v[r], dequant_scale(p.eta[m], p.gamma));
+        p.y[m * p.N + n] = dequant(v[r], sc[r]);
         if (p.y_int) p.y_int[m * p.N + n] = v[r];
     }
 }
