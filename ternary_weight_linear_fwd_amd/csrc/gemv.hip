@@ -295,10 +295,11 @@ __global__ __launch_bounds__(kFusedThreads, M <= 2 ? 6 : 4) void gemv_fused_kern
 #pragma unroll
             for (int w = 1; w < kFusedWaves; ++w) amax = fmaxf(amax, red_max[m][w]);
             const float eta = amax < kScaleFloor ? kScaleFloor : amax;
+            const float rcp = quant_recip(eta);
 #pragma unroll
             for (int r = 0; r < kFusedChunks; ++r) {
                 const int64_t i = t + (int64_t)r * kFusedThreads;
-                if (i < n4) q4[i] = quant4(v[r], eta, sum);
+                if (i < n4) q4[i] = quant4(v[r], eta, rcp, sum);
             }
             if (t == 0) eta_sh[m] = eta;
         } else {

@@ -51,16 +51,17 @@ __device__ inline void quant_row(const float* __restrict__ x, int K, int8_t* __r
     }
     amax = block_max<THREADS>(amax, redf);
     const float eta = amax < kScaleFloor ? kScaleFloor : amax;
+    const float rcp = quant_recip(eta);
 
     int sum = 0;
     if constexpr (R > 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int i = t + r * THREADS;
-            if (i < n4) store_q4<NTS>(q4 + i, quant4(cache[r], eta, sum));
+            if (i < n4) store_q4<NTS>(q4 + i, quant4(cache[r], eta, rcp, sum));
         }
     }
-    for (int i = t + R * THREADS; i < n4; i += THREADS) store_q4<NTS>(q4 + i, quant4(x4[i], eta, sum));
+    for (int i = t + R * THREADS; i < n4; i += THREADS) store_q4<NTS>(q4 + i, quant4(x4[i], eta, rcp, sum));
     if (t == 0) eta_out[0] = eta;
     if (xsum_out) {
         sum = block_sum<THREADS>(sum, redi);

@@ -29,12 +29,42 @@ __device__ inline int8_t quant_one(float x, float eta) {
     return (int8_t)(int)r;
 }
 
-__device__ inline uint32_t quant4(float4 v, float eta, int& sum) {
-    int8_t a = quant_one(v.x, eta), b = quant_one(v.y, eta), c = quant_one(v.z, eta),
-           d = quant_one(v.w, eta);
-    sum += (int)a + (int)b + (int)c + (int)d;
-    return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
-           ((uint32_t)(uint8_t)d << 24);
+// The reciprocal the fast path of quant4 multiplies by: fl(1 / eta), or NaN
+// (no fast path) when it would be subnormal.  One per row.
+__device__ inline float quant_recip(float eta) {
+    return eta < 0x1p125f ? __fdiv_rn(1.0f, eta) : __builtin_nanf("");
+}
+
+// Four elements of quant_one, the same bits with a division only where it
+// can matter.  With a = fl(x * 127) and q = a / eta, |q| <= 127 (eta is at
+// least every |x| of the row), and p = fl(a * fl(1 / eta)) is within
+// |q| (2^-24 + 2^-24 + 2^-48) < 1.6e-5 of q, while fl(q) is within
+// |q| 2^-24 < 7.6e-6 of q.  So when p is farther than 2^-12 from every
+// half-integer, fl(q) lies strictly between the same two half-integers and
+// rint(fl(q)) = rint(p).  Otherwise (a tie or a near tie of fl(q), or a
+// non-finite p) the lane takes the IEEE division.
+__device__ inline uint32_t quant4(float4 v, float eta, float rcp, int& sum) {
+    const float a[4] = {__fmul_rn(v.x, kQb), __fmul_rn(v.y, kQb), __fmul_rn(v.z, kQb), __fmul_rn(v.w, kQb)};
+    float n[4];
+    bool exact = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float p = __fmul_rn(a[j], rcp);
+        n[j] = rintf(p);
+        exact |= !(fabsf(p - n[j]) < 0.5f - 0x1p-12f);   // also true for NaN / inf
+    }
+    if (exact) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) n[j] = rintf(__fdiv_rn(a[j], eta));
+    }
+    uint32_t out = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int8_t q = (int8_t)(int)fminf(fmaxf(n[j], -128.0f), 127.0f);
+        sum += (int)q;
+        out |= (uint32_t)(uint8_t)q << (8 * j);
+    }
+    return out;
 }
 
 // Block-wide reductions through LDS (one slot per wave).

@@ -426,16 +426,17 @@ __device__ void rmsnorm_quant_row(const float* __restrict__ x, int64_t K, int8_t
     const float norm = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, kRmsEps)));
     const float an = __fmul_rn(amax, norm);
     const float eta = an < kScaleFloor ? kScaleFloor : an;
+    const float rcp = quant_recip(eta);
 
     int sum = 0;
     if constexpr (R > 0) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int64_t i = t + (int64_t)r * THREADS;
-            if (i < n4) __builtin_nontemporal_store(quant4(mul4(cache[r], norm), eta, sum), q4 + i);
+            if (i < n4) __builtin_nontemporal_store(quant4(mul4(cache[r], norm), eta, rcp, sum), q4 + i);
         }
     } else {
-        for (int64_t i = t; i < n4; i += THREADS) __builtin_nontemporal_store(quant4(mul4(x4[i], norm), eta, sum), q4 + i);
+        for (int64_t i = t; i < n4; i += THREADS) __builtin_nontemporal_store(quant4(mul4(x4[i], norm), eta, rcp, sum), q4 + i);
     }
     if (t == 0) {
         eta_out[0] = eta;
