@@ -426,7 +426,7 @@ def bench_stream_ceiling(torch, L) -> dict:
     del buf
     return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "kernel": "stream_read_kernel: 4 GiB read once, one contiguous run per wavefront, 16-byte "
-                      "non-temporal loads, 16 in flight per lane, 4 wavefronts per SIMD"}
+                      "non-temporal loads, a ring of 24 in flight per lane, 4 wavefronts per SIMD"}
 
 
 def bench_rmsnorm(torch, L, S, reps: int):

@@ -12,7 +12,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kSinkWords = 16384;       // 64 KB: one word per workgroup
 constexpr int kStreamWavesPerSimd = 4;  // resident wavefronts of the read probe
-constexpr int kStreamDepth = 16;        // 16-byte loads in flight per lane
+constexpr int kStreamDepth = 24;        // 16-byte loads in flight per lane (ring)
 
 __device__ inline uint32_t wave_xor(uint32_t v) {
 #pragma unroll
@@ -20,28 +20,46 @@ __device__ inline uint32_t wave_xor(uint32_t v) {
     return v;
 }
 
-// Each wavefront streams one contiguous run of the buffer (1 KB wave loads,
-// kStreamDepth of them in flight per lane, non-temporal), the way the decode
-// kernels stream their weight rows; of the patterns tried on this part this
-// one reads fastest.  Runs are whole 1 KB rows of chunks except the last.
+// Each wavefront streams one contiguous run of the buffer, the way the
+// decode kernels stream their weight rows: 1 KB wave loads (64 lanes x 16
+// bytes, non-temporal), kStreamDepth of them in flight as a ring of
+// registers, a slot refilled with the block kStreamDepth further on right
+// after its use.  The loads go through a buffer descriptor on exactly the
+// run (loads past it return zeros without touching memory), so all are
+// issued unconditionally and the compiler waits for one block at a time.
+// Of the patterns tried on this part this one reads fastest (a ring of 24
+// at four wavefronts per SIMD: 7.05 TB/s; rings of 8 or 16, eight waves per
+// SIMD, or batches of 16 loads consumed together: 6.95 - 7.05).  Runs are
+// whole 1 KB rows of chunks except the last.
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, uint64_t n16,
                                                           uint32_t* __restrict__ sink) {
     const uint64_t waves = (uint64_t)gridDim.x * 4;
     const uint64_t w = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const uint64_t lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63;
     const uint64_t per = ((n16 + waves - 1) / waves + 63) & ~uint64_t(63);   // chunks per wavefront
     const uint64_t begin = w * per;
     const uint64_t end = begin + per < n16 ? begin + per : n16;
+    const int nblk = __builtin_amdgcn_readfirstlane((int)(end > begin ? (end - begin) / 64 : 0));
+    const uint8_t* run = uniform_ptr(reinterpret_cast<const uint8_t*>(p + (begin < n16 ? begin : 0)));
+    const __amdgpu_buffer_rsrc_t res =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(run), 0, nblk * 1024, kBufferRsrcWord3);
+    auto ld = [&](int j) { return __builtin_amdgcn_raw_buffer_load_b128(res, lane * 16 + j * 1024, 0, kLoadNonTemporal); };
+    nv_u32x4 v[kStreamDepth];
     uint32_t x = 0;
-    uint64_t j = begin;
-    for (; j + 64 * kStreamDepth <= end; j += 64 * kStreamDepth) {
-        uint4 v[kStreamDepth];
 #pragma unroll
-        for (int u = 0; u < kStreamDepth; ++u) v[u] = ldnt_u4(p + j + u * 64 + lane);
+    for (int i = 0; i < kStreamDepth; ++i) v[i] = ld(i);
+    const int rounds = (nblk + kStreamDepth - 1) / kStreamDepth;
+    for (int r = 0; r + 1 < rounds; ++r) {
 #pragma unroll
-        for (int u = 0; u < kStreamDepth; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        for (int i = 0; i < kStreamDepth; ++i) {
+            x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+            v[i] = ld((r + 1) * kStreamDepth + i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    for (j += lane; j < end; j += 64) {
+#pragma unroll
+    for (int i = 0; i < kStreamDepth; ++i) x ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;   // zeros past the run
+    for (uint64_t j = begin + (uint64_t)nblk * 64 + lane; j < end; j += 64) {
         const uint4 a = ldnt_u4(p + j);
         x ^= a.x ^ a.y ^ a.z ^ a.w;
     }
@@ -52,9 +70,6 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
     if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
-// Eight A fragments and eight expanded weight words per lane, loaded once;
-// each round issues the eight independent MFMAs (four accumulators) and
-// nothing else.
 __global__ __launch_bounds__(256, 2) void mfma_loop_kernel(const int8_t* __restrict__ xq,
                                                            const uint8_t* __restrict__ packed, int iters,
                                                            int32_t* __restrict__ sink) {
