@@ -135,8 +135,8 @@ __global__ __launch_bounds__(256) void gemv_dot4_kernel(GemvArgs a) {
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wrun), 0, run * 1024, kBufferRsrcWord3);
         const int wl = lane * 16;
         auto wload = [&](int j) {   // block rk0 + j (zeros past the range)
-            // The whole offset in the vector operand: the range check covers
-            // the vector and instruction offsets, not the scalar one.
+            // The whole offset in the vector operand, which the range check
+            // covers.
             const nv_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wres, wl + j * 1024, 0, kLoadNonTemporal);
             return make_uint4(v.x, v.y, v.z, v.w);
         };
@@ -344,8 +344,8 @@ __global__ __launch_bounds__(kFusedThreads, M <= 2 ? 6 : 4) void gemv_fused_kern
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wrun), 0, run * 1024, kBufferRsrcWord3);
     const int wl = lane * 16;
     auto wload = [&](int j) {   // block rb0 + j of the run (zeros past its end)
-        // The whole offset in the vector operand: the range check covers the
-        // vector and instruction offsets, not the scalar one.
+        // The whole offset in the vector operand, which the range check
+        // covers.
         const nv_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wres, wl + j * 1024, 0, kLoadNonTemporal);
         return make_uint4(v.x, v.y, v.z, v.w);
     };
