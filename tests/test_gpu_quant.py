@@ -73,3 +73,46 @@ def test_empty_rows():
     bl().bitlinear_quantize_act(x, 0, 64, xq, eta)   # M = 0: nothing written
     torch.cuda.synchronize()
     assert int(xq[0, 0]) == 7 and float(eta[0]) == 3.0
+
+
+def near_tie_rows():
+    """Rows whose quotients x * 127 / eta straddle half-integers k + 1/2 at
+    offsets on both sides of the quantizers' 2^-12 fast-path margin, and hit
+    them exactly; eta (the row's first element) varies from row to row."""
+    offs = np.array([0.0, 1e-7, -1e-7, 3e-6, -3e-6, 1e-5, -1e-5, 6e-5, -6e-5,
+                     2.3e-4, -2.3e-4, 2.6e-4, -2.6e-4, 1e-3, -1e-3])
+    q = ((np.arange(-126, 126) + 0.5)[:, None] + offs[None, :]).ravel()
+    K = ((q.size + 1 + 15) // 16) * 16
+    rows = []
+    for eta in (3.0, 0.7, 1e-3, 1.0e4, 2.0 ** -10, 127.0):
+        r = np.zeros(K, np.float32)
+        r[0] = eta
+        r[1:q.size + 1] = (q * eta / 127.0).astype(np.float32)
+        rows.append(r)
+    return np.stack(rows)
+
+
+def test_near_ties():
+    # the stand-alone quantizer
+    x = near_tie_rows()
+    check(x)
+    check(-x)
+
+
+def test_near_ties_fused_forward():
+    # the fused decode quantizes inside each workgroup: same rows, one and two
+    # tokens at a time, y compared bit for bit with the oracle's forward
+    from gpu_helpers import forward_f32, pack_weights
+    x = near_tie_rows()
+    M_all, K = x.shape
+    N = 192
+    W = S.random_latent(77, N, K)
+    packed, g = pack_weights(W)
+    Wt, g_ref = oracle.quantize_weights(W)
+    assert g == g_ref
+    for m0, m in ((0, 1), (1, 2), (3, 2), (5, 1)):
+        xs = x[m0:m0 + m]
+        say(f"near-tie fused forward rows {m0}..{m0 + m - 1} K={K}")
+        y = forward_f32(xs, packed, g, N)
+        y_ref, _, _, _ = oracle.forward(xs, Wt, g_ref)
+        assert np.array_equal(y.view(np.uint32), y_ref.view(np.uint32))
