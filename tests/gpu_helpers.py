@@ -140,3 +140,20 @@ def assert_y_close(y_gpu: np.ndarray, y_ref: np.ndarray):
     lim = REL_TOL * np.abs(y_ref.astype(np.float64))
     bad = err > lim
     assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:5].tolist())
+
+
+def near_tie_rows():
+    """Rows whose quotients x * 127 / eta straddle half-integers k + 1/2 at
+    offsets on both sides of the quantizers' 2^-12 fast-path margin, and hit
+    them exactly; eta (the row's first element) varies from row to row."""
+    offs = np.array([0.0, 1e-7, -1e-7, 3e-6, -3e-6, 1e-5, -1e-5, 6e-5, -6e-5,
+                     2.3e-4, -2.3e-4, 2.6e-4, -2.6e-4, 1e-3, -1e-3])
+    q = ((np.arange(-126, 126) + 0.5)[:, None] + offs[None, :]).ravel()
+    K = ((q.size + 1 + 15) // 16) * 16
+    rows = []
+    for eta in (3.0, 0.7, 1e-3, 1.0e4, 2.0 ** -10, 127.0):
+        r = np.zeros(K, np.float32)
+        r[0] = eta
+        r[1:q.size + 1] = (q * eta / 127.0).astype(np.float32)
+        rows.append(r)
+    return np.stack(rows)

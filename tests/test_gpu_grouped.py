@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import assert_y_close, bl, pack_weights, say, torch_cuda
+from gpu_helpers import assert_y_close, bl, near_tie_rows, pack_weights, say, torch_cuda
 from ternary_weight_linear_fwd_amd import synthetic as S
 
 pytestmark = pytest.mark.gpu
@@ -368,3 +368,40 @@ def test_plan_unit_order(case):
         for a, b in zip(run, run[1:]):
             if length(a) == length(b):
                 assert a < b
+
+
+@pytest.mark.parametrize("M", [2, 6, 8, 24])
+def test_grouped_near_tie_rows(M):
+    # The grouped quantizer (and the fused decode's own quantization at M <= 4)
+    # on rows whose quotients x * 127 / eta sit on and next to rounding ties
+    # (scaling a row by a power of two keeps every quotient): x~, eta and y
+    # bit for bit against the oracle.
+    torch = torch_cuda()
+    L = bl()
+    base = near_tie_rows()                                   # 6 rows, K = 3792
+    K = base.shape[1]
+    rows = np.concatenate([base * np.float32(sign * 2.0 ** e) for e in (0, 1, -1, 3) for sign in (1, -1)])
+    specs, refs = [], []
+    for i, N in enumerate((320, 1088)):
+        x_np = np.ascontiguousarray(rows[i * M:(i + 1) * M])
+        W = S.random_latent(900 + i, N, K)
+        packed, g = pack_weights(W)
+        Wt, _ = oracle.quantize_weights(W)
+        specs.append(dict(x=torch.from_numpy(x_np).cuda(), xq=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                          eta=torch.empty(M, dtype=torch.float32, device="cuda"), packed=packed,
+                          y=torch.empty((M, N), dtype=torch.float32, device="cuda"),
+                          y_int=torch.empty((M, N), dtype=torch.int32, device="cuda"), gamma=g, N=N, K=K))
+        refs.append((x_np, Wt, g))
+    probs = L.make_problems(specs)
+    tb = L.bitlinear_grouped_table_bytes(probs, len(specs), M)
+    table = torch.empty(tb, dtype=torch.uint8, device="cuda")
+    plan = L.bitlinear_grouped_plan_init(probs, len(specs), M, table, tb)
+    say(f"grouped near-tie rows M={M} kernel={plan.kernel} quant_rows={plan.quant_rows}")
+    L.bitlinear_forward_grouped(plan)
+    torch.cuda.synchronize()
+    for s, (x_np, Wt, g) in zip(specs, refs):
+        y_ref, xq_ref, eta_ref, y_int_ref = oracle.forward(x_np, Wt, g, threads=THREADS)
+        assert np.array_equal(s["xq"].cpu().numpy(), xq_ref)
+        assert np.array_equal(s["eta"].cpu().numpy().view(np.uint32), eta_ref.view(np.uint32))
+        assert np.array_equal(s["y_int"].cpu().numpy(), y_int_ref)
+        assert np.array_equal(s["y"].cpu().numpy().view(np.uint32), y_ref.view(np.uint32))

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import quantize, say
+from gpu_helpers import near_tie_rows, quantize, say
 from ternary_weight_linear_fwd_amd import synthetic as S
 
 pytestmark = pytest.mark.gpu
@@ -73,23 +73,6 @@ def test_empty_rows():
     bl().bitlinear_quantize_act(x, 0, 64, xq, eta)   # M = 0: nothing written
     torch.cuda.synchronize()
     assert int(xq[0, 0]) == 7 and float(eta[0]) == 3.0
-
-
-def near_tie_rows():
-    """Rows whose quotients x * 127 / eta straddle half-integers k + 1/2 at
-    offsets on both sides of the quantizers' 2^-12 fast-path margin, and hit
-    them exactly; eta (the row's first element) varies from row to row."""
-    offs = np.array([0.0, 1e-7, -1e-7, 3e-6, -3e-6, 1e-5, -1e-5, 6e-5, -6e-5,
-                     2.3e-4, -2.3e-4, 2.6e-4, -2.6e-4, 1e-3, -1e-3])
-    q = ((np.arange(-126, 126) + 0.5)[:, None] + offs[None, :]).ravel()
-    K = ((q.size + 1 + 15) // 16) * 16
-    rows = []
-    for eta in (3.0, 0.7, 1e-3, 1.0e4, 2.0 ** -10, 127.0):
-        r = np.zeros(K, np.float32)
-        r[0] = eta
-        r[1:q.size + 1] = (q * eta / 127.0).astype(np.float32)
-        rows.append(r)
-    return np.stack(rows)
 
 
 def test_near_ties():
